@@ -1,0 +1,335 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow CPU oracle for dense nearest-neighbour (NN) search and
+ * reciprocal matching between two per-pixel descriptor maps.  Only the test
+ * suite, the smoke check and the benchmark's CPU-baseline leg load it; the
+ * matching library never does, and the two share no code.
+ *
+ * Arithmetic: every similarity is an IEEE binary64 sum of binary64 products of
+ * the fp32 inputs (bf16 inputs arrive exactly widened to fp32), accumulated
+ * over the descriptor components in ascending order.  fp32 x fp32 products
+ * are exact in binary64 and a 24-term sum of unit-vector products errs by
+ * about 1e-15, so for these inputs the oracle is exact for all practical
+ * purposes.  No blocking, no reordering, no vectorisation tricks; threads only
+ * split independent queries.
+ *
+ * Sources (the pages are cited by title and section, never by line):
+ *  [P1] "MASt3R dissection" (kensou.mintlify.app), section 1 architecture
+ *       diagram: the match set is the set of pixel pairs (i, j) with
+ *       NN(D1[i], D2) = j and NN(D2[j], D1) = i;
+ *       section 3 "Napkin Formula": NN is the argmax of the inner product of
+ *       L2-normalised descriptors, and the reciprocal test gives built-in
+ *       outlier filtering.
+ *  [P3] "DUSt3R and MASt3R explained" (3dgaussiansplattingcourse.com), the
+ *       paragraph on MASt3R's third change (fast reciprocal matching): start
+ *       from a sparse grid of seed pixels, repeatedly map each one to its best
+ *       match in the other image and map that match back, collecting the
+ *       pairs that map onto each other.
+ * Readings where the pages are silent (tie-break, seed origin, what one
+ * iteration is, which pair is collected) are stated at each function.
+ *
+ * Parity status: every function here is pinned by tests under tests/
+ * (closed forms, brute force on tiny inputs, invariants); none is unpinned.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_ERR_ARG (-1)
+#define ORC_ERR_NOMEM (-2)
+#define ORC_ERR_CAP (-3)
+
+/* ------------------------------------------------------------------------
+ * Similarity of two descriptors: sum over c = 0..d-1 of a[c] * b[c], in that
+ * order, in binary64.  [P1] section 3: similarity is the inner product.
+ * ------------------------------------------------------------------------ */
+static double orc_similarity(const float* a, const float* b, int d)
+{
+    double s = 0.0;
+    for (int c = 0; c < d; ++c)
+        s += (double)a[c] * (double)b[c];
+    return s;
+}
+
+/* ------------------------------------------------------------------------
+ * NN of one query among n database rows: the first (lowest) index attaining
+ * the maximum similarity, found by a scan with a strict ">" update.  Also
+ * returns the best score (top1) and the best score over all other indices
+ * (top2; an exact duplicate of the best gives top2 == top1).
+ * [P1] section 3: j = argmax_k <D1[i], D2[k]>.  The pages do not say how ties
+ * are broken; the reading here is the lowest index.
+ * ------------------------------------------------------------------------ */
+static void orc_nn_one(const float* q, const float* db, int64_t n, int d,
+                       int32_t* idx, double* top1, double* top2)
+{
+    double best = -INFINITY, second = -INFINITY;
+    int64_t arg = -1;
+    for (int64_t k = 0; k < n; ++k) {
+        double s = orc_similarity(q, db + k * (int64_t)d, d);
+        if (s > best) {
+            second = best;
+            best = s;
+            arg = k;
+        } else if (s > second) {
+            second = s;
+        }
+    }
+    *idx = (int32_t)arg;
+    *top1 = best;
+    *top2 = second;
+}
+
+/* ---- a parallel loop over independent queries ------------------------- */
+typedef struct {
+    const float* qmap;       /* query map rows */
+    const int32_t* qidx;     /* rows of qmap to query, or NULL for 0..nq-1 */
+    int64_t nq;
+    const float* db;
+    int64_t ndb;
+    int d;
+    int32_t* out_idx;
+    double* out_top1;
+    double* out_top2;
+    int64_t begin, end;
+} orc_nn_job;
+
+static void* orc_nn_worker(void* p)
+{
+    orc_nn_job* j = (orc_nn_job*)p;
+    for (int64_t t = j->begin; t < j->end; ++t) {
+        int64_t row = j->qidx ? (int64_t)j->qidx[t] : t;
+        double t1, t2;
+        int32_t id;
+        orc_nn_one(j->qmap + row * (int64_t)j->d, j->db, j->ndb, j->d, &id, &t1, &t2);
+        j->out_idx[t] = id;
+        if (j->out_top1) j->out_top1[t] = t1;
+        if (j->out_top2) j->out_top2[t] = t2;
+    }
+    return NULL;
+}
+
+static int orc_nn_parallel(const float* qmap, const int32_t* qidx, int64_t nq, const float* db,
+                           int64_t ndb, int d, int nthreads, int32_t* out_idx, double* out_top1,
+                           double* out_top2)
+{
+    if (nq <= 0) return ORC_OK;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > nq) nthreads = (int)nq;
+    orc_nn_job jobs[256];
+    pthread_t th[256];
+    int started[256];
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = (orc_nn_job){qmap, qidx, nq, db, ndb, d, out_idx, out_top1, out_top2,
+                               nq * i / nthreads, nq * (i + 1) / nthreads};
+        started[i] = 0;
+    }
+    for (int i = 1; i < nthreads; ++i)
+        started[i] = pthread_create(&th[i], NULL, orc_nn_worker, &jobs[i]) == 0;
+    orc_nn_worker(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i) {
+        if (started[i]) pthread_join(th[i], NULL);
+        else orc_nn_worker(&jobs[i]); /* could not start a thread: do the share here */
+    }
+    return ORC_OK;
+}
+
+/* ========================================================================
+ * Exported entry points
+ * ===================================================================== */
+
+/* NN of every query row q[0..nq) among db[0..ndb) (rows of d floats), as
+ * defined by orc_nn_one.  out_top1/out_top2 may be NULL. */
+int orc_nn(const float* q, int64_t nq, const float* db, int64_t ndb, int32_t d, int32_t nthreads,
+           int32_t* out_idx, double* out_top1, double* out_top2)
+{
+    if (!q || !db || !out_idx || nq < 0 || ndb < 0 || d < 1) return ORC_ERR_ARG;
+    return orc_nn_parallel(q, NULL, nq, db, ndb, d, nthreads, out_idx, out_top1, out_top2);
+}
+
+/* Same, for the query rows qmap[qidx[t]], t < nq. */
+int orc_nn_rows(const float* qmap, const int32_t* qidx, int64_t nq, const float* db, int64_t ndb,
+                int32_t d, int32_t nthreads, int32_t* out_idx, double* out_top1, double* out_top2)
+{
+    if (!qmap || !qidx || !db || !out_idx || nq < 0 || ndb < 0 || d < 1) return ORC_ERR_ARG;
+    return orc_nn_parallel(qmap, qidx, nq, db, ndb, d, nthreads, out_idx, out_top1, out_top2);
+}
+
+/* Similarity of the given row pairs: out[t] = s(A[ia[t]], B[ib[t]]). */
+int orc_similarity_pairs(const float* A, const float* B, int32_t d, const int32_t* ia,
+                         const int32_t* ib, int64_t n, double* out)
+{
+    if (!A || !B || !ia || !ib || !out || d < 1 || n < 0) return ORC_ERR_ARG;
+    for (int64_t t = 0; t < n; ++t)
+        out[t] = orc_similarity(A + (int64_t)ia[t] * d, B + (int64_t)ib[t] * d, d);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------
+ * Mutual (reciprocal) NN set from the two NN maps.
+ * [P1] section 1 diagram and section 3: (i, j) is a match iff
+ * NN(D1[i], D2) = j and NN(D2[j], D1) = i.
+ * Output pairs (i, nn12[i]) in ascending i; returns the count (or < 0).
+ * ------------------------------------------------------------------------ */
+int64_t orc_mutual(const int32_t* nn12, int64_t n1, const int32_t* nn21, int64_t n2,
+                   int32_t* pairs, int64_t cap)
+{
+    if (!nn12 || !nn21 || !pairs || n1 < 0 || n2 < 0) return ORC_ERR_ARG;
+    int64_t m = 0;
+    for (int64_t i = 0; i < n1; ++i) {
+        int32_t j = nn12[i];
+        if (j < 0 || j >= n2) continue;
+        if (nn21[j] != i) continue;
+        if (m >= cap) return ORC_ERR_CAP;
+        pairs[2 * m] = (int32_t)i;
+        pairs[2 * m + 1] = j;
+        ++m;
+    }
+    return m;
+}
+
+/* ------------------------------------------------------------------------
+ * Fast reciprocal matching.  [P3], the fast-matching paragraph; [P1] section 3.
+ *
+ * Readings (the pages give the idea, not the exact steps):
+ *  - seeds: the regular grid {(y, x): y = offset + stride*a < H1,
+ *    x = offset + stride*b < W1} of image 1, pixel id y*W1 + x;
+ *    seed_limit >= 0 keeps only the first seed_limit seeds in row-major order
+ *    (used to time a bounded sample), -1 keeps all;
+ *  - one iteration maps the current pixel u_t forward, v_t = NN12(u_t), and
+ *    back, u_{t+1} = NN21(v_t);
+ *  - if u_{t+1} == u_t the chain has converged and (u_t, v_t) is collected
+ *    (a reciprocal pair); otherwise it restarts from u_{t+1};
+ *  - iterations t = 0 .. T-1; a chain that has not converged after T
+ *    iterations contributes nothing;
+ *  - the output is the set of collected pairs, ascending in u.
+ * Every NN here is orc_nn_one (lowest index on ties); results are memoised
+ * per pixel, which changes no result.
+ *
+ * Extra records for the tests:
+ *  - active[t]   : number of distinct pixels carried by live chains at the
+ *                  start of iteration t (NULL to skip);
+ *  - pair_clean  : per output pair, 1 if some chain that collected it made
+ *                  only NN decisions whose top1 - top2 margin exceeds eps;
+ *  - nn_queries  : number of NN searches performed (after memoisation).
+ * ------------------------------------------------------------------------ */
+int orc_fast(const float* A, int32_t H1, int32_t W1, const float* B, int64_t n2, int32_t d,
+             int32_t stride, int32_t offset, int32_t T, int32_t seed_limit, int32_t nthreads,
+             double eps, int32_t* pairs, int64_t cap, int64_t* n_pairs, uint8_t* pair_clean,
+             int64_t* active, int64_t* nn_queries)
+{
+    if (!A || !B || !pairs || !n_pairs || H1 < 0 || W1 < 0 || n2 < 0 || d < 1 || stride < 1 ||
+        offset < 0 || T < 0)
+        return ORC_ERR_ARG;
+    const int64_t n1 = (int64_t)H1 * W1;
+    *n_pairs = 0;
+    if (nn_queries) *nn_queries = 0;
+    if (active)
+        for (int t = 0; t < T; ++t) active[t] = 0;
+
+    /* seeds */
+    int64_t ns = 0;
+    for (int64_t y = offset; y < H1; y += stride)
+        for (int64_t x = offset; x < W1; x += stride) ++ns;
+    if (seed_limit >= 0 && ns > seed_limit) ns = seed_limit;
+    if (ns == 0 || n1 == 0 || n2 == 0 || T == 0) return ORC_OK;
+
+    int rc = ORC_ERR_NOMEM;
+    int32_t* cur = malloc(sizeof(int32_t) * ns);       /* chain position u_t */
+    uint8_t* alive = malloc(ns);
+    uint8_t* clean = malloc(ns);
+    int32_t* nn12 = malloc(sizeof(int32_t) * n1);      /* memo: -1 = not yet known */
+    double* mg12 = malloc(sizeof(double) * n1);
+    int32_t* nn21 = malloc(sizeof(int32_t) * n2);
+    double* mg21 = malloc(sizeof(double) * n2);
+    int32_t* match = malloc(sizeof(int32_t) * n1);     /* collected v per u, -1 = none */
+    uint8_t* mclean = malloc(n1);
+    uint8_t* seen1 = malloc(n1);
+    uint8_t* seen2 = malloc(n2);
+    int32_t* todo = malloc(sizeof(int32_t) * ns);
+    int32_t* res = malloc(sizeof(int32_t) * ns);
+    double* t1 = malloc(sizeof(double) * ns);
+    double* t2 = malloc(sizeof(double) * ns);
+    if (!cur || !alive || !clean || !nn12 || !mg12 || !nn21 || !mg21 || !match || !mclean ||
+        !seen1 || !seen2 || !todo || !res || !t1 || !t2)
+        goto done;
+
+    for (int64_t i = 0; i < n1; ++i) { nn12[i] = -1; match[i] = -1; mclean[i] = 0; seen1[i] = 0; }
+    for (int64_t i = 0; i < n2; ++i) { nn21[i] = -1; seen2[i] = 0; }
+    {
+        int64_t c = 0;
+        for (int64_t y = offset; y < H1 && c < ns; y += stride)
+            for (int64_t x = offset; x < W1 && c < ns; x += stride) {
+                cur[c] = (int32_t)(y * W1 + x);
+                alive[c] = 1;
+                clean[c] = 1;
+                ++c;
+            }
+    }
+
+    for (int32_t t = 0; t < T; ++t) {
+        /* forward: NN12 of every distinct live pixel not yet known */
+        int64_t nt = 0, distinct = 0;
+        for (int64_t c = 0; c < ns; ++c) {
+            if (!alive[c]) continue;
+            int32_t u = cur[c];
+            if (!seen1[u]) { seen1[u] = 1; ++distinct; if (nn12[u] < 0) todo[nt++] = u; }
+        }
+        for (int64_t c = 0; c < ns; ++c) if (alive[c]) seen1[cur[c]] = 0;
+        if (active) active[t] = distinct;
+        if (distinct == 0) break;
+        orc_nn_parallel(A, todo, nt, B, n2, d, nthreads, res, t1, t2);
+        for (int64_t k = 0; k < nt; ++k) { nn12[todo[k]] = res[k]; mg12[todo[k]] = t1[k] - t2[k]; }
+        if (nn_queries) *nn_queries += nt;
+
+        /* backward: NN21 of every distinct landing pixel not yet known */
+        nt = 0;
+        for (int64_t c = 0; c < ns; ++c) {
+            if (!alive[c]) continue;
+            int32_t v = nn12[cur[c]];
+            if (!seen2[v]) { seen2[v] = 1; if (nn21[v] < 0) todo[nt++] = v; }
+        }
+        for (int64_t c = 0; c < ns; ++c) if (alive[c]) seen2[nn12[cur[c]]] = 0;
+        orc_nn_parallel(B, todo, nt, A, n1, d, nthreads, res, t1, t2);
+        for (int64_t k = 0; k < nt; ++k) { nn21[todo[k]] = res[k]; mg21[todo[k]] = t1[k] - t2[k]; }
+        if (nn_queries) *nn_queries += nt;
+
+        /* reciprocity check: converged chains are collected, the rest restart */
+        for (int64_t c = 0; c < ns; ++c) {
+            if (!alive[c]) continue;
+            int32_t u = cur[c];
+            int32_t v = nn12[u];
+            int32_t u2 = nn21[v];
+            if (!(mg12[u] > eps) || !(mg21[v] > eps)) clean[c] = 0;
+            if (u2 == u) {
+                match[u] = v;
+                if (clean[c]) mclean[u] = 1;
+                alive[c] = 0;
+            } else {
+                cur[c] = u2;
+            }
+        }
+    }
+
+    {
+        int64_t m = 0;
+        for (int64_t u = 0; u < n1; ++u) {
+            if (match[u] < 0) continue;
+            if (m >= cap) { rc = ORC_ERR_CAP; goto done; }
+            pairs[2 * m] = (int32_t)u;
+            pairs[2 * m + 1] = match[u];
+            if (pair_clean) pair_clean[m] = mclean[u];
+            ++m;
+        }
+        *n_pairs = m;
+    }
+    rc = ORC_OK;
+done:
+    free(cur); free(alive); free(clean); free(nn12); free(mg12); free(nn21); free(mg21);
+    free(match); free(mclean); free(seen1); free(seen2); free(todo); free(res); free(t1); free(t2);
+    return rc;
+}

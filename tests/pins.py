@@ -1,0 +1,342 @@
+"""Pins for the CPU oracle: checks against facts the pages and the mathematics fix.
+
+Each pin takes an ``oracle.Oracle`` (the real build, or a deliberately broken
+copy of the same source built by the mutation test) and raises AssertionError
+on failure.  None of them re-types the oracle's own code: they use hand-derived
+fixtures (tests/golden), closed forms (identity, permutation, planted
+noise-free fields), brute force with numpy on tiny inputs, and invariants of the
+reciprocal scheme.
+
+Run as a script (``python tests/pins.py LIBPATH``) it prints the names of the
+failing pins as JSON, which is how the mutation test runs broken builds in a
+child process.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import sys
+
+import numpy as np
+
+_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if _ROOT not in sys.path:
+    sys.path.insert(0, _ROOT)
+
+import workloads  # noqa: E402
+
+GOLDEN = os.path.join(_ROOT, "tests", "golden")
+
+
+def _load_golden(name):
+    with open(os.path.join(GOLDEN, name + ".json")) as f:
+        g = json.load(f)
+    if "angles1" in g:
+        a = np.radians(np.asarray(g["angles1"], np.float64))
+        b = np.radians(np.asarray(g["angles2"], np.float64))
+        A = np.stack([np.cos(a), np.sin(a)], 1).astype(np.float32)
+        B = np.stack([np.cos(b), np.sin(b)], 1).astype(np.float32)
+    else:
+        A = np.asarray(g["vectors1"], np.float32)
+        B = np.asarray(g["vectors2"], np.float32)
+    return g, A, B
+
+
+def _rand_unit(rng, n, d):
+    x = rng.standard_normal((n, d))
+    return (x / np.linalg.norm(x, axis=1, keepdims=True)).astype(np.float32)
+
+
+def _pairs_set(p):
+    return {(int(a), int(b)) for a, b in np.asarray(p).reshape(-1, 2)}
+
+
+# ============================================================================ NN
+
+def pin_golden_nn(orc):
+    """Hand-derived NN maps (tests/golden)."""
+    for name in ("circle_1x4", "grid_2x3", "ties_d1", "negative_scores"):
+        g, A, B = _load_golden(name)
+        i12, t1, t2 = orc.nn(A, B)
+        i21, _, _ = orc.nn(B, A)
+        assert i12.tolist() == g["nn12"], (name, i12)
+        assert i21.tolist() == g["nn21"], (name, i21)
+        if "top1_12" in g:
+            assert np.allclose(t1, g["top1_12"], atol=1e-7), (name, t1)
+            assert np.allclose(t2, g["top2_12"], atol=1e-7), (name, t2)
+
+
+def pin_nn_numpy_bruteforce(orc):
+    """argmax of the full float64 similarity matrix (numpy takes the first maximum)."""
+    rng = np.random.default_rng(11)
+    for (n1, n2, d) in ((37, 53, 24), (20, 9, 3), (5, 64, 1), (33, 31, 7)):
+        A = _rand_unit(rng, n1, d)
+        B = _rand_unit(rng, n2, d)
+        S = A.astype(np.float64) @ B.astype(np.float64).T
+        idx, t1, t2 = orc.nn(A, B)
+        assert (idx == S.argmax(1)).all()
+        assert np.allclose(t1, S.max(1), atol=1e-12, rtol=0)
+        Ss = np.sort(S, axis=1)
+        if n2 > 1:
+            assert np.allclose(t2, Ss[:, -2], atol=1e-12, rtol=0)
+
+
+def pin_nn_identity(orc):
+    """B = A with distinct rows: every row is its own NN, top1 = |a|^2."""
+    rng = np.random.default_rng(12)
+    A = _rand_unit(rng, 60, 24)
+    idx, t1, _ = orc.nn(A, A)
+    assert (idx == np.arange(60)).all()
+    sq = np.array([math.fsum(float(x) * float(x) for x in r) for r in A])
+    assert np.allclose(t1, sq, atol=1e-15, rtol=0)
+
+
+def pin_nn_permutation(orc):
+    """B[k] = A[pi(k)]: NN21 = pi and NN12 = pi^-1 (pi is not an involution)."""
+    rng = np.random.default_rng(13)
+    A = _rand_unit(rng, 40, 24)
+    pi = np.roll(np.arange(40), 7)
+    pi = pi[rng.permutation(40)]
+    assert (pi[pi] != np.arange(40)).any()
+    B = A[pi]
+    i21, _, _ = orc.nn(B, A)
+    i12, _, _ = orc.nn(A, B)
+    inv = np.empty(40, np.int64)
+    inv[pi] = np.arange(40)
+    assert (i21 == pi).all()
+    assert (i12 == inv).all()
+
+
+def pin_nn_ties_lowest_index(orc):
+    """Exact duplicates: the lowest index wins and top2 == top1."""
+    rng = np.random.default_rng(14)
+    A = _rand_unit(rng, 4, 24)
+    B = _rand_unit(rng, 12, 24)
+    B[9] = A[0]
+    B[3] = A[0]
+    B[6] = A[1]
+    B[11] = A[1]
+    idx, t1, t2 = orc.nn(A[:2], B)
+    assert idx.tolist() == [3, 6]
+    assert (t1 == t2).all()
+    ones = np.ones((7, 1), np.float32)
+    idx, t1, t2 = orc.nn(ones, ones)
+    assert (idx == 0).all() and (t1 == 1).all() and (t2 == 1).all()
+
+
+def pin_nn_margin(orc):
+    """top1/top2 against closed-form cosines: query at 0 deg, rows at 30, 10, 20, 50 deg."""
+    ang = np.radians([30.0, 10.0, 20.0, 50.0])
+    B = np.stack([np.cos(ang), np.sin(ang)], 1).astype(np.float32)
+    A = np.array([[1.0, 0.0]], np.float32)
+    idx, t1, t2 = orc.nn(A, B)
+    assert idx[0] == 1
+    assert abs(t1[0] - math.cos(math.radians(10))) < 1e-7
+    assert abs(t2[0] - math.cos(math.radians(20))) < 1e-7
+
+
+def pin_nn_rows_gather(orc):
+    """nn_rows(qmap, rows) equals nn on the gathered rows."""
+    rng = np.random.default_rng(15)
+    A = _rand_unit(rng, 30, 24)
+    B = _rand_unit(rng, 25, 24)
+    rows = np.array([29, 0, 5, 5, 17], np.int32)
+    S = A[rows].astype(np.float64) @ B.astype(np.float64).T
+    idx, _, _ = orc.nn_rows(A, rows, B)
+    assert (idx == S.argmax(1)).all()
+
+
+def pin_similarity_closed_form(orc):
+    """s((cos a, sin a), (cos b, sin b)) = cos(a - b), within fp32 input rounding."""
+    a = np.radians([0.0, 33.0, 170.0, -80.0])
+    b = np.radians([45.0, 33.0, 10.0, 100.0])
+    A = np.stack([np.cos(a), np.sin(a)], 1).astype(np.float32)
+    B = np.stack([np.cos(b), np.sin(b)], 1).astype(np.float32)
+    s = orc.similarity_pairs(A, B, np.arange(4), np.arange(4))
+    assert np.allclose(s, np.cos(a - b), atol=2e-7, rtol=0)
+
+
+# ============================================================================ mutual
+
+def pin_golden_mutual(orc):
+    for name in ("circle_1x4", "grid_2x3", "ties_d1", "negative_scores"):
+        g, A, B = _load_golden(name)
+        pairs = orc.mutual_nn(A, B)[0]
+        assert pairs.tolist() == g["mutual"], (name, pairs)
+
+
+def pin_mutual_symmetry_and_one_to_one(orc):
+    """M*(B, A) is M*(A, B) with each pair swapped; M* is one-to-one."""
+    p = workloads.make_pair(12, 10, 24, seed=21, warp="shift", sigma=0.1, rho=0.2)
+    m12 = _pairs_set(orc.mutual_nn(p.D1, p.D2)[0])
+    m21 = _pairs_set(orc.mutual_nn(p.D2, p.D1)[0])
+    assert m12 == {(j, i) for (i, j) in m21}
+    assert len({i for i, _ in m12}) == len(m12) == len({j for _, j in m12})
+    assert len(m12) > 0
+
+
+def pin_mutual_planted_closed_form(orc):
+    """Noise-free planted field (D2[q] = D1[src(q)] exactly, distinct D1 rows):
+    M* = {(p, min{q : src(q) = p})} -- clamped borders plant exact duplicates."""
+    p = workloads.make_pair(14, 11, 24, seed=22, warp="shift", sigma=0.0, rho=0.0)
+    assert (p.D2 == p.D1[p.src]).all()
+    first = {}
+    for q, s in enumerate(p.src.tolist()):
+        first.setdefault(s, q)
+    expect = sorted(first.items())
+    got = orc.mutual_nn(p.D1, p.D2)[0].tolist()
+    assert got == [list(e) for e in expect]
+
+
+# ============================================================================ fast scheme
+
+def _chain_set(n12, n21, seeds, T):
+    """The fast scheme's output by its set characterisation: every p reached from a
+    seed within t <= T-1 applications of f = NN21 o NN12 with f(p) = p."""
+    out = set()
+    for s in seeds:
+        u = int(s)
+        for _ in range(T):
+            v = int(n12[u])
+            u2 = int(n21[v])
+            if u2 == u:
+                out.add((u, v))
+                break
+            u = u2
+    return out
+
+
+def _grid(H, W, stride, offset):
+    return [y * W + x for y in range(offset, H, stride) for x in range(offset, W, stride)]
+
+
+def pin_golden_fast(orc):
+    for name in ("circle_1x4", "grid_2x3", "ties_d1", "negative_scores"):
+        g, A, B = _load_golden(name)
+        for case in g["fast"]:
+            r = orc.fast(A, g["H1"], g["W1"], B, case["stride"], case["offset"], case["T"])
+            assert r["pairs"].tolist() == case["pairs"], (name, case, r["pairs"])
+
+
+def pin_fast_subset_of_mutual(orc):
+    """Every fast match is a mutual NN (so the output is one-to-one)."""
+    p = workloads.make_pair(24, 20, 24, seed=23, warp="shift", sigma=0.1, rho=0.2)
+    mset = _pairs_set(orc.mutual_nn(p.D1, p.D2)[0])
+    for stride, off, T in ((4, 2, 5), (3, 0, 2), (5, 1, 10)):
+        f = _pairs_set(orc.fast(p.D1, p.H, p.W, p.D2, stride, off, T)["pairs"])
+        assert f <= mset
+        assert len({u for u, _ in f}) == len(f) == len({v for _, v in f})
+
+
+def pin_fast_stride1_is_bruteforce(orc):
+    """Stride 1 seeds every pixel; each mutual pixel is its own fixed point, so the
+    scheme returns exactly the brute-force mutual set for any T >= 1."""
+    p = workloads.make_pair(16, 13, 24, seed=24, warp="affine", sigma=0.15, rho=0.3)
+    mset = _pairs_set(orc.mutual_nn(p.D1, p.D2)[0])
+    for T in (1, 3):
+        f = _pairs_set(orc.fast(p.D1, p.H, p.W, p.D2, 1, 0, T)["pairs"])
+        assert f == mset
+
+
+def pin_fast_set_characterisation(orc):
+    """Output equals {(p, NN12(p)) : f(p) = p, p = f^t(seed), t <= T-1}, built here from
+    the NN maps by walking each seed's chain."""
+    p = workloads.make_pair(20, 18, 24, seed=25, warp="shift", sigma=0.1, rho=0.2)
+    n12 = orc.nn(p.D1, p.D2)[0]
+    n21 = orc.nn(p.D2, p.D1)[0]
+    for stride, off, T in ((4, 2, 1), (4, 2, 2), (4, 2, 3), (3, 1, 10), (7, 0, 4), (2, 1, 1)):
+        want = _chain_set(n12, n21, _grid(p.H, p.W, stride, off), T)
+        got = _pairs_set(orc.fast(p.D1, p.H, p.W, p.D2, stride, off, T)["pairs"])
+        assert got == want, (stride, off, T)
+
+
+def pin_fast_monotone_ascent(orc):
+    """Along a chain s(u_t, v_t) <= s(u_{t+1}, v_t) <= s(u_{t+1}, v_{t+1}); with lowest-index
+    ties no chain cycles, so every chain reaches a reciprocal pair."""
+    p = workloads.make_pair(20, 16, 24, seed=26, warp="shift", sigma=0.25, rho=0.4)
+    n12 = orc.nn(p.D1, p.D2)[0]
+    n21 = orc.nn(p.D2, p.D1)[0]
+    N = p.H * p.W
+    for s in range(N):
+        u = s
+        seen = set()
+        while True:
+            v = int(n12[u])
+            u2 = int(n21[v])
+            s0, s1 = orc.similarity_pairs(p.D1, p.D2, [u, u2], [v, v])
+            assert s0 <= s1
+            if u2 == u:
+                break
+            v2 = int(n12[u2])
+            s2 = orc.similarity_pairs(p.D1, p.D2, [u2], [v2])[0]
+            assert s1 <= s2
+            assert u not in seen
+            seen.add(u)
+            u = u2
+
+
+def pin_fast_planted_noise_free(orc):
+    """Noise-free planted field: a seed that is a source pixel converges in the first
+    iteration to min{q : src(q) = seed}; every match (u, v) has u = src(v)."""
+    p = workloads.make_pair(24, 16, 24, seed=27, warp="shift", sigma=0.0, rho=0.0)
+    first = {}
+    for q, s in enumerate(p.src.tolist()):
+        first.setdefault(s, q)
+    r1 = orc.fast(p.D1, p.H, p.W, p.D2, 4, 2, 1)
+    got = _pairs_set(r1["pairs"])
+    seeds = _grid(p.H, p.W, 4, 2)
+    assert got == {(s, first[s]) for s in seeds if s in first}
+    r = orc.fast(p.D1, p.H, p.W, p.D2, 4, 2, 10)
+    for u, v in r["pairs"].tolist():
+        assert p.src[v] == u
+
+
+def pin_fast_edges(orc):
+    """T = 0 gives nothing; a stride beyond the image leaves the single seed at the
+    offset; the number of live pixels starts at the seed count and never grows."""
+    p = workloads.make_pair(12, 9, 24, seed=28, warp="shift", sigma=0.1, rho=0.2)
+    assert orc.fast(p.D1, p.H, p.W, p.D2, 3, 1, 0)["pairs"].shape[0] == 0
+    n12 = orc.nn(p.D1, p.D2)[0]
+    n21 = orc.nn(p.D2, p.D1)[0]
+    r = orc.fast(p.D1, p.H, p.W, p.D2, 50, 0, 6)
+    assert _pairs_set(r["pairs"]) == _chain_set(n12, n21, [0], 6)
+    r = orc.fast(p.D1, p.H, p.W, p.D2, 3, 1, 8)
+    a = r["active"]
+    assert a[0] == len(_grid(p.H, p.W, 3, 1))
+    assert all(a[t + 1] <= a[t] for t in range(len(a) - 1))
+
+
+def pin_fast_clean_flag(orc):
+    """Chains through exact ties are not clean; well-separated chains are."""
+    g, A, B = _load_golden("ties_d1")
+    r = orc.fast(A, g["H1"], g["W1"], B, 1, 0, 1)
+    assert r["clean"].tolist() == [0]
+    g, A, B = _load_golden("circle_1x4")
+    r = orc.fast(A, g["H1"], g["W1"], B, 1, 0, 1)
+    assert r["clean"].tolist() == [1, 1, 1]
+    # a tie only in the backward search: image-1 pixels 0 and 1 are identical
+    A = np.array([[1, 0], [1, 0], [0, 1]], np.float32)
+    b = np.radians([10.0, 100.0])
+    B = np.stack([np.cos(b), np.sin(b)], 1).astype(np.float32)
+    r = orc.fast(A, 1, 3, B, 1, 0, 1)
+    assert r["pairs"].tolist() == [[0, 0], [2, 1]]
+    assert r["clean"].tolist() == [0, 1]
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
+
+
+def failing_pins(orc):
+    bad = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except Exception:  # noqa: BLE001 -- any failure of a broken build counts
+            bad.append(pin.__name__)
+    return bad
+
+
+if __name__ == "__main__":
+    import oracle
+    print(json.dumps(failing_pins(oracle.Oracle(sys.argv[1]))))
