@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Benchmark: fast reciprocal matching of one 512x384 d=24 fp32 descriptor-map pair.
+
+One step = one mr_fast_reciprocal call on inputs already resident in HBM:
+seed grid (stride 8, 3072 seeds), up to 10 forward/backward NN iterations with
+cycle check and frontier compaction, and the ordered match list.  The JSON line
+reports image pairs/s, NN queries/s, the similarity kernel's fraction of the
+fp32 matrix-core peak (timed live with HIP events around each launch), and the
+CPU oracle timed on the host for the same pair.  Other workloads (brute-force
+bf16 mutual NN, the 64-pair batch, the 1024x768 bf16 pair) are reported under
+"other" unless --main-only.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "image pairs/sec fast reciprocal NN @512×384 d=24; NN-queries/sec; %MFMA peak"
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense matrix-core peaks
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--main-only", action="store_true", help="skip the other workloads")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    return ap.parse_args()
+
+
+def dev_maps(p, torch, dev):
+    import numpy as np
+    if p.dtype == "bf16":
+        A = torch.from_numpy(np.ascontiguousarray(p.D1_bits).reshape(p.H, p.W, p.d)).view(torch.bfloat16)
+        B = torch.from_numpy(np.ascontiguousarray(p.D2_bits).reshape(p.H, p.W, p.d)).view(torch.bfloat16)
+    else:
+        A = torch.from_numpy(p.D1.reshape(p.H, p.W, p.d))
+        B = torch.from_numpy(p.D2.reshape(p.H, p.W, p.d))
+    return A.to(dev).unsqueeze(0), B.to(dev).unsqueeze(0)
+
+
+def time_steps(fn, steps, warmup, torch, prof_launches=0):
+    """Warm up, then time exactly `steps` calls between two synchronisations.
+    Returns (ms per step, summed similarity-kernel ms, launches timed)."""
+    import dense_grounded_image_amd as mr
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    if prof_launches:
+        mr.profile_begin(prof_launches)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    kms, kn = mr.profile_end() if prof_launches else (0.0, 0)
+    return t0.elapsed_time(t1) / steps, kms, kn
+
+
+def fast_work(active, N, d):
+    """Algorithmic work of one fast-scheme call: every live pixel is one forward and one
+    backward NN query, each 2*N*d flops against the other map."""
+    q = 2 * int(active.sum())
+    return q, 2.0 * N * d * q
+
+
+def run_fast(p, batch_pairs, args, torch, dev, prof=True):
+    import dense_grounded_image_amd as mr
+    if batch_pairs is None:
+        A, B = dev_maps(p, torch, dev)
+    else:
+        A, B = batch_pairs
+    f = mr.FastReciprocal(A, B, p.stride, p.offset, p.max_iters)
+    launches = 2 * p.max_iters * args.steps
+    ms, kms, kn = time_steps(lambda: f(A, B), args.steps, args.warmup, torch, launches if prof else 0)
+    pairs, n_pairs, active = f(A, B)
+    torch.cuda.synchronize()
+    act = active.cpu().numpy()
+    q, flops = fast_work(act, p.N, p.d)
+    return dict(ms=ms, kernel_ms=kms, launches=kn, nn_queries=q, flops=flops,
+                active=act[0].tolist(), matches=[int(x) for x in n_pairs.cpu()], batch=A.shape[0])
+
+
+def roofline(flops_per_step, steps, kernel_ms, launches, dtype):
+    if not launches:
+        return None
+    per_launch = flops_per_step * steps / launches
+    avg_ms = kernel_ms / launches
+    achieved = per_launch / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[dtype]
+    return {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "kernel": "nn_argmax_kernel", "avg_launch_us": round(avg_ms * 1e3, 2),
+            "flops_per_launch": per_launch}
+
+
+def cpu_baseline(p):
+    import oracle
+    threads = oracle.default_threads()
+    t = time.perf_counter()
+    r = oracle.fast(p.D1, p.H, p.W, p.D2, p.stride, p.offset, p.max_iters, nthreads=threads)
+    dt = time.perf_counter() - t
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(1.0 / dt, 4), "unit": "pairs/s", "cores": threads, "kind": "oracle",
+            "sample": "the whole 512x384 pair (3072 seeds, 10 iterations), binary64 C oracle, %d threads, "
+                      "%.2f s, %d NN queries, CPU %s, nproc %d" % (threads, dt, r["nn_queries"], cpu,
+                                                                   os.cpu_count() or 0),
+            "nn_queries_per_s": round(r["nn_queries"] / dt, 1), "matches": int(len(r["pairs"]))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this matcher has no multi-GPU path "
+              "(the 64-pair batch would shard by pairs; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dense_grounded_image_amd as mr
+    import workloads
+    mr.load_library()
+    dev = torch.device("cuda:0")
+
+    p = workloads.config_pair(1)
+    print("bench: workload pair-512x384-f32 ready", file=sys.stderr, flush=True)
+    r = run_fast(p, None, args, torch, dev)
+    value = 1000.0 / r["ms"]
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "pairs/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "pair-512x384-f32: fast reciprocal matching, one 512x384 pair, d=24 fp32, "
+                               "seed stride 8 offset 4 (3072 seeds), 10 iterations",
+                   "H": 512, "W": 384, "d": 24, "batch": 1, "stride": 8, "offset": 4, "max_iters": 10},
+        "nn_queries_per_s": round(r["nn_queries"] * 1000.0 / r["ms"], 1),
+        "nn_queries_per_step": r["nn_queries"], "iter_active": r["active"], "matches": r["matches"][0],
+        "roofline": roofline(r["flops"], args.steps, r["kernel_ms"], r["launches"], "f32"),
+        "step_mfma_frac": round(r["flops"] / (r["ms"] * 1e-3) / 1e12 / PEAK_TFLOPS["f32"], 4),
+    }
+    print("bench: fast pair %.4f ms/step" % r["ms"], file=sys.stderr, flush=True)
+
+    if not args.main_only:
+        other = {}
+        # 64-pair batch, fp32
+        ps = [workloads.config_pair(3, b) for b in range(64)]
+        A = torch.stack([dev_maps(q, torch, dev)[0][0] for q in ps])
+        B = torch.stack([dev_maps(q, torch, dev)[1][0] for q in ps])
+        del ps
+        print("bench: batch data ready", file=sys.stderr, flush=True)
+        rb = run_fast(workloads.config_pair(3, 0), (A, B), args, torch, dev)
+        other["batch64-512x384-f32"] = {
+            "pairs_per_s": round(64000.0 / rb["ms"], 2), "ms_per_call": round(rb["ms"], 3),
+            "nn_queries_per_s": round(rb["nn_queries"] * 1000.0 / rb["ms"], 1),
+            "roofline": roofline(rb["flops"], args.steps, rb["kernel_ms"], rb["launches"], "f32")}
+        del A, B
+        # 1024x768 bf16 pair
+        p4 = workloads.config_pair(4)
+        r4 = run_fast(p4, None, args, torch, dev)
+        other["pair-1024x768-bf16"] = {
+            "pairs_per_s": round(1000.0 / r4["ms"], 2), "ms_per_call": round(r4["ms"], 3),
+            "nn_queries_per_s": round(r4["nn_queries"] * 1000.0 / r4["ms"], 1),
+            "iter_active": r4["active"], "matches": r4["matches"][0],
+            "roofline": roofline(r4["flops"], args.steps, r4["kernel_ms"], r4["launches"], "bf16")}
+        # brute-force mutual NN, bf16
+        p2 = workloads.config_pair(2)
+        A2, B2 = dev_maps(p2, torch, dev)
+        ws = torch.empty(mr.workspace_bytes(mr.MR_OP_MUTUAL_NN, A2, B2), dtype=torch.uint8, device=dev)
+        ms, kms, kn = time_steps(lambda: mr.mutual_nn(A2, B2, ws=ws), max(3, args.steps // 4), 2, torch,
+                                 2 * max(3, args.steps // 4))
+        fl = 2.0 * 2 * p2.N * p2.N * p2.d   # both directions are computed
+        other["pair-512x384-bf16-bruteforce"] = {
+            "pairs_per_s": round(1000.0 / ms, 2), "ms_per_call": round(ms, 3),
+            "nn_queries_per_s": round(2 * p2.N * 1000.0 / ms, 1),
+            "mfma_frac_algorithmic": round(2.0 * p2.N * p2.N * p2.d / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+            "roofline": roofline(fl, max(3, args.steps // 4), kms, kn, "bf16")}
+        out["other"] = other
+
+    if not args.no_cpu:
+        print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(p)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * mr.h -- dense nearest-neighbour search and reciprocal matching between two
+ * per-pixel descriptor maps, on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (the pages are cited by title and section):
+ *  - Similarity of two descriptors is their inner product; the maps hold one
+ *    L2-normalised descriptor per pixel (d = 24 in MASt3R).
+ *    ["MASt3R dissection", section 3 "Napkin Formula"; "DUSt3R and MASt3R
+ *    explained", paragraph on MASt3R's dense local-feature head.]
+ *  - The NN of a query is the database row of maximal similarity; ties go to
+ *    the lowest row index (the pages are silent on ties).
+ *  - A reciprocal (mutual) match is a pair (i, j) with NN(D1[i], D2) = j and
+ *    NN(D2[j], D1) = i.  ["MASt3R dissection", section 1 diagram, section 3.]
+ *  - The fast reciprocal scheme seeds a regular grid of image 1, maps every
+ *    live pixel to its NN in image 2 and back, keeps the pairs that map onto
+ *    each other and restarts the others from where they landed, for a fixed
+ *    number of iterations.  ["DUSt3R and MASt3R explained", the paragraph on
+ *    MASt3R's fast reciprocal matching.]
+ *
+ * Arithmetic: fp32 maps are multiplied in fp32 on the matrix cores with fp32
+ * accumulation; bf16 maps use exact bf16 products with fp32 accumulation.
+ * Every kernel computes s(i, j) with the same instruction and the same
+ * component order, so a score is bitwise the same whichever map plays the
+ * query.  -0.0 is treated as +0.0.  Inputs must be finite (NaN/Inf are out of
+ * contract).
+ *
+ * Conventions shared by every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates no device memory: scratch space comes in through `ws`
+ *    (`ws_bytes` long, 256-byte aligned, size from mr_workspace_bytes).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls are asynchronous on that stream; outputs are valid once the stream
+ *    has completed the call.  Calls that share a workspace must not overlap.
+ *  - Arguments are validated on the host before anything is launched; a
+ *    nonzero return means nothing was enqueued.  MR_ERR_DEVICE reports a
+ *    launch failure after some work may have been enqueued.
+ *  - A map is a contiguous row-major array [batch][h][w][d]; pixel id
+ *    p = y*w + x.  Supported: 1 <= d <= 64, dtype MR_F32 or MR_BF16 (bf16
+ *    needs d to be a multiple of 8), h*w <= 2^28.  Both maps of a call must
+ *    agree on batch, d and dtype; their h and w may differ.
+ */
+#ifndef MR_H
+#define MR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MR_F32 = 0, MR_BF16 = 1 } mr_dtype;
+
+typedef enum {
+    MR_OK = 0,
+    MR_ERR_NULL = 1,      /* a required pointer is NULL */
+    MR_ERR_SHAPE = 2,     /* sizes out of range or inconsistent between the maps */
+    MR_ERR_DTYPE = 3,     /* unknown dtype, dtypes differ, or bf16 with d % 8 != 0 */
+    MR_ERR_PARAM = 4,     /* stride < 1, offset < 0, max_iters < 0, bad op, n_q < 0 */
+    MR_ERR_WORKSPACE = 5, /* ws NULL/misaligned while needed, or ws_bytes too small */
+    MR_ERR_CAPACITY = 6,  /* cap below the static bound on the number of pairs */
+    MR_ERR_DEVICE = 7     /* a HIP call failed */
+} mr_status;
+
+typedef struct {
+    const void* data; /* device pointer to [batch][h][w][d] */
+    int32_t batch, h, w, d;
+    int32_t dtype;    /* mr_dtype */
+} mr_map;
+
+enum { MR_OP_NN_ARGMAX = 0, MR_OP_MUTUAL_NN = 1, MR_OP_FAST_RECIPROCAL = 2 };
+
+/* Workspace bytes that entry point `op` needs for these maps and parameters
+ * (n_q: queries per pair for MR_OP_NN_ARGMAX; stride/offset for
+ * MR_OP_FAST_RECIPROCAL; other arguments are ignored).  Returns 0 for invalid
+ * arguments (the entry point itself then reports the error). */
+size_t mr_workspace_bytes(int op, const mr_map* a, const mr_map* b, int64_t n_q, int32_t stride,
+                          int32_t offset);
+
+/* Static text for a status code. */
+const char* mr_status_str(int status);
+
+/* Number of seeds on the grid {(offset + stride*a, offset + stride*b)} of an
+ * h x w image, i.e. the capacity mr_fast_reciprocal needs per pair; -1 for
+ * invalid arguments. */
+int64_t mr_seed_count(int32_t h, int32_t w, int32_t stride, int32_t offset);
+
+/* ---------------------------------------------------------------------------
+ * mr_nn_argmax: nearest neighbour of query rows of map q among all rows of
+ * map db of the same pair ("MASt3R dissection", section 3: j = argmax_k of
+ * the inner product).
+ *   q_idx    : NULL to query every row of q (then n_q must be q->h*q->w), or
+ *              [batch][n_q] row ids local to each pair's q map.
+ *   out_idx  : [batch][n_q] NN row id in db (lowest index on ties); -1 when
+ *              db has no rows.
+ *   out_score: NULL or [batch][n_q] fp32 similarity of that NN.
+ * --------------------------------------------------------------------------- */
+int mr_nn_argmax(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q,
+                 int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mr_mutual_nn: brute-force reciprocal NN ("MASt3R dissection", section 1
+ * diagram and section 3; "DUSt3R and MASt3R explained": the quadratic
+ * all-pairs baseline).
+ *   nn_ab  : [batch][Na] NN in b of every pixel of a.
+ *   nn_ba  : [batch][Nb] NN in a of every pixel of b.
+ *   pairs  : [batch][cap][2] (i, j) with nn_ab[i] = j and nn_ba[j] = i,
+ *            ascending in i; cap >= min(Na, Nb).
+ *   n_pairs: [batch] int64 counts.
+ * --------------------------------------------------------------------------- */
+int mr_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba, int32_t* pairs,
+                 int64_t cap, int64_t* n_pairs, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mr_fast_reciprocal: the fast reciprocal matching scheme ("DUSt3R and
+ * MASt3R explained", paragraph on the fast reciprocal matching; "MASt3R
+ * dissection", section 3: early termination plus bidirectional NN).
+ *   Seeds: pixels (y, x) of image a with y = offset + stride*i < h and
+ *   x = offset + stride*j < w.  One iteration maps every live pixel u to
+ *   v = NN(a[u], b) and back to u' = NN(b[v], a).  If u' == u, (u, v) is kept
+ *   and u stops; otherwise u' becomes live unless it is already matched or was
+ *   live in this or an earlier iteration (its future is then already being
+ *   followed).  max_iters iterations at most; max_iters = 0 gives no pairs.
+ *   The kept set equals {(p, NN(a[p], b)) : p = f(p), p = f^t(seed),
+ *   t < max_iters} with f(u) = u'.
+ *   pairs      : [batch][cap][2] ascending in u; cap >= mr_seed_count(...).
+ *   n_pairs    : [batch] int64 counts.
+ *   iter_active: NULL or [batch][max_iters] int32: live pixels at the start
+ *                of each iteration.
+ * --------------------------------------------------------------------------- */
+int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset,
+                       int32_t max_iters, int32_t* pairs, int64_t cap, int64_t* n_pairs,
+                       int32_t* iter_active, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement aid (not thread-safe; one profiling window per process).
+ * mr_profile_begin(n): from now on, record a pair of hipEvents on the call's
+ * stream around every launch of the similarity/argmax kernel, for up to n
+ * launches.  mr_profile_end: wait for those events, return the summed kernel
+ * time in milliseconds and the number of launches timed, release the events.
+ * --------------------------------------------------------------------------- */
+int mr_profile_begin(int32_t max_launches);
+int mr_profile_end(double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MR_H */

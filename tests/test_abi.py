@@ -1,0 +1,147 @@
+"""The C ABI on the host: every declared symbol is exported, and argument validation
+returns its documented status before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import dense_grounded_image_amd as mr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mr.h")
+
+OK, NULL, SHAPE, DTYPE, PARAM, WS, CAP = 0, 1, 2, 3, 4, 5, 6
+FAKE = 1 << 20  # an aligned non-NULL address; validation failures never dereference it
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mr.LIB_PATH):
+        from dense_grounded_image_amd.build import build_library
+        build_library()
+    return mr.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mr_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(mr.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", mr.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, n
+        assert getattr(lib, n) is not None
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = mr._lib
+    mr._lib = None
+    try:
+        with pytest.raises(ImportError):
+            mr.load_library(str(tmp_path / "nope.so"))
+    finally:
+        mr._lib = saved
+
+
+def M(h=8, w=6, d=24, dtype=0, batch=1, data=FAKE):
+    return mr.MrMap(data, batch, h, w, d, dtype)
+
+
+def R(x):
+    return ctypes.byref(x)
+
+
+def test_status_strings_and_seed_count(lib):
+    for code in range(0, 8):
+        assert lib.mr_status_str(code)
+    assert lib.mr_seed_count(512, 384, 8, 4) == 3072
+    assert lib.mr_seed_count(1024, 768, 8, 4) == 12288
+    assert lib.mr_seed_count(64, 48, 8, 4) == 48
+    assert lib.mr_seed_count(4, 4, 100, 0) == 1
+    assert lib.mr_seed_count(4, 4, 2, 4) == 0
+    assert lib.mr_seed_count(4, 4, 0, 0) == -1
+    assert lib.mr_seed_count(4, 4, 1, -1) == -1
+
+
+def test_map_validation(lib):
+    ws = ctypes.c_void_p(FAKE)
+    out = ctypes.c_void_p(FAKE)
+    cases = [
+        (None, M(), NULL),
+        (M(d=0), M(d=0), SHAPE),
+        (M(d=65), M(d=65), SHAPE),
+        (M(h=-1), M(), SHAPE),
+        (M(batch=0), M(batch=0), SHAPE),
+        (M(h=1 << 15, w=1 << 14), M(), SHAPE),
+        (M(dtype=7), M(dtype=7), DTYPE),
+        (M(dtype=1, d=12), M(dtype=1, d=12), DTYPE),
+        (M(), M(dtype=1), DTYPE),
+        (M(), M(batch=2), SHAPE),
+        (M(), M(d=16), SHAPE),
+        (M(data=FAKE + 4), M(), SHAPE),
+        (M(data=None), M(), NULL),
+    ]
+    for a, b, want in cases:
+        pa = R(a) if a is not None else None
+        rc = lib.mr_fast_reciprocal(pa, R(b), 8, 4, 10, out, 1 << 20, out, None, ws, 1 << 30, None)
+        assert rc == want, (a and (a.h, a.w, a.d, a.dtype, a.batch, a.data), want, rc)
+        rc = lib.mr_mutual_nn(pa, R(b), out, out, out, 1 << 20, out, ws, 1 << 30, None)
+        assert rc == want
+        if a is not None:
+            assert lib.mr_workspace_bytes(2, pa, R(b), 0, 8, 4) == 0
+
+
+def test_fast_reciprocal_validation(lib):
+    a, b = M(64, 48), M(64, 48)
+    out = ctypes.c_void_p(FAKE)
+    need = lib.mr_workspace_bytes(2, R(a), R(b), 0, 8, 4)
+    assert need > 0
+    good_ws = ctypes.c_void_p(FAKE)
+    call = lambda stride=8, offset=4, T=10, pairs=out, cap=48, n=out, ws=good_ws, wsb=need: \
+        lib.mr_fast_reciprocal(R(a), R(b), stride, offset, T, pairs, cap, n, None, ws, wsb, None)
+    assert call(stride=0) == PARAM
+    assert call(offset=-1) == PARAM
+    assert call(T=-1) == PARAM
+    assert call(pairs=None) == NULL
+    assert call(n=None) == NULL
+    assert call(cap=47) == CAP
+    assert call(ws=None) == WS
+    assert call(ws=ctypes.c_void_p(FAKE + 64)) == WS
+    assert call(wsb=need - 1) == WS
+    # a larger image or more seeds never needs less workspace
+    big = M(128, 96)
+    assert lib.mr_workspace_bytes(2, R(big), R(big), 0, 8, 4) >= need
+    assert lib.mr_workspace_bytes(2, R(a), R(b), 0, 4, 2) >= need
+
+
+def test_mutual_and_nn_validation(lib):
+    a, b = M(10, 10), M(7, 9)
+    out = ctypes.c_void_p(FAKE)
+    need = lib.mr_workspace_bytes(1, R(a), R(b), 0, 1, 0)
+    assert need > 0
+    assert lib.mr_mutual_nn(R(a), R(b), None, out, out, 63, out, out, need, None) == NULL
+    assert lib.mr_mutual_nn(R(a), R(b), out, out, out, 62, out, out, need, None) == CAP
+    assert lib.mr_mutual_nn(R(a), R(b), out, out, out, 63, out, out, need - 1, None) == WS
+    assert lib.mr_mutual_nn(R(a), R(b), out, out, out, 63, out, None, need, None) == WS
+    nneed = lib.mr_workspace_bytes(0, R(a), R(b), 100, 1, 0)
+    assert lib.mr_nn_argmax(R(a), R(b), None, 99, out, None, out, nneed, None) == PARAM
+    assert lib.mr_nn_argmax(R(a), R(b), None, -1, out, None, out, nneed, None) == PARAM
+    assert lib.mr_nn_argmax(R(a), R(b), None, 100, None, None, out, nneed, None) == NULL
+    assert lib.mr_nn_argmax(R(a), R(b), None, 100, out, None, out, nneed - 8, None) == WS
+    assert lib.mr_nn_argmax(R(a), R(b), None, 0, None, None, None, 0, None) == PARAM
+    empty = M(0, 5, data=None)
+    assert lib.mr_nn_argmax(R(empty), R(b), out, 3, out, None, out, 1 << 20, None) == SHAPE
+    assert lib.mr_workspace_bytes(7, R(a), R(b), 0, 1, 0) == 0
+
+
+def test_profile_end_without_begin(lib):
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    assert lib.mr_profile_end(ctypes.byref(ms), ctypes.byref(n)) == PARAM
