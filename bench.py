@@ -31,7 +31,20 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--main-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib, torch):
+    """A plain device-to-device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}), flush=True)
 
 
 def dev_maps(p, torch, dev):
@@ -132,6 +145,9 @@ def main():
               "(the 64-pair batch would shard by pairs; see the design notes).", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_mb:
+        copy_calibration(args.copy_mb, torch)
+        return
     import dense_grounded_image_amd as mr
     import workloads
     mr.load_library()

@@ -15,6 +15,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # never let the compiler form packed-fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in VGPRs: the argmax epilogue reads them without accvgpr moves
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

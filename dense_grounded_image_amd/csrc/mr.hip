@@ -17,13 +17,14 @@
 //    and MASt3R explained", the paragraph on MASt3R's fast reciprocal
 //    matching).
 //
-// Layout of the MFMA operands (wave64, 16x16 output tile):
-//  - lane l holds output column j = l & 15 (a query) and rows
-//    i = 4*(l >> 4) + v, v = 0..3 (four database rows) of every tile;
-//  - fp32 maps use V_MFMA_F32_16X16X4_F32 in P = ceil(d/4) steps; in step s
-//    lane group g = l >> 4 supplies component c = P*g + s of its row;
-//  - bf16 maps use V_MFMA_F32_16X16X32_BF16 in P = ceil(d/32) steps; in step s
-//    lane group g supplies components 8*(P*g + s) .. +7 (zero past d).
+// Layout of the MFMA operands (wave64, 32x32 output tile):
+//  - lane l holds output column j = l & 31 (a query) and the 16 rows
+//    i = 8*(v >> 2) + 4*(l >> 5) + (v & 3), v = 0..15 (database rows), so the
+//    rows a lane sees rise with v and with the tile index;
+//  - fp32 maps use V_MFMA_F32_32X32X2_F32 in P = ceil(d/2) steps; in step s
+//    lane half h = l >> 5 supplies component c = P*h + s of its row;
+//  - bf16 maps use V_MFMA_F32_32X32X16_BF16 in P = ceil(d/16) steps; in step s
+//    lane half h supplies components 8*(P*h + s) .. +7 (zero past d).
 // A and B use the same component-to-k assignment, products commute, and the
 // accumulation order depends only on k, so s(i, j) is bitwise identical
 // whichever map is the query side.
@@ -37,17 +38,15 @@
 
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;        // waves per workgroup
+constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQT = 8;           // 16-query tiles held per wave
-constexpr int kQBW = 16 * kQT;   // queries per wave
+constexpr int kMaxSegGroups = 256;   // database segments per query block (bounds atomic contention)
 constexpr int kCompactChunk = 2048;  // elements per block in the ordered compaction
 constexpr int kMaxD = 64;
-constexpr int kTargetWaves = 4096;   // 256 CUs x 4 SIMDs x 4 waves
 
 // ---------------------------------------------------------------------------- keys
 
@@ -80,47 +79,113 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
 
 // ---------------------------------------------------------------------------- operands
 
-template <int DT, int P> struct Operand;
+// How a similarity is computed on the matrix cores.
+//  AR_F32 : fp32 maps, fp32 products, V_MFMA_F32_32X32X2_F32 (any d).
+//  AR_BF16: bf16 maps, exact bf16 products, V_MFMA_F32_32X32X16_BF16.
+//  AR_X3  : fp32 maps split exactly into three bf16 parts x = h + m + l (a
+//           preprocessing kernel writes the planes [row][h m l][d]); the six products
+//           hh, hm, mh, mm, hl, lh are summed on V_MFMA_F32_32X32X16_BF16.  The three
+//           dropped products are below 2^-23 |x||y|, so the result matches an fp32
+//           dot product to within its own rounding, at 2.7x the matrix-core rate.
+//           Each map keeps one fixed product order (image 1: h h m h l m, image 2:
+//           h m h l h m over the six product slots), so a pair's products meet at
+//           the same k whichever map is the query: scores stay bitwise symmetric.
+enum Arith { AR_F32 = 0, AR_BF16 = 1, AR_X3 = 2 };
 
-template <int P> struct Operand<MR_F32, P> {
+template <int AR, int P> struct Operand;
+
+template <int P> struct Operand<AR_F32, P> {
     float x[P];
-    __device__ __forceinline__ void load(const void* base, int64_t row, bool valid, int g, int d) {
-        // branch-free: out-of-range components read the row's first element, then select 0
+    __device__ __forceinline__ void load(const void* base, int64_t row, bool valid, int h, int d, int) {
         const float* p = static_cast<const float*>(base) + row * d;
+        if constexpr (P % 4 == 0) {
+            // d == 2P: the lane's P components are contiguous and 16-byte aligned
+            if (d == 2 * P) {
+                const float4* p4 = reinterpret_cast<const float4*>(p + (valid ? P * h : 0));
+#pragma unroll
+                for (int i = 0; i < P / 4; ++i) {
+                    const float4 v = p4[i];
+                    x[4 * i] = valid ? v.x : 0.0f;
+                    x[4 * i + 1] = valid ? v.y : 0.0f;
+                    x[4 * i + 2] = valid ? v.z : 0.0f;
+                    x[4 * i + 3] = valid ? v.w : 0.0f;
+                }
+                return;
+            }
+        }
+        // generic d: out-of-range components read the row's first element, then select 0
 #pragma unroll
         for (int s = 0; s < P; ++s) {
-            const int c = P * g + s;
+            const int c = P * h + s;
             const bool ok = valid && c < d;
             const float t = p[ok ? c : 0];
             x[s] = ok ? t : 0.0f;
         }
     }
-    __device__ __forceinline__ f32x4 mfma(const Operand& b, f32x4 acc) const {
+    __device__ __forceinline__ f32x16 mfma(const Operand& b, f32x16 acc) const {
 #pragma unroll
-        for (int s = 0; s < P; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], b.x[s], acc, 0, 0, 0);
+        for (int s = 0; s < P; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(x[s], b.x[s], acc, 0, 0, 0);
         return acc;
     }
 };
 
-template <int P> struct Operand<MR_BF16, P> {
+template <int P> struct Operand<AR_BF16, P> {
     bf16x8 x[P];
-    __device__ __forceinline__ void load(const void* base, int64_t row, bool valid, int g, int d) {
+    __device__ __forceinline__ void load(const void* base, int64_t row, bool valid, int h, int d, int) {
         const uint16_t* p = static_cast<const uint16_t*>(base) + row * d;
 #pragma unroll
         for (int s = 0; s < P; ++s) {
-            const int c = 8 * (P * g + s);
+            const int c = 8 * (P * h + s);
             const bool ok = valid && c < d;
             u32x4 raw = *reinterpret_cast<const u32x4*>(p + (ok ? c : 0));
             if (!ok) raw = u32x4{0u, 0u, 0u, 0u};
             x[s] = __builtin_bit_cast(bf16x8, raw);
         }
     }
-    __device__ __forceinline__ f32x4 mfma(const Operand& b, f32x4 acc) const {
+    __device__ __forceinline__ f32x16 mfma(const Operand& b, f32x16 acc) const {
 #pragma unroll
-        for (int s = 0; s < P; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x[s], b.x[s], acc, 0, 0, 0);
+        for (int s = 0; s < P; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[s], b.x[s], acc, 0, 0, 0);
         return acc;
     }
 };
+
+// Plane (0 = h, 1 = m, 2 = l) feeding product slot p for a map of the given role.
+__host__ __device__ __forceinline__ constexpr int x3_plane(int role, int p) {
+    return role == 1 ? (p == 2 || p == 5 ? 1 : (p == 4 ? 2 : 0))
+                     : (p == 1 || p == 5 ? 1 : (p == 3 ? 2 : 0));
+}
+
+// P = 6d/16 steps (d = 8P/3); slot q = 16*s + 8*h + e holds product type q / d and
+// component q % d.  The offsets are compile-time for each lane half.
+template <int P> struct Operand<AR_X3, P> {
+    static constexpr int D = 8 * P / 3;
+    bf16x8 x[P];
+    static __device__ __forceinline__ constexpr int offset(int role, int s, int h) {
+        return x3_plane(role, (16 * s + 8 * h) / D) * D + (16 * s + 8 * h) % D;
+    }
+    __device__ __forceinline__ void load(const void* base, int64_t row, bool valid, int h, int, int role) {
+        const uint16_t* p = static_cast<const uint16_t*>(base) + row * 3 * D;
+#pragma unroll
+        for (int s = 0; s < P; ++s) {
+            const int o0 = role == 1 ? offset(1, s, 0) : offset(2, s, 0);
+            const int o1 = role == 1 ? offset(1, s, 1) : offset(2, s, 1);
+            const int off = h ? o1 : o0;
+            u32x4 raw = *reinterpret_cast<const u32x4*>(p + (valid ? off : 0));
+            if (!valid) raw = u32x4{0u, 0u, 0u, 0u};
+            x[s] = __builtin_bit_cast(bf16x8, raw);
+        }
+    }
+    __device__ __forceinline__ f32x16 mfma(const Operand& b, f32x16 acc) const {
+#pragma unroll
+        for (int s = 0; s < P; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[s], b.x[s], acc, 0, 0, 0);
+        return acc;
+    }
+};
+
+template <int AR> struct ArithTraits;
+template <> struct ArithTraits<AR_F32> { using elem = float; static constexpr int row_mult = 1; static constexpr int qt = 4; };
+template <> struct ArithTraits<AR_BF16> { using elem = uint16_t; static constexpr int row_mult = 1; static constexpr int qt = 4; };
+template <> struct ArithTraits<AR_X3> { using elem = uint16_t; static constexpr int row_mult = 3; static constexpr int qt = 2; };
 
 // ---------------------------------------------------------------------------- NN kernel
 
@@ -146,120 +211,380 @@ struct NNArgs {
     int64_t active_stride;
     int32_t* zero_count;       // optional: set this per-pair counter to 0
     int64_t zero_stride;
+    int32_t q_role, db_role;   // 1 = image 1, 2 = image 2 (fixes the split product order)
 };
 
-// Each wave owns (query block, database segment) work items; the number of
-// segments adapts to the live query count so small frontiers still fill the GPU.
-template <int DT, int P>
+// Scores are compared after clearing their 4 lowest fp32 bits; that order, with
+// the lowest row winning ties, is the NN rule of every kernel (both directions use
+// it, so it is symmetric).  The cleared bits carry the row's place in the tile, so
+// one integer max3 tree finds a tile's best candidate.
+__device__ __forceinline__ float trunc4(float s) { return __int_as_float(__float_as_int(s) & ~15); }
+
+// Row (within its 32-row tile) of accumulator register v in lane half h.
+__device__ __forceinline__ int tile_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
+
+// Best key of one tile for one lane: (score bits with 4 low bits cleared) | (15 - v).
+// Valid whenever the lane's best score is >= 0 (float bits then order as ints).
+template <bool RAGGED>
+__device__ __forceinline__ int tile_key(const f32x16& acc, int t, int h, int ndb) {
+    int k[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        k[v] = (__float_as_int(acc[v]) & ~15) | (15 - v);
+        if (RAGGED && t * 32 + tile_row(v, h) >= ndb) k[v] = INT_MIN;
+    }
+    const int a0 = max(max(k[0], k[1]), k[2]), a1 = max(max(k[3], k[4]), k[5]);
+    const int a2 = max(max(k[6], k[7]), k[8]), a3 = max(max(k[9], k[10]), k[11]);
+    const int a4 = max(max(k[12], k[13]), k[14]);
+    return max(max(max(a0, a1), a2), max(max(a3, a4), k[15]));
+}
+
+// The same rule, exactly, for lanes whose best score is negative (rare): a running
+// maximum of trunc4(s) over rows in increasing order, strict '>'.
+template <bool RAGGED>
+__device__ __forceinline__ void tile_exact(const f32x16& acc, int t, int h, int ndb, float& bv, int& bt) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const float s = trunc4(acc[v]);
+        bool gt = s > bv;
+        if (RAGGED) gt = gt && (t * 32 + tile_row(v, h) < ndb);
+        bv = gt ? s : bv;
+        bt = gt ? (t * 16 + v) : bt;
+    }
+}
+
+template <int AR> __device__ __forceinline__ const void* pair_base(const void* p, int64_t elems, int pair) {
+    return static_cast<const typename ArithTraits<AR>::elem*>(p) + pair * elems * ArithTraits<AR>::row_mult;
+}
+
+// Bytes of one map row as the kernel reads it, and an upper bound for the template.
+template <int AR> __device__ __forceinline__ int row_bytes(int d) {
+    return (int)sizeof(typename ArithTraits<AR>::elem) * ArithTraits<AR>::row_mult * d;
+}
+template <int AR, int P> constexpr int max_row_bytes() {
+    return AR == AR_F32 ? 8 * P : (AR == AR_BF16 ? 32 * P : 16 * P);
+}
+
+// One workgroup streams 32-row database tiles through a double-buffered LDS stage
+// (one cooperative 16-byte-chunk copy per tile, one barrier per tile); each of its
+// four waves multiplies the staged tile against its own QT query tiles held in
+// registers and keeps a per-lane running best.
+template <int AR, int P, bool EXACT>
+__device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb,
+                                             char* lds, const Operand<AR, P> (&q)[ArithTraits<AR>::qt],
+                                             int nact, int h, int jl, int d, int role,
+                                             int (&bk)[ArithTraits<AR>::qt], int (&bt)[ArithTraits<AR>::qt],
+                                             float (&bv)[ArithTraits<AR>::qt]) {
+    constexpr int QT = ArithTraits<AR>::qt;
+    constexpr int MAXC = (32 * max_row_bytes<AR, P>() / 16 + kThreads - 1) / kThreads;
+    constexpr int BUF = 32 * max_row_bytes<AR, P>();
+    const int tile_bytes = 32 * rb;
+    const int nchunk = tile_bytes >> 4;
+    const int nt = t1 - t0;
+    u32x4 stage0[MAXC], stage1[MAXC];
+
+    auto fetch = [&](int t, u32x4 (&stage)[MAXC]) {
+        const int64_t tb = (int64_t)t * tile_bytes;
+        const int64_t limit = (int64_t)ndb * rb;   // bytes of real rows
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = threadIdx.x + c * kThreads;
+            const int64_t off = tb + (int64_t)ch * 16;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (ch < nchunk && off + 16 <= limit) {
+                v = *reinterpret_cast<const u32x4*>(dbytes + off);
+            } else if (ch < nchunk && off < limit) {
+                // the chunk holding the end of the last row (row sizes are multiples of 4 bytes)
+                const uint32_t* w = reinterpret_cast<const uint32_t*>(dbytes + off);
+                const int nw = (int)((limit - off) >> 2);
+                v.x = w[0];
+                if (nw > 1) v.y = w[1];
+                if (nw > 2) v.z = w[2];
+            }
+            stage[c] = v;
+        }
+    };
+    auto put = [&](int buf, const u32x4 (&stage)[MAXC]) {
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = threadIdx.x + c * kThreads;
+            if (ch < nchunk) *reinterpret_cast<u32x4*>(lds + buf * BUF + ch * 16) = stage[c];
+        }
+    };
+
+    auto compute = [&](int i) {
+        const int t = t0 + i;
+        const bool ragged = (t + 1) * 32 > ndb;
+        Operand<AR, P> r;
+        r.load(lds + (i & 1) * BUF, jl, true, h, d, role);
+#pragma unroll
+        for (int j = 0; j < QT; ++j) {
+            if (j < nact) {
+                f32x16 acc = {};
+                acc = r.mfma(q[j], acc);
+                if (EXACT) {
+                    if (ragged) tile_exact<true>(acc, t, h, ndb, bv[j], bt[j]);
+                    else tile_exact<false>(acc, t, h, ndb, bv[j], bt[j]);
+                } else {
+                    const int km = ragged ? tile_key<true>(acc, t, h, ndb) : tile_key<false>(acc, t, h, ndb);
+                    const bool gt = km > (bk[j] | 15);   // strictly better score: earliest tile wins ties
+                    bk[j] = gt ? km : bk[j];
+                    bt[j] = gt ? t : bt[j];
+                }
+            }
+        }
+    };
+
+    if (nt <= 0) return;
+    // tile i is fetched into registers two iterations before it is needed, written to
+    // LDS buffer i&1 at the end of iteration i-1, and read after that iteration's barrier
+    fetch(t0, stage0);
+    put(0, stage0);
+    if (nt > 1) fetch(t0 + 1, stage1);
+    __syncthreads();
+    for (int i = 0; i < nt; i += 2) {
+        if (i + 2 < nt) fetch(t0 + i + 2, stage0);
+        compute(i);
+        if (i + 1 < nt) put(1, stage1);
+        __syncthreads();
+        if (i + 1 >= nt) break;
+        if (i + 3 < nt) fetch(t0 + i + 3, stage1);
+        compute(i + 1);
+        if (i + 2 < nt) put(0, stage0);
+        __syncthreads();
+    }
+}
+
+// Small frontiers (all live queries fit in one wave): every wave of the workgroup
+// holds the same queries and streams its own database segment straight from global
+// memory, one tile ahead in registers, with no LDS staging and no barriers.
+template <int AR, int P, bool EXACT>
+__device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1, int ndb,
+                                              const Operand<AR, P> (&q)[ArithTraits<AR>::qt],
+                                              int nact, int h, int jl, int d, int role,
+                                              int (&bk)[ArithTraits<AR>::qt], int (&bt)[ArithTraits<AR>::qt],
+                                              float (&bv)[ArithTraits<AR>::qt]) {
+    constexpr int QT = ArithTraits<AR>::qt;
+    if (t0 >= t1) return;
+    auto row_of = [&](int t) { return (int64_t)t * 32 + jl; };
+    Operand<AR, P> rn;
+    rn.load(dbase, row_of(t0) < ndb ? row_of(t0) : 0, row_of(t0) < ndb, h, d, role);
+    for (int t = t0; t < t1; ++t) {
+        const Operand<AR, P> r = rn;
+        const int tn = t + 1 < t1 ? t + 1 : t;
+        rn.load(dbase, row_of(tn) < ndb ? row_of(tn) : 0, row_of(tn) < ndb, h, d, role);
+        const bool ragged = (t + 1) * 32 > ndb;
+#pragma unroll
+        for (int j = 0; j < QT; ++j) {
+            if (j < nact) {
+                f32x16 acc = {};
+                acc = r.mfma(q[j], acc);
+                if (EXACT) {
+                    if (ragged) tile_exact<true>(acc, t, h, ndb, bv[j], bt[j]);
+                    else tile_exact<false>(acc, t, h, ndb, bv[j], bt[j]);
+                } else {
+                    const int km = ragged ? tile_key<true>(acc, t, h, ndb) : tile_key<false>(acc, t, h, ndb);
+                    const bool gt = km > (bk[j] | 15);
+                    bk[j] = gt ? km : bk[j];
+                    bt[j] = gt ? t : bt[j];
+                }
+            }
+        }
+    }
+}
+
+// Work item = (query group, database segment).  A query group is four query blocks of
+// 32*QT queries, one per wave; the segment is a contiguous range of 32-row tiles.
+// The number of segments follows the live query count (read on the device), so a
+// shrinking frontier still spreads over the whole GPU; it is a multiple of 8 when
+// possible so that each XCD keeps streaming the same eighth of the database through
+// its own L2.  Every wave leaves one atomicMax per query and item.
+template <int AR, int P>
 __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
+    constexpr int QT = ArithTraits<AR>::qt;
+    constexpr int QB = 32 * QT;          // queries per wave
+    constexpr int QG = kWaves * QB;      // queries per workgroup item
+    constexpr int LDS_TILES = 2 * 32 * max_row_bytes<AR, P>();
+    constexpr int LDS_RED = kWaves * QB * 8;
+    __shared__ __attribute__((aligned(16))) char lds[LDS_TILES > LDS_RED ? LDS_TILES : LDS_RED];
     const int lane = threadIdx.x & 63;
-    const int g = lane >> 4;
-    const int jl = lane & 15;
+    const int h = lane >> 5;
+    const int jl = lane & 31;
+    const int wv = threadIdx.x >> 6;
     const int pair = blockIdx.y;
     const int n = a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (a.active_out) a.active_out[pair * a.active_stride] = n;
         if (a.zero_count) a.zero_count[pair * a.zero_stride] = 0;
     }
-    const int ntiles = (a.ndb + 15) >> 4;
-    const int qblocks = (n + kQBW - 1) / kQBW;
-    if (qblocks == 0 || ntiles == 0) return;
-    const int total_waves = gridDim.x * kWaves;
-    int nseg = total_waves / qblocks;
-    nseg = nseg < 1 ? 1 : (nseg > ntiles ? ntiles : nseg);
-    const int items = qblocks * nseg;
-    const int full_tiles = a.ndb >> 4;
+    const int ntiles = (a.ndb + 31) >> 5;
+    const int qgroups = (n + QG - 1) / QG;
+    if (qgroups == 0 || ntiles == 0) return;
+    int nsg = (int)gridDim.x / qgroups;
+    const int sg_cap = ntiles < kMaxSegGroups ? ntiles : kMaxSegGroups;
+    nsg = nsg < 1 ? 1 : (nsg > sg_cap ? sg_cap : nsg);
+    if (nsg >= 8) nsg &= ~7;
+    const int items = qgroups * nsg;
+    const void* qbase = pair_base<AR>(a.qmap, a.q_pair_elems, pair);
+    const char* dbytes = static_cast<const char*>(pair_base<AR>(a.dbmap, a.db_pair_elems, pair));
+    const int rb = row_bytes<AR>(a.d);
 
-    const void* qbase = (DT == MR_F32)
-        ? (const void*)(static_cast<const float*>(a.qmap) + pair * a.q_pair_elems)
-        : (const void*)(static_cast<const uint16_t*>(a.qmap) + pair * a.q_pair_elems);
-    const void* dbase = (DT == MR_F32)
-        ? (const void*)(static_cast<const float*>(a.dbmap) + pair * a.db_pair_elems)
-        : (const void*)(static_cast<const uint16_t*>(a.dbmap) + pair * a.db_pair_elems);
-
-    for (int it = blockIdx.x * kWaves + (threadIdx.x >> 6); it < items; it += total_waves) {
-        const int seg = it / qblocks;
-        const int qb = it - seg * qblocks;
-
-        // queries of this block -> B operands
-        Operand<DT, P> q[kQT];
+    auto load_queries = [&](Operand<AR, P> (&q)[QT], int q0, int nact) {
 #pragma unroll
-        for (int j = 0; j < kQT; ++j) {
-            const int qp = qb * kQBW + j * 16 + jl;
-            int64_t row = qp;
-            bool valid = qp < n;
-            if (valid && a.qsrc == Q_LIST)
-                row = static_cast<const int32_t*>(a.qlist)[pair * a.qlist_stride + qp];
-            else if (valid && a.qsrc == Q_KEYS)
-                row = key_row(static_cast<const uint64_t*>(a.qlist)[pair * a.qlist_stride + qp]);
-            valid = valid && row >= 0 && row < a.nq_rows;
-            q[j].load(qbase, valid ? row : 0, valid, g, a.d);
-        }
-
-        const int t0 = (int)((int64_t)seg * ntiles / nseg);
-        const int t1 = (int)((int64_t)(seg + 1) * ntiles / nseg);
-        const int tf = t1 < full_tiles ? t1 : full_tiles;
-
-        float bv[kQT];
-        int bt[kQT];
-#pragma unroll
-        for (int j = 0; j < kQT; ++j) { bv[j] = -INFINITY; bt[j] = -1; }
-
-        // full tiles: every row valid
-        for (int t = t0; t < tf; ++t) {
-            Operand<DT, P> r;
-            r.load(dbase, (int64_t)t * 16 + jl, true, g, a.d);
-#pragma unroll
-            for (int j = 0; j < kQT; ++j) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = r.mfma(q[j], acc);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float s = acc[v];
-                    const bool gt = s > bv[j];
-                    bv[j] = gt ? s : bv[j];
-                    bt[j] = gt ? (t * 4 + v) : bt[j];
-                }
+        for (int j = 0; j < QT; ++j) {
+            if (j < nact) {
+                const int qp = q0 + j * 32 + jl;
+                int64_t row = qp;
+                bool valid = qp < n;
+                if (valid && a.qsrc == Q_LIST)
+                    row = static_cast<const int32_t*>(a.qlist)[pair * a.qlist_stride + qp];
+                else if (valid && a.qsrc == Q_KEYS)
+                    row = key_row(static_cast<const uint64_t*>(a.qlist)[pair * a.qlist_stride + qp]);
+                valid = valid && row >= 0 && row < a.nq_rows;
+                q[j].load(qbase, valid ? row : 0, valid, h, a.d, a.q_role);
             }
         }
-        // the ragged last tile
-        if (tf < t1) {
-            const int t = tf;
-            const int64_t rrow = (int64_t)t * 16 + jl;
-            Operand<DT, P> r;
-            r.load(dbase, rrow < a.ndb ? rrow : 0, rrow < a.ndb, g, a.d);
+    };
+    auto finish = [&](int (&bk)[QT], int (&bt)[QT], float (&sv)[QT], int (&rw)[QT]) {
 #pragma unroll
-            for (int j = 0; j < kQT; ++j) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = r.mfma(q[j], acc);
+        for (int j = 0; j < QT; ++j) {
+            sv[j] = __int_as_float(bk[j] & ~15);
+            rw[j] = bt[j] >= 0 ? bt[j] * 32 + tile_row(15 - (bk[j] & 15), h) : -1;
+        }
+    };
+    auto finish_exact = [&](const float (&bv)[QT], const int (&bx)[QT], float (&sv)[QT], int (&rw)[QT]) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const bool ok = t * 16 + 4 * g + v < a.ndb;
-                    const float s = acc[v];
-                    const bool gt = ok && s > bv[j];
-                    bv[j] = gt ? s : bv[j];
-                    bt[j] = gt ? (t * 4 + v) : bt[j];
-                }
+        for (int j = 0; j < QT; ++j) {
+            sv[j] = bv[j];
+            rw[j] = bx[j] >= 0 ? (bx[j] >> 4) * 32 + tile_row(bx[j] & 15, h) : -1;
+        }
+    };
+
+    if (n <= QB) {
+        // small frontier: the four waves share the queries and split the database
+        const int cap = (ntiles + kWaves - 1) / kWaves < kMaxSegGroups ? (ntiles + kWaves - 1) / kWaves
+                                                                       : kMaxSegGroups;
+        const int ngroups = (int)gridDim.x < cap ? (int)gridDim.x : cap;
+        const int nact = (n + 31) >> 5;
+        uint64_t* red = reinterpret_cast<uint64_t*>(lds);
+        for (int item = blockIdx.x; item < ngroups; item += gridDim.x) {
+            Operand<AR, P> q[QT];
+            load_queries(q, 0, nact);
+            const int seg = item * kWaves + wv, nseg = ngroups * kWaves;
+            const int t0 = (int)((int64_t)seg * ntiles / nseg);
+            const int t1 = (int)((int64_t)(seg + 1) * ntiles / nseg);
+            int bk[QT], bt[QT];
+            float bv[QT];
+#pragma unroll
+            for (int j = 0; j < QT; ++j) { bk[j] = INT_MIN; bt[j] = -1; bv[j] = -INFINITY; }
+            stream_direct<AR, P, false>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
+            float sv[QT];
+            int rw[QT];
+            finish(bk, bt, sv, rw);
+            bool neg = false;
+#pragma unroll
+            for (int j = 0; j < QT; ++j) neg = neg || (j < nact && bk[j] < 0 && t0 < t1);
+            if (__ballot(neg) != 0) {
+                int bx[QT];
+#pragma unroll
+                for (int j = 0; j < QT; ++j) bx[j] = -1;
+                stream_direct<AR, P, true>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, bk, bx, bv);
+                finish_exact(bv, bx, sv, rw);
             }
+#pragma unroll
+            for (int j = 0; j < QT; ++j) {
+                uint64_t key = rw[j] >= 0 ? pack_key(sv[j], (uint32_t)rw[j]) : 0;
+                const uint64_t o = shfl_xor_u64(key, 32);
+                key = o > key ? o : key;
+                if (h == 0) red[wv * QB + j * 32 + jl] = j < nact ? key : 0;
+            }
+            __syncthreads();
+            if (threadIdx.x < QB) {
+                uint64_t key = red[threadIdx.x];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w) key = red[w * QB + threadIdx.x] > key ? red[w * QB + threadIdx.x] : key;
+                if ((int)threadIdx.x < n && key != 0)
+                    atomicMax(reinterpret_cast<unsigned long long*>(&a.keys[pair * a.keys_stride + threadIdx.x]),
+                              (unsigned long long)key);
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int qg = item / nsg;
+        const int sg = item - qg * nsg;
+        const int q0 = qg * QG + wv * QB;                 // this wave's first query
+        const int left = n - q0;
+        const int nact = left <= 0 ? 0 : (left >= QB ? QT : (left + 31) >> 5);
+
+        Operand<AR, P> q[QT];
+        load_queries(q, q0, nact);
+        const int t0 = (int)((int64_t)sg * ntiles / nsg);
+        const int t1 = (int)((int64_t)(sg + 1) * ntiles / nsg);
+
+        int bk[QT], bt[QT];
+        float bv[QT];
+#pragma unroll
+        for (int j = 0; j < QT; ++j) { bk[j] = INT_MIN; bt[j] = -1; bv[j] = -INFINITY; }
+        stream_tiles<AR, P, false>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
+
+        // (score, row) per lane and query tile
+        float sv[QT];
+        int rw[QT];
+        finish(bk, bt, sv, rw);
+        bool neg = false;
+#pragma unroll
+        for (int j = 0; j < QT; ++j) neg = neg || (j < nact && bk[j] < 0);
+        if (__syncthreads_or(neg)) {
+            // some lane's best score is negative, where float bits do not order as
+            // integers: the workgroup streams its segment again with the exact comparison
+            int bx[QT];
+#pragma unroll
+            for (int j = 0; j < QT; ++j) bx[j] = -1;
+            stream_tiles<AR, P, true>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bx, bv);
+            finish_exact(bv, bx, sv, rw);
         }
 
-        // merge the four lane groups holding each query, then across segments
+        // merge the two lane halves of each query, then across items with atomicMax
 #pragma unroll
-        for (int j = 0; j < kQT; ++j) {
-            uint64_t key = 0;
-            if (bt[j] >= 0) {
-                const uint32_t row = (uint32_t)((bt[j] >> 2) * 16 + 4 * g + (bt[j] & 3));
-                key = pack_key(bv[j], row);
-            }
-            uint64_t o = shfl_xor_u64(key, 16);
+        for (int j = 0; j < QT; ++j) {
+            uint64_t key = rw[j] >= 0 ? pack_key(sv[j], (uint32_t)rw[j]) : 0;
+            const uint64_t o = shfl_xor_u64(key, 32);
             key = o > key ? o : key;
-            o = shfl_xor_u64(key, 32);
-            key = o > key ? o : key;
-            const int qp = qb * kQBW + j * 16 + jl;
-            if (g == 0 && qp < n && key != 0)
+            const int qp = q0 + j * 32 + jl;
+            if (h == 0 && j < nact && qp < n && key != 0)
                 atomicMax(reinterpret_cast<unsigned long long*>(&a.keys[pair * a.keys_stride + qp]),
                           (unsigned long long)key);
         }
+    }
+}
+
+// fp32 map -> planes [row][h, m, l][d] of bf16 with x = h + m + l (round to nearest
+// even at each step; every difference is exact in fp32).
+__device__ __forceinline__ uint16_t bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_widen(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__global__ void split_x3_kernel(const float* __restrict__ x, int64_t rows, int d, uint16_t* __restrict__ out) {
+    const int64_t n = rows * d;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / d;
+        const int c = (int)(i - r * d);
+        const float v = x[i];
+        const uint16_t hb = bf16_rne(v);
+        const float r1 = v - bf16_widen(hb);
+        const uint16_t mb = bf16_rne(r1);
+        const float r2 = r1 - bf16_widen(mb);
+        const uint16_t lb = bf16_rne(r2);
+        uint16_t* o = out + r * 3 * d;
+        o[c] = hb;
+        o[d + c] = mb;
+        o[2 * d + c] = lb;
     }
 }
 
@@ -490,26 +815,71 @@ int grid_1d(int64_t n, int threads = 256, int cap = 1 << 24) {
 
 int dev_err() { return hipGetLastError() == hipSuccess ? MR_OK : MR_ERR_DEVICE; }
 
-template <int DT, int P>
-void launch_nn_t(const NNArgs& a, dim3 grid, hipStream_t st) {
-    hipLaunchKernelGGL((nn_argmax_kernel<DT, P>), grid, dim3(kThreads), 0, st, a);
+// Workgroups per pair: as many as the GPU holds at once (all pairs together); a
+// multiple of 8 when large, so that work items keep to one XCD's share of the
+// database rows.
+// Workgroups per pair: as many as the GPU holds at once (all pairs together); a
+// multiple of 8 when large, so that work items keep to one XCD's share of the
+// database rows.
+template <int AR, int P>
+int nn_grid_x(int batch) {
+    static int resident = 0;
+    if (resident == 0) {
+        int dev = 0, cus = 256, per_cu = 0;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            hipDeviceProp_t prop;
+            if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
+        }
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nn_argmax_kernel<AR, P>, kThreads, 0) !=
+                hipSuccess || per_cu < 1)
+            per_cu = 1;
+        resident = cus * per_cu;
+    }
+    int g = resident / (batch > 0 ? batch : 1);
+    if (g >= 64) g &= ~7;
+    return g < 1 ? 1 : g;
 }
 
-int launch_nn(const NNArgs& a, int dtype, int batch, int gridx, hipStream_t st) {
-    const dim3 grid(gridx, batch);
+template <int AR, int P>
+void launch_nn_t(const NNArgs& a, int batch, hipStream_t st) {
+    hipLaunchKernelGGL((nn_argmax_kernel<AR, P>), dim3(nn_grid_x<AR, P>(batch), batch), dim3(kThreads), 0, st, a);
+}
+
+// Arithmetic for a map dtype and descriptor length (see the Arith enum).
+int choose_arith(int dtype, int d) {
+    if (dtype == MR_BF16) return AR_BF16;
+    return (d % 8 == 0 && d <= 32) ? AR_X3 : AR_F32;
+}
+
+int launch_nn(const NNArgs& a, int ar, int batch, hipStream_t st) {
     const bool prof = g_prof.on && g_prof.used < g_prof.cap;
     if (prof && hipEventRecord(g_prof.ev[2 * g_prof.used], st) != hipSuccess) return MR_ERR_DEVICE;
-    if (dtype == MR_F32) {
-        switch ((a.d + 3) / 4) {
-#define MR_CASE(p) case p: launch_nn_t<MR_F32, p>(a, grid, st); break;
+    if (ar == AR_F32) {
+        switch ((a.d + 1) / 2) {
+#define MR_CASE(p) case p: launch_nn_t<AR_F32, p>(a, batch, st); break;
             MR_CASE(1) MR_CASE(2) MR_CASE(3) MR_CASE(4) MR_CASE(5) MR_CASE(6) MR_CASE(7) MR_CASE(8)
             MR_CASE(9) MR_CASE(10) MR_CASE(11) MR_CASE(12) MR_CASE(13) MR_CASE(14) MR_CASE(15) MR_CASE(16)
+            MR_CASE(17) MR_CASE(18) MR_CASE(19) MR_CASE(20) MR_CASE(21) MR_CASE(22) MR_CASE(23) MR_CASE(24)
+            MR_CASE(25) MR_CASE(26) MR_CASE(27) MR_CASE(28) MR_CASE(29) MR_CASE(30) MR_CASE(31) MR_CASE(32)
 #undef MR_CASE
             default: return MR_ERR_SHAPE;
         }
+    } else if (ar == AR_BF16) {
+        switch ((a.d + 15) / 16) {
+            case 1: launch_nn_t<AR_BF16, 1>(a, batch, st); break;
+            case 2: launch_nn_t<AR_BF16, 2>(a, batch, st); break;
+            case 3: launch_nn_t<AR_BF16, 3>(a, batch, st); break;
+            case 4: launch_nn_t<AR_BF16, 4>(a, batch, st); break;
+            default: return MR_ERR_SHAPE;
+        }
     } else {
-        if (a.d <= 32) launch_nn_t<MR_BF16, 1>(a, grid, st);
-        else launch_nn_t<MR_BF16, 2>(a, grid, st);
+        switch (a.d) {
+            case 8: launch_nn_t<AR_X3, 3>(a, batch, st); break;
+            case 16: launch_nn_t<AR_X3, 6>(a, batch, st); break;
+            case 24: launch_nn_t<AR_X3, 9>(a, batch, st); break;
+            case 32: launch_nn_t<AR_X3, 12>(a, batch, st); break;
+            default: return MR_ERR_SHAPE;
+        }
     }
     if (dev_err()) return MR_ERR_DEVICE;
     if (prof) {
@@ -519,35 +889,46 @@ int launch_nn(const NNArgs& a, int dtype, int batch, int gridx, hipStream_t st) 
     return MR_OK;
 }
 
-// Workgroups per pair: enough waves for every (query block, segment) item to fill the GPU.
-int nn_grid_x(int64_t n_queries, int batch) {
-    const int64_t per_pair = (kTargetWaves + batch - 1) / batch;
-    int64_t qblocks = (n_queries + kQBW - 1) / kQBW;
-    int64_t waves = per_pair > qblocks ? per_pair : qblocks;
-    int64_t wgs = (waves + kWaves - 1) / kWaves;
-    if (wgs < 1) wgs = 1;
-    return (int)(wgs > 65535 ? 65535 : wgs);
-}
-
-NNArgs nn_args(const mr_map* q, const mr_map* db) {
+// Kernel arguments for queries taken from map q (role q_role) against map db.
+// qdata / dbdata are the maps themselves, or their split planes for AR_X3.
+NNArgs nn_args(const mr_map* q, const void* qdata, int q_role, const mr_map* db, const void* dbdata, int db_role) {
     NNArgs a;
     memset(&a, 0, sizeof(a));
-    a.qmap = q->data;
-    a.dbmap = db->data;
+    a.qmap = qdata;
+    a.dbmap = dbdata;
     a.q_pair_elems = npix(q) * q->d;
     a.db_pair_elems = npix(db) * db->d;
     a.nq_rows = (int32_t)npix(q);
     a.ndb = (int32_t)npix(db);
     a.d = q->d;
+    a.q_role = q_role;
+    a.db_role = db_role;
     return a;
 }
 
+size_t x3_bytes(const mr_map* m) {
+    return choose_arith(m->dtype, m->d) == AR_X3 ? align256((size_t)m->batch * npix(m) * 3 * m->d * 2) : 0;
+}
+
+// Operand source for a map: the map itself, or its split planes written into `planes`.
+int prepare_map(const mr_map* m, void* planes, const void** data, hipStream_t st) {
+    *data = m->data;
+    if (choose_arith(m->dtype, m->d) != AR_X3 || npix(m) == 0) return MR_OK;
+    const int64_t rows = (int64_t)m->batch * npix(m);
+    hipLaunchKernelGGL(split_x3_kernel, dim3(grid_1d(rows * m->d)), dim3(256), 0, st,
+                       static_cast<const float*>(m->data), rows, m->d, static_cast<uint16_t*>(planes));
+    *data = planes;
+    return dev_err();
+}
+
 struct FastLayout {
-    size_t keys_f[2], keys_b[2], front[2], cnt[2], state, blk, total;
+    size_t keys_f[2], keys_b[2], front[2], cnt[2], state, blk, x3a, x3b, total;
 };
 
-FastLayout fast_layout(int batch, int64_t nseeds, int64_t n1) {
+FastLayout fast_layout(const mr_map* a, const mr_map* b, int64_t nseeds) {
     FastLayout L;
+    const int batch = a->batch;
+    const int64_t n1 = npix(a);
     size_t off = 0;
     const size_t slots = (size_t)batch * (size_t)(nseeds > 0 ? nseeds : 1);
     for (int i = 0; i < 2; ++i) { L.keys_f[i] = off; off = align256(off + slots * 8); }
@@ -556,18 +937,36 @@ FastLayout fast_layout(int batch, int64_t nseeds, int64_t n1) {
     for (int i = 0; i < 2; ++i) { L.cnt[i] = off; off = align256(off + (size_t)batch * 4); }
     L.state = off; off = align256(off + (size_t)batch * (size_t)(n1 > 0 ? n1 : 1) * 4);
     L.blk = off; off = align256(off + (size_t)batch * (size_t)(nblk_of(n1) > 0 ? nblk_of(n1) : 1) * 4);
+    L.x3a = off; off += x3_bytes(a);
+    L.x3b = off; off += x3_bytes(b);
     L.total = off;
     return L;
 }
 
-struct MutualLayout { size_t keys_ab, keys_ba, blk, total; };
+struct MutualLayout { size_t keys_ab, keys_ba, blk, x3a, x3b, total; };
 
-MutualLayout mutual_layout(int batch, int64_t na, int64_t nb) {
+MutualLayout mutual_layout(const mr_map* a, const mr_map* b) {
     MutualLayout L;
+    const int batch = a->batch;
+    const int64_t na = npix(a), nb = npix(b);
     size_t off = 0;
     L.keys_ab = off; off = align256(off + (size_t)batch * (size_t)(na > 0 ? na : 1) * 8);
     L.keys_ba = off; off = align256(off + (size_t)batch * (size_t)(nb > 0 ? nb : 1) * 8);
     L.blk = off; off = align256(off + (size_t)batch * (size_t)(nblk_of(na) > 0 ? nblk_of(na) : 1) * 4);
+    L.x3a = off; off += x3_bytes(a);
+    L.x3b = off; off += x3_bytes(b);
+    L.total = off;
+    return L;
+}
+
+struct NNLayout { size_t keys, x3q, x3db, total; };
+
+NNLayout nn_layout(const mr_map* q, const mr_map* db, int64_t n_q) {
+    NNLayout L;
+    size_t off = 0;
+    L.keys = off; off = align256(off + (size_t)q->batch * (size_t)(n_q > 0 ? n_q : 1) * 8);
+    L.x3q = off; off += x3_bytes(q);
+    L.x3db = off; off += x3_bytes(db);
     L.total = off;
     return L;
 }
@@ -611,13 +1010,13 @@ size_t mr_workspace_bytes(int op, const mr_map* a, const mr_map* b, int64_t n_q,
     switch (op) {
         case MR_OP_NN_ARGMAX:
             if (n_q < 0) return 0;
-            return align256((size_t)a->batch * (size_t)(n_q > 0 ? n_q : 1) * 8);
+            return nn_layout(a, b, n_q).total;
         case MR_OP_MUTUAL_NN:
-            return mutual_layout(a->batch, npix(a), npix(b)).total;
+            return mutual_layout(a, b).total;
         case MR_OP_FAST_RECIPROCAL: {
             const int64_t ns = seed_count(a->h, a->w, stride, offset);
             if (ns < 0) return 0;
-            return fast_layout(a->batch, ns, npix(a)).total;
+            return fast_layout(a, b, ns).total;
         }
         default: return 0;
     }
@@ -632,21 +1031,24 @@ int mr_nn_argmax(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_
     if (n_q == 0) return MR_OK;
     if (npix(q) == 0) return MR_ERR_SHAPE;  // query ids cannot name a row of an empty map
     if (!out_idx) return MR_ERR_NULL;
-    const size_t need = align256((size_t)q->batch * (size_t)n_q * 8);
-    if ((rc = check_ws(ws, ws_bytes, need))) return rc;
+    const NNLayout L = nn_layout(q, db, n_q);
+    if ((rc = check_ws(ws, ws_bytes, L.total))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    uint64_t* keys = static_cast<uint64_t*>(ws);
+    uint64_t* keys = at<uint64_t>(ws, L.keys);
     const int64_t tot = (int64_t)q->batch * n_q;
     hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(tot)), dim3(256), 0, st, keys, tot, (uint64_t)0);
     if (dev_err()) return MR_ERR_DEVICE;
-    NNArgs a = nn_args(q, db);
+    const void *qd, *dd;
+    if ((rc = prepare_map(q, at<void>(ws, L.x3q), &qd, st))) return rc;
+    if ((rc = prepare_map(db, at<void>(ws, L.x3db), &dd, st))) return rc;
+    NNArgs a = nn_args(q, qd, 1, db, dd, 2);
     a.qsrc = q_idx ? Q_LIST : Q_ALL;
     a.qlist = q_idx;
     a.qlist_stride = n_q;
     a.host_count = (int32_t)n_q;
     a.keys = keys;
     a.keys_stride = n_q;
-    if ((rc = launch_nn(a, q->dtype, q->batch, nn_grid_x(n_q, q->batch), st))) return rc;
+    if ((rc = launch_nn(a, choose_arith(q->dtype, q->d), q->batch, st))) return rc;
     hipLaunchKernelGGL(decode_keys_kernel, dim3(grid_1d(tot)), dim3(256), 0, st, keys, tot, out_idx, out_score);
     return dev_err();
 }
@@ -659,28 +1061,32 @@ int mr_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_b
     const int64_t na = npix(a), nb = npix(b);
     const int64_t bound = na < nb ? na : nb;
     if (cap < bound) return MR_ERR_CAPACITY;
-    const MutualLayout L = mutual_layout(a->batch, na, nb);
+    const MutualLayout L = mutual_layout(a, b);
     if ((rc = check_ws(ws, ws_bytes, L.total))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int batch = a->batch;
+    const int ar = choose_arith(a->dtype, a->d);
     uint64_t* kab = at<uint64_t>(ws, L.keys_ab);
     uint64_t* kba = at<uint64_t>(ws, L.keys_ba);
     int32_t* blk = at<int32_t>(ws, L.blk);
     hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(batch * na)), dim3(256), 0, st, kab, batch * na, (uint64_t)0);
     hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(batch * nb)), dim3(256), 0, st, kba, batch * nb, (uint64_t)0);
     if (dev_err()) return MR_ERR_DEVICE;
-    NNArgs f = nn_args(a, b);
+    const void *ad, *bd;
+    if ((rc = prepare_map(a, at<void>(ws, L.x3a), &ad, st))) return rc;
+    if ((rc = prepare_map(b, at<void>(ws, L.x3b), &bd, st))) return rc;
+    NNArgs f = nn_args(a, ad, 1, b, bd, 2);
     f.qsrc = Q_ALL;
     f.host_count = (int32_t)na;
     f.keys = kab;
     f.keys_stride = na;
-    if ((rc = launch_nn(f, a->dtype, batch, nn_grid_x(na, batch), st))) return rc;
-    NNArgs r = nn_args(b, a);
+    if ((rc = launch_nn(f, ar, batch, st))) return rc;
+    NNArgs r = nn_args(b, bd, 2, a, ad, 1);
     r.qsrc = Q_ALL;
     r.host_count = (int32_t)nb;
     r.keys = kba;
     r.keys_stride = nb;
-    if ((rc = launch_nn(r, a->dtype, batch, nn_grid_x(nb, batch), st))) return rc;
+    if ((rc = launch_nn(r, ar, batch, st))) return rc;
     hipLaunchKernelGGL(decode_keys_kernel, dim3(grid_1d(batch * na)), dim3(256), 0, st, kab, batch * na, nn_ab,
                        (float*)nullptr);
     hipLaunchKernelGGL(decode_keys_kernel, dim3(grid_1d(batch * nb)), dim3(256), 0, st, kba, batch * nb, nn_ba,
@@ -704,10 +1110,11 @@ int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t
     const int64_t ns = seed_count(a->h, a->w, stride, offset);
     if (cap < ns) return MR_ERR_CAPACITY;
     const int64_t n1 = npix(a), n2 = npix(b);
-    const FastLayout L = fast_layout(a->batch, ns, n1);
+    const FastLayout L = fast_layout(a, b, ns);
     if ((rc = check_ws(ws, ws_bytes, L.total))) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int batch = a->batch;
+    const int ar = choose_arith(a->dtype, a->d);
     const int64_t slot = ns > 0 ? ns : 1;
     uint64_t* kf[2] = {at<uint64_t>(ws, L.keys_f[0]), at<uint64_t>(ws, L.keys_f[1])};
     uint64_t* kb[2] = {at<uint64_t>(ws, L.keys_b[0]), at<uint64_t>(ws, L.keys_b[1])};
@@ -726,23 +1133,25 @@ int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t
     hipLaunchKernelGGL(fast_init_kernel, dim3(grid_1d(init_n > 0 ? init_n : 1), batch), dim3(256), 0, st, ia);
     if (dev_err()) return MR_ERR_DEVICE;
 
-    if (n1 > 0 && n2 > 0 && ns > 0) {
-        const int gx = nn_grid_x(ns, batch);
+    if (n1 > 0 && n2 > 0 && ns > 0 && max_iters > 0) {
+        const void *ad, *bd;
+        if ((rc = prepare_map(a, at<void>(ws, L.x3a), &ad, st))) return rc;
+        if ((rc = prepare_map(b, at<void>(ws, L.x3b), &bd, st))) return rc;
         const int cyc_grid = grid_1d(ns);
         for (int t = 0; t < max_iters; ++t) {
             const int c = t & 1, x = c ^ 1;
-            NNArgs f = nn_args(a, b);
+            NNArgs f = nn_args(a, ad, 1, b, bd, 2);
             f.qsrc = Q_LIST; f.qlist = fr[c]; f.qlist_stride = slot;
             f.dev_count = cnt[c]; f.count_stride = 1;
             f.keys = kf[c]; f.keys_stride = slot;
             if (iter_active) { f.active_out = iter_active + t; f.active_stride = max_iters; }
             f.zero_count = cnt[x]; f.zero_stride = 1;
-            if ((rc = launch_nn(f, a->dtype, batch, gx, st))) return rc;
-            NNArgs r = nn_args(b, a);
+            if ((rc = launch_nn(f, ar, batch, st))) return rc;
+            NNArgs r = nn_args(b, bd, 2, a, ad, 1);
             r.qsrc = Q_KEYS; r.qlist = kf[c]; r.qlist_stride = slot;
             r.dev_count = cnt[c]; r.count_stride = 1;
             r.keys = kb[c]; r.keys_stride = slot;
-            if ((rc = launch_nn(r, a->dtype, batch, gx, st))) return rc;
+            if ((rc = launch_nn(r, ar, batch, st))) return rc;
             CycleArgs ca;
             ca.front = fr[c]; ca.keys_f = kf[c]; ca.keys_b = kb[c];
             ca.keys_f_next = kf[x]; ca.keys_b_next = kb[x]; ca.front_next = fr[x];
