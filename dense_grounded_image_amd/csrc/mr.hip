@@ -44,7 +44,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxSegGroups = 256;   // database segments per query block (bounds atomic contention)
+constexpr int kMaxSegGroups = 512;   // database segments per query block (bounds atomic contention)
 constexpr int kCompactChunk = 2048;  // elements per block in the ordered compaction
 constexpr int kMaxD = 64;
 
@@ -155,14 +155,30 @@ __host__ __device__ __forceinline__ constexpr int x3_plane(int role, int p) {
                      : (p == 1 || p == 5 ? 1 : (p == 3 ? 2 : 0));
 }
 
+// Exact split of an fp32 value into three bf16 parts v = h + m + l (round to nearest
+// even at each step; each difference is exact in fp32).
+__device__ __forceinline__ void split3(float v, uint16_t& hb, uint16_t& mb, uint16_t& lb) {
+    const __bf16 h = (__bf16)v;
+    const float r1 = v - (float)h;
+    const __bf16 m = (__bf16)r1;
+    const float r2 = r1 - (float)m;
+    const __bf16 l = (__bf16)r2;
+    hb = __builtin_bit_cast(uint16_t, h);
+    mb = __builtin_bit_cast(uint16_t, m);
+    lb = __builtin_bit_cast(uint16_t, l);
+}
+
 // P = 6d/16 steps (d = 8P/3); slot q = 16*s + 8*h + e holds product type q / d and
-// component q % d.  The offsets are compile-time for each lane half.
+// component q % d.  A staged database tile holds each row as planes [h | m | l] of d
+// bf16 (written by the workgroup from the fp32 map); query rows are split in
+// registers.  The offsets are compile-time for each lane half.
 template <int P> struct Operand<AR_X3, P> {
     static constexpr int D = 8 * P / 3;
     bf16x8 x[P];
     static __device__ __forceinline__ constexpr int offset(int role, int s, int h) {
         return x3_plane(role, (16 * s + 8 * h) / D) * D + (16 * s + 8 * h) % D;
     }
+    // from a staged tile: planes [row][3][D]
     __device__ __forceinline__ void load(const void* base, int64_t row, bool valid, int h, int, int role) {
         const uint16_t* p = static_cast<const uint16_t*>(base) + row * 3 * D;
 #pragma unroll
@@ -175,6 +191,37 @@ template <int P> struct Operand<AR_X3, P> {
             x[s] = __builtin_bit_cast(bf16x8, raw);
         }
     }
+    // from an fp32 row of the map, split here
+    __device__ __forceinline__ void load_f32(const float* rowp, bool valid, int h, int role) {
+        uint32_t pl[3][D / 2];   // planes, two bf16 per word
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) {
+            const float4 v = valid ? reinterpret_cast<const float4*>(rowp)[i] : float4{0.f, 0.f, 0.f, 0.f};
+            uint16_t a[3][4];
+            split3(v.x, a[0][0], a[1][0], a[2][0]);
+            split3(v.y, a[0][1], a[1][1], a[2][1]);
+            split3(v.z, a[0][2], a[1][2], a[2][2]);
+            split3(v.w, a[0][3], a[1][3], a[2][3]);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                pl[k][2 * i] = (uint32_t)a[k][0] | ((uint32_t)a[k][1] << 16);
+                pl[k][2 * i + 1] = (uint32_t)a[k][2] | ((uint32_t)a[k][3] << 16);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < P; ++s) {
+            const int o0 = role == 1 ? offset(1, s, 0) : offset(2, s, 0);
+            const int o1 = role == 1 ? offset(1, s, 1) : offset(2, s, 1);
+            u32x4 w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w0 = pl[o0 / D][(o0 % D) / 2 + e];
+                const uint32_t w1 = pl[o1 / D][(o1 % D) / 2 + e];
+                w[e] = h ? w1 : w0;
+            }
+            x[s] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
     __device__ __forceinline__ f32x16 mfma(const Operand& b, f32x16 acc) const {
 #pragma unroll
         for (int s = 0; s < P; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[s], b.x[s], acc, 0, 0, 0);
@@ -185,7 +232,7 @@ template <int P> struct Operand<AR_X3, P> {
 template <int AR> struct ArithTraits;
 template <> struct ArithTraits<AR_F32> { using elem = float; static constexpr int row_mult = 1; static constexpr int qt = 4; };
 template <> struct ArithTraits<AR_BF16> { using elem = uint16_t; static constexpr int row_mult = 1; static constexpr int qt = 4; };
-template <> struct ArithTraits<AR_X3> { using elem = uint16_t; static constexpr int row_mult = 3; static constexpr int qt = 2; };
+template <> struct ArithTraits<AR_X3> { using elem = float; static constexpr int row_mult = 1; static constexpr int qt = 2; };
 
 // ---------------------------------------------------------------------------- NN kernel
 
@@ -261,8 +308,11 @@ template <int AR> __device__ __forceinline__ const void* pair_base(const void* p
 template <int AR> __device__ __forceinline__ int row_bytes(int d) {
     return (int)sizeof(typename ArithTraits<AR>::elem) * ArithTraits<AR>::row_mult * d;
 }
-template <int AR, int P> constexpr int max_row_bytes() {
-    return AR == AR_F32 ? 8 * P : (AR == AR_BF16 ? 32 * P : 16 * P);
+template <int AR, int P> constexpr int max_row_bytes() {        // a map row in memory
+    return AR == AR_F32 ? 8 * P : (AR == AR_BF16 ? 32 * P : 32 * P / 3);
+}
+template <int AR, int P> constexpr int lds_row_bytes() {        // a staged row (X3: three planes)
+    return AR == AR_X3 ? 16 * P : max_row_bytes<AR, P>();
 }
 
 // One workgroup streams 32-row database tiles through a double-buffered LDS stage
@@ -277,7 +327,7 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
                                              float (&bv)[ArithTraits<AR>::qt]) {
     constexpr int QT = ArithTraits<AR>::qt;
     constexpr int MAXC = (32 * max_row_bytes<AR, P>() / 16 + kThreads - 1) / kThreads;
-    constexpr int BUF = 32 * max_row_bytes<AR, P>();
+    constexpr int BUF = 32 * lds_row_bytes<AR, P>();
     const int tile_bytes = 32 * rb;
     const int nchunk = tile_bytes >> 4;
     const int nt = t1 - t0;
@@ -308,7 +358,23 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
             const int ch = threadIdx.x + c * kThreads;
-            if (ch < nchunk) *reinterpret_cast<u32x4*>(lds + buf * BUF + ch * 16) = stage[c];
+            if (ch < nchunk) {
+                if constexpr (AR == AR_X3) {
+                    // four fp32 components -> their h, m, l bf16 in the row's three planes
+                    constexpr int D = 8 * P / 3;
+                    const int r = ch / (D / 4), c0 = (ch - r * (D / 4)) * 4;
+                    uint16_t a[3][4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) split3(__uint_as_float(stage[c][e]), a[0][e], a[1][e], a[2][e]);
+                    char* dst = lds + buf * BUF + r * 6 * D + c0 * 2;
+#pragma unroll
+                    for (int k = 0; k < 3; ++k)
+                        *reinterpret_cast<uint2*>(dst + k * 2 * D) =
+                            uint2{(uint32_t)a[k][0] | ((uint32_t)a[k][1] << 16), (uint32_t)a[k][2] | ((uint32_t)a[k][3] << 16)};
+                } else {
+                    *reinterpret_cast<u32x4*>(lds + buf * BUF + ch * 16) = stage[c];
+                }
+            }
         }
     };
 
@@ -367,12 +433,17 @@ __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1,
     constexpr int QT = ArithTraits<AR>::qt;
     if (t0 >= t1) return;
     auto row_of = [&](int t) { return (int64_t)t * 32 + jl; };
+    auto get = [&](Operand<AR, P>& o, int t) {
+        const int64_t row = row_of(t) < ndb ? row_of(t) : 0;
+        if constexpr (AR == AR_X3) o.load_f32(static_cast<const float*>(dbase) + row * d, row_of(t) < ndb, h, role);
+        else o.load(dbase, row, row_of(t) < ndb, h, d, role);
+    };
     Operand<AR, P> rn;
-    rn.load(dbase, row_of(t0) < ndb ? row_of(t0) : 0, row_of(t0) < ndb, h, d, role);
+    get(rn, t0);
     for (int t = t0; t < t1; ++t) {
         const Operand<AR, P> r = rn;
         const int tn = t + 1 < t1 ? t + 1 : t;
-        rn.load(dbase, row_of(tn) < ndb ? row_of(tn) : 0, row_of(tn) < ndb, h, d, role);
+        get(rn, tn);
         const bool ragged = (t + 1) * 32 > ndb;
 #pragma unroll
         for (int j = 0; j < QT; ++j) {
@@ -404,7 +475,7 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
     constexpr int QT = ArithTraits<AR>::qt;
     constexpr int QB = 32 * QT;          // queries per wave
     constexpr int QG = kWaves * QB;      // queries per workgroup item
-    constexpr int LDS_TILES = 2 * 32 * max_row_bytes<AR, P>();
+    constexpr int LDS_TILES = 2 * 32 * lds_row_bytes<AR, P>();
     constexpr int LDS_RED = kWaves * QB * 8;
     __shared__ __attribute__((aligned(16))) char lds[LDS_TILES > LDS_RED ? LDS_TILES : LDS_RED];
     const int lane = threadIdx.x & 63;
@@ -441,7 +512,10 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
                 else if (valid && a.qsrc == Q_KEYS)
                     row = key_row(static_cast<const uint64_t*>(a.qlist)[pair * a.qlist_stride + qp]);
                 valid = valid && row >= 0 && row < a.nq_rows;
-                q[j].load(qbase, valid ? row : 0, valid, h, a.d, a.q_role);
+                if constexpr (AR == AR_X3)
+                    q[j].load_f32(static_cast<const float*>(qbase) + (valid ? row : 0) * a.d, valid, h, a.q_role);
+                else
+                    q[j].load(qbase, valid ? row : 0, valid, h, a.d, a.q_role);
             }
         }
     };
@@ -460,17 +534,22 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
         }
     };
 
-    if (n <= QB) {
-        // small frontier: the four waves share the queries and split the database
+    if (qgroups == 1) {
+        // small frontier (one query group): the four waves share each query block and
+        // split the database four ways; query blocks are taken one after another
         const int cap = (ntiles + kWaves - 1) / kWaves < kMaxSegGroups ? (ntiles + kWaves - 1) / kWaves
                                                                        : kMaxSegGroups;
         const int ngroups = (int)gridDim.x < cap ? (int)gridDim.x : cap;
-        const int nact = (n + 31) >> 5;
+        const int nqb = (n + QB - 1) / QB;
         uint64_t* red = reinterpret_cast<uint64_t*>(lds);
-        for (int item = blockIdx.x; item < ngroups; item += gridDim.x) {
+        for (int item = blockIdx.x; item < ngroups * nqb; item += gridDim.x) {
+            const int qb = item / ngroups, grp = item - qb * ngroups;
+            const int q0 = qb * QB;
+            const int left = n - q0;
+            const int nact = left >= QB ? QT : (left + 31) >> 5;
             Operand<AR, P> q[QT];
-            load_queries(q, 0, nact);
-            const int seg = item * kWaves + wv, nseg = ngroups * kWaves;
+            load_queries(q, q0, nact);
+            const int seg = grp * kWaves + wv, nseg = ngroups * kWaves;
             const int t0 = (int)((int64_t)seg * ntiles / nseg);
             const int t1 = (int)((int64_t)(seg + 1) * ntiles / nseg);
             int bk[QT], bt[QT];
@@ -503,8 +582,9 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
                 uint64_t key = red[threadIdx.x];
 #pragma unroll
                 for (int w = 1; w < kWaves; ++w) key = red[w * QB + threadIdx.x] > key ? red[w * QB + threadIdx.x] : key;
-                if ((int)threadIdx.x < n && key != 0)
-                    atomicMax(reinterpret_cast<unsigned long long*>(&a.keys[pair * a.keys_stride + threadIdx.x]),
+                const int qp = q0 + (int)threadIdx.x;
+                if (qp < n && key != 0)
+                    atomicMax(reinterpret_cast<unsigned long long*>(&a.keys[pair * a.keys_stride + qp]),
                               (unsigned long long)key);
             }
             __syncthreads();
@@ -560,35 +640,6 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
         }
     }
 }
-
-// fp32 map -> planes [row][h, m, l][d] of bf16 with x = h + m + l (round to nearest
-// even at each step; every difference is exact in fp32).
-__device__ __forceinline__ uint16_t bf16_rne(float x) {
-    uint32_t u = __float_as_uint(x);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ float bf16_widen(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
-
-__global__ void split_x3_kernel(const float* __restrict__ x, int64_t rows, int d, uint16_t* __restrict__ out) {
-    const int64_t n = rows * d;
-    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t r = i / d;
-        const int c = (int)(i - r * d);
-        const float v = x[i];
-        const uint16_t hb = bf16_rne(v);
-        const float r1 = v - bf16_widen(hb);
-        const uint16_t mb = bf16_rne(r1);
-        const float r2 = r1 - bf16_widen(mb);
-        const uint16_t lb = bf16_rne(r2);
-        uint16_t* o = out + r * 3 * d;
-        o[c] = hb;
-        o[d + c] = mb;
-        o[2 * d + c] = lb;
-    }
-}
-
-// ---------------------------------------------------------------------------- small kernels
 
 __global__ void fill_u64_kernel(uint64_t* p, int64_t n, uint64_t v) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
@@ -890,7 +941,6 @@ int launch_nn(const NNArgs& a, int ar, int batch, hipStream_t st) {
 }
 
 // Kernel arguments for queries taken from map q (role q_role) against map db.
-// qdata / dbdata are the maps themselves, or their split planes for AR_X3.
 NNArgs nn_args(const mr_map* q, const void* qdata, int q_role, const mr_map* db, const void* dbdata, int db_role) {
     NNArgs a;
     memset(&a, 0, sizeof(a));
@@ -906,23 +956,8 @@ NNArgs nn_args(const mr_map* q, const void* qdata, int q_role, const mr_map* db,
     return a;
 }
 
-size_t x3_bytes(const mr_map* m) {
-    return choose_arith(m->dtype, m->d) == AR_X3 ? align256((size_t)m->batch * npix(m) * 3 * m->d * 2) : 0;
-}
-
-// Operand source for a map: the map itself, or its split planes written into `planes`.
-int prepare_map(const mr_map* m, void* planes, const void** data, hipStream_t st) {
-    *data = m->data;
-    if (choose_arith(m->dtype, m->d) != AR_X3 || npix(m) == 0) return MR_OK;
-    const int64_t rows = (int64_t)m->batch * npix(m);
-    hipLaunchKernelGGL(split_x3_kernel, dim3(grid_1d(rows * m->d)), dim3(256), 0, st,
-                       static_cast<const float*>(m->data), rows, m->d, static_cast<uint16_t*>(planes));
-    *data = planes;
-    return dev_err();
-}
-
 struct FastLayout {
-    size_t keys_f[2], keys_b[2], front[2], cnt[2], state, blk, x3a, x3b, total;
+    size_t keys_f[2], keys_b[2], front[2], cnt[2], state, blk, total;
 };
 
 FastLayout fast_layout(const mr_map* a, const mr_map* b, int64_t nseeds) {
@@ -937,13 +972,11 @@ FastLayout fast_layout(const mr_map* a, const mr_map* b, int64_t nseeds) {
     for (int i = 0; i < 2; ++i) { L.cnt[i] = off; off = align256(off + (size_t)batch * 4); }
     L.state = off; off = align256(off + (size_t)batch * (size_t)(n1 > 0 ? n1 : 1) * 4);
     L.blk = off; off = align256(off + (size_t)batch * (size_t)(nblk_of(n1) > 0 ? nblk_of(n1) : 1) * 4);
-    L.x3a = off; off += x3_bytes(a);
-    L.x3b = off; off += x3_bytes(b);
     L.total = off;
     return L;
 }
 
-struct MutualLayout { size_t keys_ab, keys_ba, blk, x3a, x3b, total; };
+struct MutualLayout { size_t keys_ab, keys_ba, blk, total; };
 
 MutualLayout mutual_layout(const mr_map* a, const mr_map* b) {
     MutualLayout L;
@@ -953,20 +986,16 @@ MutualLayout mutual_layout(const mr_map* a, const mr_map* b) {
     L.keys_ab = off; off = align256(off + (size_t)batch * (size_t)(na > 0 ? na : 1) * 8);
     L.keys_ba = off; off = align256(off + (size_t)batch * (size_t)(nb > 0 ? nb : 1) * 8);
     L.blk = off; off = align256(off + (size_t)batch * (size_t)(nblk_of(na) > 0 ? nblk_of(na) : 1) * 4);
-    L.x3a = off; off += x3_bytes(a);
-    L.x3b = off; off += x3_bytes(b);
     L.total = off;
     return L;
 }
 
-struct NNLayout { size_t keys, x3q, x3db, total; };
+struct NNLayout { size_t keys, total; };
 
 NNLayout nn_layout(const mr_map* q, const mr_map* db, int64_t n_q) {
     NNLayout L;
     size_t off = 0;
     L.keys = off; off = align256(off + (size_t)q->batch * (size_t)(n_q > 0 ? n_q : 1) * 8);
-    L.x3q = off; off += x3_bytes(q);
-    L.x3db = off; off += x3_bytes(db);
     L.total = off;
     return L;
 }
@@ -1038,10 +1067,7 @@ int mr_nn_argmax(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_
     const int64_t tot = (int64_t)q->batch * n_q;
     hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(tot)), dim3(256), 0, st, keys, tot, (uint64_t)0);
     if (dev_err()) return MR_ERR_DEVICE;
-    const void *qd, *dd;
-    if ((rc = prepare_map(q, at<void>(ws, L.x3q), &qd, st))) return rc;
-    if ((rc = prepare_map(db, at<void>(ws, L.x3db), &dd, st))) return rc;
-    NNArgs a = nn_args(q, qd, 1, db, dd, 2);
+    NNArgs a = nn_args(q, q->data, 1, db, db->data, 2);
     a.qsrc = q_idx ? Q_LIST : Q_ALL;
     a.qlist = q_idx;
     a.qlist_stride = n_q;
@@ -1072,9 +1098,7 @@ int mr_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_b
     hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(batch * na)), dim3(256), 0, st, kab, batch * na, (uint64_t)0);
     hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(batch * nb)), dim3(256), 0, st, kba, batch * nb, (uint64_t)0);
     if (dev_err()) return MR_ERR_DEVICE;
-    const void *ad, *bd;
-    if ((rc = prepare_map(a, at<void>(ws, L.x3a), &ad, st))) return rc;
-    if ((rc = prepare_map(b, at<void>(ws, L.x3b), &bd, st))) return rc;
+    const void *ad = a->data, *bd = b->data;
     NNArgs f = nn_args(a, ad, 1, b, bd, 2);
     f.qsrc = Q_ALL;
     f.host_count = (int32_t)na;
@@ -1134,9 +1158,7 @@ int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t
     if (dev_err()) return MR_ERR_DEVICE;
 
     if (n1 > 0 && n2 > 0 && ns > 0 && max_iters > 0) {
-        const void *ad, *bd;
-        if ((rc = prepare_map(a, at<void>(ws, L.x3a), &ad, st))) return rc;
-        if ((rc = prepare_map(b, at<void>(ws, L.x3b), &bd, st))) return rc;
+        const void *ad = a->data, *bd = b->data;
         const int cyc_grid = grid_1d(ns);
         for (int t = 0; t < max_iters; ++t) {
             const int c = t & 1, x = c ^ 1;

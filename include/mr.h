@@ -7,8 +7,11 @@
  *    L2-normalised descriptor per pixel (d = 24 in MASt3R).
  *    ["MASt3R dissection", section 3 "Napkin Formula"; "DUSt3R and MASt3R
  *    explained", paragraph on MASt3R's dense local-feature head.]
- *  - The NN of a query is the database row of maximal similarity; ties go to
- *    the lowest row index (the pages are silent on ties).
+ *  - The NN of a query is the database row of maximal similarity, compared
+ *    after clearing the 4 lowest bits of the fp32 score (a relative step of at
+ *    most 2^-19, far inside the 1e-5 parity tolerance); ties go to the lowest
+ *    row index (the pages are silent on ties).  Both search directions use
+ *    this one rule, so reciprocity is judged consistently.
  *  - A reciprocal (mutual) match is a pair (i, j) with NN(D1[i], D2) = j and
  *    NN(D2[j], D1) = i.  ["MASt3R dissection", section 1 diagram, section 3.]
  *  - The fast reciprocal scheme seeds a regular grid of image 1, maps every
@@ -17,8 +20,11 @@
  *    number of iterations.  ["DUSt3R and MASt3R explained", the paragraph on
  *    MASt3R's fast reciprocal matching.]
  *
- * Arithmetic: fp32 maps are multiplied in fp32 on the matrix cores with fp32
- * accumulation; bf16 maps use exact bf16 products with fp32 accumulation.
+ * Arithmetic: bf16 maps use exact bf16 products with fp32 accumulation on the
+ * matrix cores.  fp32 maps with d a multiple of 8 (d <= 32) are split exactly
+ * into three bf16 parts x = h + m + l and the six products hh, hm, mh, mm, hl,
+ * lh are accumulated in fp32 (the dropped terms are below 2^-23 |x||y|, i.e.
+ * fp32-accurate); other fp32 maps use fp32 products on the matrix cores.
  * Every kernel computes s(i, j) with the same instruction and the same
  * component order, so a score is bitwise the same whichever map plays the
  * query.  -0.0 is treated as +0.0.  Inputs must be finite (NaN/Inf are out of
@@ -93,7 +99,8 @@ int64_t mr_seed_count(int32_t h, int32_t w, int32_t stride, int32_t offset);
  *              [batch][n_q] row ids local to each pair's q map.
  *   out_idx  : [batch][n_q] NN row id in db (lowest index on ties); -1 when
  *              db has no rows.
- *   out_score: NULL or [batch][n_q] fp32 similarity of that NN.
+ *   out_score: NULL or [batch][n_q] fp32 similarity of that NN (with its 4
+ *              lowest bits cleared, as compared).
  * --------------------------------------------------------------------------- */
 int mr_nn_argmax(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q,
                  int32_t* out_idx, float* out_score, void* ws, size_t ws_bytes, void* stream);
