@@ -232,7 +232,10 @@ template <int P> struct Operand<AR_X3, P> {
 template <int AR> struct ArithTraits;
 template <> struct ArithTraits<AR_F32> { using elem = float; static constexpr int row_mult = 1; static constexpr int qt = 4; };
 template <> struct ArithTraits<AR_BF16> { using elem = uint16_t; static constexpr int row_mult = 1; static constexpr int qt = 4; };
-template <> struct ArithTraits<AR_X3> { using elem = float; static constexpr int row_mult = 1; static constexpr int qt = 2; };
+template <> struct ArithTraits<AR_X3> { using elem = float; static constexpr int row_mult = 1; static constexpr int qt = 3; };
+
+// Query tiles held per wave (fewer for long descriptors, to stay out of scratch).
+template <int AR, int P> constexpr int qt_of() { return AR == AR_X3 && P > 9 ? 2 : ArithTraits<AR>::qt; }
 
 // ---------------------------------------------------------------------------- NN kernel
 
@@ -321,11 +324,11 @@ template <int AR, int P> constexpr int lds_row_bytes() {        // a staged row 
 // registers and keeps a per-lane running best.
 template <int AR, int P, bool EXACT>
 __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb,
-                                             char* lds, const Operand<AR, P> (&q)[ArithTraits<AR>::qt],
+                                             char* lds, const Operand<AR, P> (&q)[qt_of<AR, P>()],
                                              int nact, int h, int jl, int d, int role,
-                                             int (&bk)[ArithTraits<AR>::qt], int (&bt)[ArithTraits<AR>::qt],
-                                             float (&bv)[ArithTraits<AR>::qt]) {
-    constexpr int QT = ArithTraits<AR>::qt;
+                                             int (&bk)[qt_of<AR, P>()], int (&bt)[qt_of<AR, P>()],
+                                             float (&bv)[qt_of<AR, P>()]) {
+    constexpr int QT = qt_of<AR, P>();
     constexpr int MAXC = (32 * max_row_bytes<AR, P>() / 16 + kThreads - 1) / kThreads;
     constexpr int BUF = 32 * lds_row_bytes<AR, P>();
     const int tile_bytes = 32 * rb;
@@ -426,11 +429,11 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
 // memory, one tile ahead in registers, with no LDS staging and no barriers.
 template <int AR, int P, bool EXACT>
 __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1, int ndb,
-                                              const Operand<AR, P> (&q)[ArithTraits<AR>::qt],
+                                              const Operand<AR, P> (&q)[qt_of<AR, P>()],
                                               int nact, int h, int jl, int d, int role,
-                                              int (&bk)[ArithTraits<AR>::qt], int (&bt)[ArithTraits<AR>::qt],
-                                              float (&bv)[ArithTraits<AR>::qt]) {
-    constexpr int QT = ArithTraits<AR>::qt;
+                                              int (&bk)[qt_of<AR, P>()], int (&bt)[qt_of<AR, P>()],
+                                              float (&bv)[qt_of<AR, P>()]) {
+    constexpr int QT = qt_of<AR, P>();
     if (t0 >= t1) return;
     auto row_of = [&](int t) { return (int64_t)t * 32 + jl; };
     auto get = [&](Operand<AR, P>& o, int t) {
@@ -472,9 +475,8 @@ __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1,
 // its own L2.  Every wave leaves one atomicMax per query and item.
 template <int AR, int P>
 __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
-    constexpr int QT = ArithTraits<AR>::qt;
+    constexpr int QT = qt_of<AR, P>();
     constexpr int QB = 32 * QT;          // queries per wave
-    constexpr int QG = kWaves * QB;      // queries per workgroup item
     constexpr int LDS_TILES = 2 * 32 * lds_row_bytes<AR, P>();
     constexpr int LDS_RED = kWaves * QB * 8;
     __shared__ __attribute__((aligned(16))) char lds[LDS_TILES > LDS_RED ? LDS_TILES : LDS_RED];
@@ -489,7 +491,8 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
         if (a.zero_count) a.zero_count[pair * a.zero_stride] = 0;
     }
     const int ntiles = (a.ndb + 31) >> 5;
-    const int qgroups = (n + QG - 1) / QG;
+    const int nqt = (n + 31) >> 5;                        // query tiles
+    const int qgroups = (nqt + kWaves * QT - 1) / (kWaves * QT);
     if (qgroups == 0 || ntiles == 0) return;
     int nsg = (int)gridDim.x / qgroups;
     const int sg_cap = ntiles < kMaxSegGroups ? ntiles : kMaxSegGroups;
@@ -500,11 +503,12 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
     const char* dbytes = static_cast<const char*>(pair_base<AR>(a.dbmap, a.db_pair_elems, pair));
     const int rb = row_bytes<AR>(a.d);
 
-    auto load_queries = [&](Operand<AR, P> (&q)[QT], int q0, int nact) {
+    // query tile j of a wave is tile (tb + j*ts) of the query list
+    auto load_queries = [&](Operand<AR, P> (&q)[QT], int tb, int ts, int nact) {
 #pragma unroll
         for (int j = 0; j < QT; ++j) {
             if (j < nact) {
-                const int qp = q0 + j * 32 + jl;
+                const int qp = (tb + j * ts) * 32 + jl;
                 int64_t row = qp;
                 bool valid = qp < n;
                 if (valid && a.qsrc == Q_LIST)
@@ -548,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
             const int left = n - q0;
             const int nact = left >= QB ? QT : (left + 31) >> 5;
             Operand<AR, P> q[QT];
-            load_queries(q, q0, nact);
+            load_queries(q, q0 >> 5, 1, nact);
             const int seg = grp * kWaves + wv, nseg = ngroups * kWaves;
             const int t0 = (int)((int64_t)seg * ntiles / nseg);
             const int t1 = (int)((int64_t)(seg + 1) * ntiles / nseg);
@@ -595,12 +599,14 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
     for (int item = blockIdx.x; item < items; item += gridDim.x) {
         const int qg = item / nsg;
         const int sg = item - qg * nsg;
-        const int q0 = qg * QG + wv * QB;                 // this wave's first query
-        const int left = n - q0;
-        const int nact = left <= 0 ? 0 : (left >= QB ? QT : (left + 31) >> 5);
+        // the query tiles are spread evenly over the groups; a group's tiles are dealt
+        // round-robin to its waves (tile g0 + wv + kWaves*j)
+        const int g0 = (int)((int64_t)qg * nqt / qgroups);
+        const int g1 = (int)((int64_t)(qg + 1) * nqt / qgroups);
+        const int nact = g0 + wv < g1 ? (g1 - g0 - wv + kWaves - 1) / kWaves : 0;
 
         Operand<AR, P> q[QT];
-        load_queries(q, q0, nact);
+        load_queries(q, g0 + wv, kWaves, nact);
         const int t0 = (int)((int64_t)sg * ntiles / nsg);
         const int t1 = (int)((int64_t)(sg + 1) * ntiles / nsg);
 
@@ -633,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
             uint64_t key = rw[j] >= 0 ? pack_key(sv[j], (uint32_t)rw[j]) : 0;
             const uint64_t o = shfl_xor_u64(key, 32);
             key = o > key ? o : key;
-            const int qp = q0 + j * 32 + jl;
+            const int qp = (g0 + wv + j * kWaves) * 32 + jl;
             if (h == 0 && j < nact && qp < n && key != 0)
                 atomicMax(reinterpret_cast<unsigned long long*>(&a.keys[pair * a.keys_stride + qp]),
                           (unsigned long long)key);
