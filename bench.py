@@ -103,17 +103,42 @@ def run_fast(p, batch_pairs, args, torch, dev, prof=True):
                 active=act[0].tolist(), matches=[int(x) for x in n_pairs.cpu()], batch=A.shape[0])
 
 
-def roofline(flops_per_step, steps, kernel_ms, launches, dtype):
+def measured_traffic(name):
+    """HBM bytes per launch of the similarity kernel from a committed counter summary, or
+    None when the kernel source has changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", name)) as f:
+            rec = json.load(f)
+        with open(os.path.join(ROOT, "dense_grounded_image_amd", "csrc", "mr.hip"), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    return rec["hbm_bytes_per_launch"] if rec.get("source_sha256") == sha else None
+
+
+def roofline(flops_per_step, steps, kernel_ms, launches, dtype, traffic=None):
+    """Algorithmic flops (2*N*d per NN query) per launch of the similarity kernel over its
+    average launch time, against the matrix-core peak of the maps' dtype.  fp32 maps are
+    computed as an exact three-way bf16 split (six bf16 products per fp32 product), so
+    their executed bf16 work and its fraction of the bf16 peak are reported as well."""
     if not launches:
         return None
     per_launch = flops_per_step * steps / launches
     avg_ms = kernel_ms / launches
     achieved = per_launch / (avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[dtype]
-    return {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": None,
-            "kernel": "nn_argmax_kernel", "avg_launch_us": round(avg_ms * 1e3, 2),
-            "flops_per_launch": per_launch}
+    out = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+           "frac": round(achieved / peak, 4), "traffic": traffic,
+           "kernel": "nn_argmax_kernel", "avg_launch_us": round(avg_ms * 1e3, 2),
+           "flops_per_launch": per_launch}
+    if traffic is not None:
+        out["hbm_GBps"] = round(traffic / (avg_ms * 1e-3) / 1e9, 1)
+    if dtype == "f32":
+        out["executed"] = {"arith": "bf16 x3 split, 6 bf16 products per fp32 product",
+                           "achieved_bf16_TFLOPs": round(6 * achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                           "frac": round(6 * achieved / PEAK_TFLOPS["bf16"], 4)}
+    return out
 
 
 def cpu_baseline(p):
@@ -167,7 +192,8 @@ def main():
                    "H": 512, "W": 384, "d": 24, "batch": 1, "stride": 8, "offset": 4, "max_iters": 10},
         "nn_queries_per_s": round(r["nn_queries"] * 1000.0 / r["ms"], 1),
         "nn_queries_per_step": r["nn_queries"], "iter_active": r["active"], "matches": r["matches"][0],
-        "roofline": roofline(r["flops"], args.steps, r["kernel_ms"], r["launches"], "f32"),
+        "roofline": roofline(r["flops"], args.steps, r["kernel_ms"], r["launches"], "f32",
+                             measured_traffic("nn_argmax_pair512x384_f32_traffic.json")),
         "step_mfma_frac": round(r["flops"] / (r["ms"] * 1e-3) / 1e12 / PEAK_TFLOPS["f32"], 4),
     }
     print("bench: fast pair %.4f ms/step" % r["ms"], file=sys.stderr, flush=True)
