@@ -71,6 +71,12 @@ __device__ __forceinline__ int32_t key_row(uint64_t k) {
     return k ? (int32_t)(~(uint32_t)k) : -1;
 }
 
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t x, int src) {
+    const uint32_t lo = __shfl((uint32_t)x, src);
+    const uint32_t hi = __shfl((uint32_t)(x >> 32), src);
+    return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
     uint32_t lo = __shfl_xor((uint32_t)x, m);
     uint32_t hi = __shfl_xor((uint32_t)(x >> 32), m);
@@ -230,9 +236,22 @@ template <int P> struct Operand<AR_X3, P> {
 };
 
 template <int AR> struct ArithTraits;
-template <> struct ArithTraits<AR_F32> { using elem = float; static constexpr int row_mult = 1; static constexpr int qt = 4; };
-template <> struct ArithTraits<AR_BF16> { using elem = uint16_t; static constexpr int row_mult = 1; static constexpr int qt = 4; };
-template <> struct ArithTraits<AR_X3> { using elem = float; static constexpr int row_mult = 1; static constexpr int qt = 3; };
+// tile_best: the streaming pass keeps each lane's best score and the tile it lies in
+// (a short epilogue, for arithmetics whose matrix-core step is short next to it); a
+// second kernel recomputes that tile to find the row.  Otherwise the pass keeps the
+// row itself with a keyed maximum.
+template <> struct ArithTraits<AR_F32> {
+    using elem = float; static constexpr int row_mult = 1; static constexpr int qt = 4;
+    static constexpr bool tile_best = false;
+};
+template <> struct ArithTraits<AR_BF16> {
+    using elem = uint16_t; static constexpr int row_mult = 1; static constexpr int qt = 4;
+    static constexpr bool tile_best = true;
+};
+template <> struct ArithTraits<AR_X3> {
+    using elem = float; static constexpr int row_mult = 1; static constexpr int qt = 3;
+    static constexpr bool tile_best = false;
+};
 
 // Query tiles held per wave (fewer for long descriptors, to stay out of scratch).
 template <int AR, int P> constexpr int qt_of() { return AR == AR_X3 && P > 9 ? 2 : ArithTraits<AR>::qt; }
@@ -303,6 +322,28 @@ __device__ __forceinline__ void tile_exact(const f32x16& acc, int t, int h, int 
     }
 }
 
+// Tile-level form of the same rule: a running maximum of trunc4(tile maximum) over
+// tiles in increasing order, strict '>', remembering the tile.  trunc4 is monotone,
+// so trunc4 of the tile's maximum is the tile's best compared score, and the first
+// tile reaching a lane's final best holds that lane's NN (the lowest such row is
+// found later by recomputing that one tile).  IEEE maximum needs no operand
+// canonicalisation and treats every finite input exactly; the running best is
+// folded into the tree, so "improved" is a plain inequality.
+template <bool RAGGED>
+__device__ __forceinline__ void tile_track(const f32x16& acc, int t, int h, int ndb, float& bv, int& bt) {
+    float k[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) k[v] = (RAGGED && t * 32 + tile_row(v, h) >= ndb) ? -INFINITY : acc[v];
+    auto mx3 = [](float a, float b, float c) {
+        return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+    };
+    const float m0 = mx3(k[0], k[1], k[2]), m1 = mx3(k[3], k[4], k[5]), m2 = mx3(k[6], k[7], k[8]);
+    const float m3 = mx3(k[9], k[10], k[11]), m4 = mx3(k[12], k[13], k[14]), m5 = mx3(k[15], bv, m0);
+    const float m = trunc4(mx3(mx3(m1, m2, m3), m4, m5));
+    bt = m != bv ? t : bt;
+    bv = m;
+}
+
 template <int AR> __device__ __forceinline__ const void* pair_base(const void* p, int64_t elems, int pair) {
     return static_cast<const typename ArithTraits<AR>::elem*>(p) + pair * elems * ArithTraits<AR>::row_mult;
 }
@@ -322,7 +363,11 @@ template <int AR, int P> constexpr int lds_row_bytes() {        // a staged row 
 // (one cooperative 16-byte-chunk copy per tile, one barrier per tile); each of its
 // four waves multiplies the staged tile against its own QT query tiles held in
 // registers and keeps a per-lane running best.
-template <int AR, int P, bool EXACT>
+// Epilogue of a streamed tile: keyed row maximum, exact row maximum (for negative
+// bests), or tile-level maximum.
+enum Epilogue { EP_KEY = 0, EP_EXACT = 1, EP_TILE = 2 };
+
+template <int AR, int P, int EP>
 __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb,
                                              char* lds, const Operand<AR, P> (&q)[qt_of<AR, P>()],
                                              int nact, int h, int jl, int d, int role,
@@ -391,7 +436,10 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
             if (j < nact) {
                 f32x16 acc = {};
                 acc = r.mfma(q[j], acc);
-                if (EXACT) {
+                if constexpr (EP == EP_TILE) {
+                    if (ragged) tile_track<true>(acc, t, h, ndb, bv[j], bt[j]);
+                    else tile_track<false>(acc, t, h, ndb, bv[j], bt[j]);
+                } else if constexpr (EP == EP_EXACT) {
                     if (ragged) tile_exact<true>(acc, t, h, ndb, bv[j], bt[j]);
                     else tile_exact<false>(acc, t, h, ndb, bv[j], bt[j]);
                 } else {
@@ -424,10 +472,126 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
     }
 }
 
+// Database tiles per LDS stage in stream_full.
+template <int AR> constexpr int stage_tiles() { return AR == AR_BF16 ? 2 : 1; }
+
+// The common work item -- every query tile of the wave live, every database tile of
+// the segment full -- without bounds checks and with a deeper pipeline than
+// stream_tiles: a ring of three LDS stages of S tiles, global loads issued two stages
+// ahead of their LDS write, the operands of stage k+1 read from LDS while stage k is
+// multiplied, one barrier per stage.
+template <int AR, int P, int EP, int S>
+__device__ __forceinline__ void stream_full(const char* __restrict__ dbytes, int rb, int t0, int t1, char* lds,
+                                            const Operand<AR, P> (&q)[qt_of<AR, P>()], int h, int jl, int d,
+                                            int role, int (&bk)[qt_of<AR, P>()], int (&bt)[qt_of<AR, P>()],
+                                            float (&bv)[qt_of<AR, P>()]) {
+    constexpr int QT = qt_of<AR, P>();
+    constexpr int NB = 3;
+    constexpr int TILE_LDS = 32 * lds_row_bytes<AR, P>();
+    constexpr int STAGE = S * TILE_LDS;
+    constexpr int MAXC = (S * 32 * max_row_bytes<AR, P>() / 16 + kThreads - 1) / kThreads;
+    const int tile_chunks = (32 * rb) >> 4;
+    const int nst = (t1 - t0 + S - 1) / S;
+    u32x4 slot0[MAXC], slot1[MAXC];
+    Operand<AR, P> opr0[S], opr1[S];
+
+    auto chunks_of = [&](int k) {   // chunks of stage k that lie in real tiles
+        const int tl = t1 - (t0 + S * k);
+        return (tl < S ? tl : S) * tile_chunks;
+    };
+    auto fetch = [&](int k, u32x4 (&st)[MAXC]) {
+        const char* src = dbytes + (int64_t)(t0 + S * k) * 32 * rb;
+        const int nch = chunks_of(k);
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = threadIdx.x + c * kThreads;
+            if (ch < nch) st[c] = *reinterpret_cast<const u32x4*>(src + ch * 16);
+        }
+    };
+    auto put = [&](int k, const u32x4 (&st)[MAXC]) {
+        char* buf = lds + (k % NB) * STAGE;
+        const int nch = chunks_of(k);
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int ch = threadIdx.x + c * kThreads;
+            if (ch < nch) {
+                if constexpr (AR == AR_X3) {
+                    constexpr int D = 8 * P / 3;
+                    const int r = ch / (D / 4), c0 = (ch - r * (D / 4)) * 4;
+                    uint16_t a[3][4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) split3(__uint_as_float(st[c][e]), a[0][e], a[1][e], a[2][e]);
+                    char* dst = buf + r * 6 * D + c0 * 2;
+#pragma unroll
+                    for (int x = 0; x < 3; ++x)
+                        *reinterpret_cast<uint2*>(dst + x * 2 * D) =
+                            uint2{(uint32_t)a[x][0] | ((uint32_t)a[x][1] << 16), (uint32_t)a[x][2] | ((uint32_t)a[x][3] << 16)};
+                } else {
+                    *reinterpret_cast<u32x4*>(buf + ch * 16) = st[c];
+                }
+            }
+        }
+    };
+    // a stage holds 32*S consecutive rows: fp32-split rows in their three planes,
+    // other rows as they are in the map
+    const int tile_lds = AR == AR_X3 ? TILE_LDS : 32 * rb;
+    auto read = [&](int k, Operand<AR, P> (&o)[S]) {
+        const char* buf = lds + (k % NB) * STAGE;
+#pragma unroll
+        for (int x = 0; x < S; ++x) o[x].load(buf + x * tile_lds, jl, true, h, d, role);
+    };
+    auto compute = [&](int k, const Operand<AR, P> (&o)[S]) {
+#pragma unroll
+        for (int x = 0; x < S; ++x) {
+            const int t = t0 + S * k + x;
+            if (S == 1 || t < t1) {
+                f32x16 acc[QT];
+#pragma unroll
+                for (int j = 0; j < QT; ++j) acc[j] = o[x].mfma(q[j], f32x16{});
+#pragma unroll
+                for (int j = 0; j < QT; ++j) {
+                    if constexpr (EP == EP_TILE) {
+                        tile_track<false>(acc[j], t, h, 0, bv[j], bt[j]);
+                    } else {
+                        const int km = tile_key<false>(acc[j], t, h, 0);
+                        const bool gt = km > (bk[j] | 15);
+                        bk[j] = gt ? km : bk[j];
+                        bt[j] = gt ? t : bt[j];
+                    }
+                }
+            }
+        }
+    };
+
+    if (nst <= 0) return;
+    // stage k: global -> slot k&1 at iteration k-3 (prologue for k < 3), LDS buffer k%3
+    // at iteration k-2, operands at iteration k-1, multiplied at iteration k
+    fetch(0, slot0);
+    if (nst > 1) fetch(1, slot1);
+    put(0, slot0);
+    if (nst > 2) fetch(2, slot0);
+    if (nst > 1) put(1, slot1);
+    __syncthreads();
+    read(0, opr0);
+    for (int k = 0; k < nst; k += 2) {
+        if (k + 3 < nst) fetch(k + 3, slot1);
+        if (k + 1 < nst) read(k + 1, opr1);
+        compute(k, opr0);
+        if (k + 2 < nst) put(k + 2, slot0);
+        __syncthreads();
+        if (k + 1 >= nst) break;
+        if (k + 4 < nst) fetch(k + 4, slot0);
+        if (k + 2 < nst) read(k + 2, opr0);
+        compute(k + 1, opr1);
+        if (k + 3 < nst) put(k + 3, slot1);
+        __syncthreads();
+    }
+}
+
 // Small frontiers (all live queries fit in one wave): every wave of the workgroup
 // holds the same queries and streams its own database segment straight from global
 // memory, one tile ahead in registers, with no LDS staging and no barriers.
-template <int AR, int P, bool EXACT>
+template <int AR, int P, int EP>
 __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1, int ndb,
                                               const Operand<AR, P> (&q)[qt_of<AR, P>()],
                                               int nact, int h, int jl, int d, int role,
@@ -453,7 +617,10 @@ __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1,
             if (j < nact) {
                 f32x16 acc = {};
                 acc = r.mfma(q[j], acc);
-                if (EXACT) {
+                if constexpr (EP == EP_TILE) {
+                    if (ragged) tile_track<true>(acc, t, h, ndb, bv[j], bt[j]);
+                    else tile_track<false>(acc, t, h, ndb, bv[j], bt[j]);
+                } else if constexpr (EP == EP_EXACT) {
                     if (ragged) tile_exact<true>(acc, t, h, ndb, bv[j], bt[j]);
                     else tile_exact<false>(acc, t, h, ndb, bv[j], bt[j]);
                 } else {
@@ -472,18 +639,21 @@ __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1,
 // The number of segments follows the live query count (read on the device), so a
 // shrinking frontier still spreads over the whole GPU; it is a multiple of 8 when
 // possible so that each XCD keeps streaming the same eighth of the database through
-// its own L2.  Every wave leaves one atomicMax per query and item.
+// its own L2.  Every wave leaves one atomicMax per query and item.  With
+// tile_best arithmetic the merged key names (score, tile) and recover_rows_kernel
+// turns it into (score, row).
 template <int AR, int P>
 __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
     constexpr int QT = qt_of<AR, P>();
+    constexpr bool TB = ArithTraits<AR>::tile_best;   // keys carry (score, tile), not (score, row)
     constexpr int QB = 32 * QT;          // queries per wave
-    constexpr int LDS_TILES = 2 * 32 * lds_row_bytes<AR, P>();
+    constexpr int LDS_TILES = (TB ? 3 * stage_tiles<AR>() : 2) * 32 * lds_row_bytes<AR, P>();
     constexpr int LDS_RED = kWaves * QB * 8;
     __shared__ __attribute__((aligned(16))) char lds[LDS_TILES > LDS_RED ? LDS_TILES : LDS_RED];
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5;
     const int jl = lane & 31;
-    const int wv = threadIdx.x >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, so branches on it stay scalar
     const int pair = blockIdx.y;
     const int n = a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -560,19 +730,25 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
             float bv[QT];
 #pragma unroll
             for (int j = 0; j < QT; ++j) { bk[j] = INT_MIN; bt[j] = -1; bv[j] = -INFINITY; }
-            stream_direct<AR, P, false>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
             float sv[QT];
-            int rw[QT];
-            finish(bk, bt, sv, rw);
-            bool neg = false;
+            int rw[QT];   // row, or tile with TB
+            if constexpr (TB) {
+                stream_direct<AR, P, EP_TILE>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
 #pragma unroll
-            for (int j = 0; j < QT; ++j) neg = neg || (j < nact && bk[j] < 0 && t0 < t1);
-            if (__ballot(neg) != 0) {
-                int bx[QT];
+                for (int j = 0; j < QT; ++j) { sv[j] = bv[j]; rw[j] = bt[j]; }
+            } else {
+                stream_direct<AR, P, EP_KEY>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
+                finish(bk, bt, sv, rw);
+                bool neg = false;
 #pragma unroll
-                for (int j = 0; j < QT; ++j) bx[j] = -1;
-                stream_direct<AR, P, true>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, bk, bx, bv);
-                finish_exact(bv, bx, sv, rw);
+                for (int j = 0; j < QT; ++j) neg = neg || (j < nact && bk[j] < 0 && t0 < t1);
+                if (__ballot(neg) != 0) {
+                    int bx[QT];
+#pragma unroll
+                    for (int j = 0; j < QT; ++j) bx[j] = -1;
+                    stream_direct<AR, P, EP_EXACT>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, bk, bx, bv);
+                    finish_exact(bv, bx, sv, rw);
+                }
             }
 #pragma unroll
             for (int j = 0; j < QT; ++j) {
@@ -614,23 +790,36 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
         float bv[QT];
 #pragma unroll
         for (int j = 0; j < QT; ++j) { bk[j] = INT_MIN; bt[j] = -1; bv[j] = -INFINITY; }
-        stream_tiles<AR, P, false>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
-
-        // (score, row) per lane and query tile
+        // (score, row) -- or (score, tile) with TB -- per lane and query tile
         float sv[QT];
         int rw[QT];
-        finish(bk, bt, sv, rw);
-        bool neg = false;
+        if constexpr (TB) {
+            // the choice must be the same for all four waves: both paths stage tiles
+            // cooperatively, with workgroup barriers
+            if (g1 - g0 == kWaves * QT && (int64_t)t1 * 32 <= a.ndb)
+                stream_full<AR, P, EP_TILE, stage_tiles<AR>()>(dbytes, rb, t0, t1, lds, q, h, jl, a.d, a.db_role,
+                                                               bk, bt, bv);
+            else
+                stream_tiles<AR, P, EP_TILE>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bt,
+                                             bv);
 #pragma unroll
-        for (int j = 0; j < QT; ++j) neg = neg || (j < nact && bk[j] < 0);
-        if (__syncthreads_or(neg)) {
-            // some lane's best score is negative, where float bits do not order as
-            // integers: the workgroup streams its segment again with the exact comparison
-            int bx[QT];
+            for (int j = 0; j < QT; ++j) { sv[j] = bv[j]; rw[j] = bt[j]; }
+        } else {
+            stream_tiles<AR, P, EP_KEY>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
+            finish(bk, bt, sv, rw);
+            bool neg = false;
 #pragma unroll
-            for (int j = 0; j < QT; ++j) bx[j] = -1;
-            stream_tiles<AR, P, true>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bx, bv);
-            finish_exact(bv, bx, sv, rw);
+            for (int j = 0; j < QT; ++j) neg = neg || (j < nact && bk[j] < 0);
+            if (__syncthreads_or(neg)) {
+                // some lane's best score is negative, where float bits do not order as
+                // integers: the workgroup streams its segment again with the exact comparison
+                int bx[QT];
+#pragma unroll
+                for (int j = 0; j < QT; ++j) bx[j] = -1;
+                stream_tiles<AR, P, EP_EXACT>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bx,
+                                              bv);
+                finish_exact(bv, bx, sv, rw);
+            }
         }
 
         // merge the two lane halves of each query, then across items with atomicMax
@@ -644,6 +833,71 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
                 atomicMax(reinterpret_cast<unsigned long long*>(&a.keys[pair * a.keys_stride + qp]),
                           (unsigned long long)key);
         }
+    }
+}
+
+// (score, tile) -> (score, row): one query tile per workgroup; each wave takes 8 of
+// its 32 queries.  For query c the wave loads the 32 rows of c's tile as the A
+// operand and multiplies them with the query block exactly as the streaming pass
+// did (same instruction, same operand layout, same step order), so column c holds
+// bitwise the scores that were compared there; the lowest row whose trunc4 score
+// equals the key's score is c's NN.  Keys are rewritten in place.
+template <int AR, int P>
+__global__ __launch_bounds__(kThreads) void recover_rows_kernel(NNArgs a) {
+    constexpr int CPW = 32 / kWaves;   // queries resolved per wave
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5;
+    const int jl = lane & 31;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, so branches on it stay scalar
+    const int pair = blockIdx.y;
+    const int n = a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count;
+    const int nqt = (n + 31) >> 5;
+    const void* qbase = pair_base<AR>(a.qmap, a.q_pair_elems, pair);
+    const void* dbase = pair_base<AR>(a.dbmap, a.db_pair_elems, pair);
+    uint64_t* keys = a.keys + pair * a.keys_stride;
+    for (int g = blockIdx.x; g < nqt; g += gridDim.x) {
+        const int qp = g * 32 + jl;
+        int64_t row = qp;
+        bool valid = qp < n;
+        if (valid && a.qsrc == Q_LIST)
+            row = static_cast<const int32_t*>(a.qlist)[pair * a.qlist_stride + qp];
+        else if (valid && a.qsrc == Q_KEYS)
+            row = key_row(static_cast<const uint64_t*>(a.qlist)[pair * a.qlist_stride + qp]);
+        valid = valid && row >= 0 && row < a.nq_rows;
+        Operand<AR, P> q;
+        q.load(qbase, valid ? row : 0, valid, h, a.d, a.q_role);
+        // this lane's query key; only columns 8*wv.. are read back below, and only this
+        // wave rewrites them, after the read
+        const uint64_t key = qp < n ? keys[qp] : 0;
+        Operand<AR, P> r[CPW];
+        int tile[CPW];
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) {
+            const uint64_t kc = shfl_u64(key, CPW * wv + k);
+            tile[k] = kc ? (int)~(uint32_t)kc : -1;
+            const int64_t drow = (int64_t)tile[k] * 32 + jl;
+            const bool ok = tile[k] >= 0 && drow < a.ndb;
+            r[k].load(dbase, ok ? drow : 0, ok, h, a.d, a.db_role);
+        }
+        uint64_t out = 0;
+#pragma unroll
+        for (int k = 0; k < CPW; ++k) {
+            const int c = CPW * wv + k;
+            const uint64_t kc = shfl_u64(key, c);
+            const float best = from_ordered((uint32_t)(kc >> 32));
+            f32x16 acc = {};
+            acc = r[k].mfma(q, acc);
+            int found = INT_MAX;
+#pragma unroll
+            for (int v = 15; v >= 0; --v) {
+                const int rr = tile[k] * 32 + tile_row(v, h);
+                if (trunc4(acc[v]) == best && rr < a.ndb) found = rr;
+            }
+            const int o = __shfl_xor(found, 32);
+            found = o < found ? o : found;
+            if (jl == c) out = (kc != 0 && found != INT_MAX) ? pack_key(best, (uint32_t)found) : 0;
+        }
+        if (h == 0 && qp < n && jl >= CPW * wv && jl < CPW * (wv + 1)) keys[qp] = out;
     }
 }
 
@@ -942,6 +1196,19 @@ int launch_nn(const NNArgs& a, int ar, int batch, hipStream_t st) {
     if (prof) {
         if (hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st) != hipSuccess) return MR_ERR_DEVICE;
         ++g_prof.used;
+    }
+    if (ar == AR_BF16) {
+        // tile keys -> row keys
+        const int64_t max_n = a.dev_count ? a.qlist_stride : a.host_count;
+        const int gx = (int)((max_n + 31) / 32 < (1 << 20) ? (max_n + 31) / 32 : (1 << 20));
+        if (gx < 1) return MR_OK;
+        switch ((a.d + 15) / 16) {
+#define MR_CASE(p) case p: hipLaunchKernelGGL((recover_rows_kernel<AR_BF16, p>), dim3(gx, batch), dim3(kThreads), 0, st, a); break;
+            MR_CASE(1) MR_CASE(2) MR_CASE(3) MR_CASE(4)
+#undef MR_CASE
+            default: return MR_ERR_SHAPE;
+        }
+        if (dev_err()) return MR_ERR_DEVICE;
     }
     return MR_OK;
 }
