@@ -148,6 +148,22 @@ template <int P> struct Operand<AR_BF16, P> {
             x[s] = __builtin_bit_cast(bf16x8, raw);
         }
     }
+    // Database side only: k-slots past d take the row's first chunk instead of zeros.
+    // The query operand is zero in those slots and the maps are finite, so the
+    // products there are +-0 and every score is unchanged (up to the sign of an
+    // exact zero, which compares equal).  `tile` is the tile's first row (uniform);
+    // off[s] the lane's byte offset in the tile (db_offsets).
+    __device__ __forceinline__ void load_db(const char* tile, const int (&off)[P]) {
+#pragma unroll
+        for (int s = 0; s < P; ++s) x[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(tile + off[s]));
+    }
+    static __device__ __forceinline__ void db_offsets(int jl, int h, int d, int (&off)[P]) {
+#pragma unroll
+        for (int s = 0; s < P; ++s) {
+            const int c = 8 * (P * h + s);
+            off[s] = (jl * d + (c < d ? c : 0)) * 2;
+        }
+    }
     __device__ __forceinline__ f32x16 mfma(const Operand& b, f32x16 acc) const {
 #pragma unroll
         for (int s = 0; s < P; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[s], b.x[s], acc, 0, 0, 0);
@@ -495,22 +511,27 @@ __device__ __forceinline__ void stream_full(const char* __restrict__ dbytes, int
     u32x4 slot0[MAXC], slot1[MAXC];
     Operand<AR, P> opr0[S], opr1[S];
 
-    auto chunks_of = [&](int k) {   // chunks of stage k that lie in real tiles
-        const int tl = t1 - (t0 + S * k);
-        return (tl < S ? tl : S) * tile_chunks;
-    };
+    // Loads, LDS writes and operand reads are issued unconditionally (stage indices
+    // past the end are clamped to the last stage, chunks past the end to the stage's
+    // last chunk) so that the compiler can count outstanding memory operations
+    // exactly and wait only for the oldest stage.
     auto fetch = [&](int k, u32x4 (&st)[MAXC]) {
+        k = k < nst ? k : nst - 1;
+        const int tl = t1 - (t0 + S * k);
+        const int nch = (tl < S ? tl : S) * tile_chunks;
         const char* src = dbytes + (int64_t)(t0 + S * k) * 32 * rb;
-        const int nch = chunks_of(k);
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
             const int ch = threadIdx.x + c * kThreads;
-            if (ch < nch) st[c] = *reinterpret_cast<const u32x4*>(src + ch * 16);
+            st[c] = *reinterpret_cast<const u32x4*>(src + (ch < nch ? ch : nch - 1) * 16);
         }
     };
     auto put = [&](int k, const u32x4 (&st)[MAXC]) {
+        // chunk ch of the stage goes to LDS; chunks past the stage's end are dropped
+        const int kc = k < nst ? k : nst - 1;
+        const int tl = t1 - (t0 + S * kc);
+        const int nch = (tl < S ? tl : S) * tile_chunks;
         char* buf = lds + (k % NB) * STAGE;
-        const int nch = chunks_of(k);
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
             const int ch = threadIdx.x + c * kThreads;
@@ -567,25 +588,81 @@ __device__ __forceinline__ void stream_full(const char* __restrict__ dbytes, int
     // stage k: global -> slot k&1 at iteration k-3 (prologue for k < 3), LDS buffer k%3
     // at iteration k-2, operands at iteration k-1, multiplied at iteration k
     fetch(0, slot0);
-    if (nst > 1) fetch(1, slot1);
+    fetch(1, slot1);
     put(0, slot0);
-    if (nst > 2) fetch(2, slot0);
-    if (nst > 1) put(1, slot1);
+    fetch(2, slot0);
+    put(1, slot1);
     __syncthreads();
     read(0, opr0);
     for (int k = 0; k < nst; k += 2) {
-        if (k + 3 < nst) fetch(k + 3, slot1);
-        if (k + 1 < nst) read(k + 1, opr1);
+        // buffers of stages past the end are free: writing or reading them is harmless
+        fetch(k + 3, slot1);
+        read(k + 1, opr1);
         compute(k, opr0);
-        if (k + 2 < nst) put(k + 2, slot0);
+        put(k + 2, slot0);
         __syncthreads();
         if (k + 1 >= nst) break;
-        if (k + 4 < nst) fetch(k + 4, slot0);
-        if (k + 2 < nst) read(k + 2, opr0);
+        fetch(k + 4, slot0);
+        read(k + 2, opr0);
         compute(k + 1, opr1);
-        if (k + 3 < nst) put(k + 3, slot1);
+        put(k + 3, slot1);
         __syncthreads();
     }
+}
+
+// Full work items of bf16 maps, without LDS or barriers: each wave reads the
+// database operand straight from global memory (the four waves of a workgroup read
+// the same tiles, so L1 serves all but the first) into a ring of D tiles issued D
+// tiles ahead of their use.
+template <int AR, int P, int EP, int D>
+__device__ __forceinline__ void stream_regs(const void* dbase, int t0, int t1,
+                                            const Operand<AR, P> (&q)[qt_of<AR, P>()], int h, int jl, int d,
+                                            int (&bk)[qt_of<AR, P>()], int (&bt)[qt_of<AR, P>()],
+                                            float (&bv)[qt_of<AR, P>()]) {
+    constexpr int QT = qt_of<AR, P>();
+    static_assert(AR == AR_BF16, "direct database operands are bf16 only");
+    Operand<AR, P> r[D];
+    int off[P];
+    Operand<AR, P>::db_offsets(jl, h, d, off);
+    const char* dbytes = static_cast<const char*>(dbase);
+    const int64_t tile_bytes = (int64_t)64 * d;   // 32 rows of 2d bytes
+    const int tlast = t1 - 1;
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+        const int tt = t0 + u < tlast ? t0 + u : tlast;
+        r[u].load_db(dbytes + tt * tile_bytes, off);
+    }
+    auto compute = [&](const Operand<AR, P>& rr, int tt) {
+        f32x16 acc[QT];
+#pragma unroll
+        for (int j = 0; j < QT; ++j) acc[j] = rr.mfma(q[j], f32x16{});
+#pragma unroll
+        for (int j = 0; j < QT; ++j) {
+            if constexpr (EP == EP_TILE) {
+                tile_track<false>(acc[j], tt, h, 0, bv[j], bt[j]);
+            } else {
+                const int km = tile_key<false>(acc[j], tt, h, 0);
+                const bool gt = km > (bk[j] | 15);
+                bk[j] = gt ? km : bk[j];
+                bt[j] = gt ? tt : bt[j];
+            }
+        }
+    };
+    // whole groups of D tiles: no branch inside, refills clamped, so the compiler
+    // counts outstanding loads exactly
+    int t = t0;
+    for (; t + D <= t1; t += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            compute(r[u], t + u);
+            const int tn = t + u + D < tlast ? t + u + D : tlast;
+            r[u].load_db(dbytes + tn * tile_bytes, off);
+        }
+    }
+    // the last t1 - t < D tiles are already in the ring
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u)
+        if (t + u < t1) compute(r[u], t + u);
 }
 
 // Small frontiers (all live queries fit in one wave): every wave of the workgroup
@@ -642,8 +719,14 @@ __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1,
 // its own L2.  Every wave leaves one atomicMax per query and item.  With
 // tile_best arithmetic the merged key names (score, tile) and recover_rows_kernel
 // turns it into (score, row).
+// Waves per SIMD the compiler must leave room for (register budget): three for the
+// short bf16 contraction, whose database ring and accumulators otherwise land just
+// above that budget; the split-fp32 and fp32 forms need their registers.
+template <int AR, int P> constexpr int min_waves() { return AR == AR_BF16 && P <= 2 ? 3 : 1; }
+
 template <int AR, int P>
-__global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves<AR, P>())))
+void nn_argmax_kernel(NNArgs a) {
     constexpr int QT = qt_of<AR, P>();
     constexpr bool TB = ArithTraits<AR>::tile_best;   // keys carry (score, tile), not (score, row)
     constexpr int QB = 32 * QT;          // queries per wave
@@ -797,8 +880,7 @@ __global__ __launch_bounds__(kThreads) void nn_argmax_kernel(NNArgs a) {
             // the choice must be the same for all four waves: both paths stage tiles
             // cooperatively, with workgroup barriers
             if (g1 - g0 == kWaves * QT && (int64_t)t1 * 32 <= a.ndb)
-                stream_full<AR, P, EP_TILE, stage_tiles<AR>()>(dbytes, rb, t0, t1, lds, q, h, jl, a.d, a.db_role,
-                                                               bk, bt, bv);
+                stream_regs<AR, P, EP_TILE, 4>(dbytes, t0, t1, q, h, jl, a.d, bk, bt, bv);
             else
                 stream_tiles<AR, P, EP_TILE>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bt,
                                              bv);
