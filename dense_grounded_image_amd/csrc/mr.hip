@@ -488,37 +488,42 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
     }
 }
 
-// Database tiles per LDS stage in stream_full.
-template <int AR> constexpr int stage_tiles() { return AR == AR_BF16 ? 2 : 1; }
+// Database tiles per LDS stage in stream_staged.
+template <int AR> constexpr int stage_tiles() { return 2; }
 
-// The common work item -- every query tile of the wave live, every database tile of
-// the segment full -- without bounds checks and with a deeper pipeline than
-// stream_tiles: a ring of three LDS stages of S tiles, global loads issued two stages
-// ahead of their LDS write, the operands of stage k+1 read from LDS while stage k is
-// multiplied, one barrier per stage.
-template <int AR, int P, int EP, int S>
-__device__ __forceinline__ void stream_full(const char* __restrict__ dbytes, int rb, int t0, int t1, char* lds,
-                                            const Operand<AR, P> (&q)[qt_of<AR, P>()], int h, int jl, int d,
-                                            int role, int (&bk)[qt_of<AR, P>()], int (&bt)[qt_of<AR, P>()],
-                                            float (&bv)[qt_of<AR, P>()]) {
+// One workgroup streams its database segment through a ring of three LDS stages of S
+// tiles: global loads are issued two stages ahead of their LDS write, one barrier
+// per stage, and (RA) the operands of stage k+1 are read from LDS while stage k is
+// multiplied.  Each wave multiplies the staged tiles against its own nact query
+// tiles held in registers and keeps a per-lane running best (epilogue EP).  Rows
+// must be a multiple of 16 bytes.  Loads, LDS writes and operand reads are issued
+// unconditionally -- stage indices past the end clamp to the last stage, chunks past
+// the map's last row to that row's last chunk -- so that the compiler counts
+// outstanding memory operations exactly and waits only for the oldest stage.  LDS
+// rows past the map's end hold stale (finite) data; the ragged epilogue masks them.
+template <int AR, int P, int EP, int S, bool RA>
+__device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb,
+                                              char* lds, const Operand<AR, P> (&q)[qt_of<AR, P>()], int nact,
+                                              int h, int jl, int d, int role, int (&bk)[qt_of<AR, P>()],
+                                              int (&bt)[qt_of<AR, P>()], float (&bv)[qt_of<AR, P>()]) {
     constexpr int QT = qt_of<AR, P>();
     constexpr int NB = 3;
-    constexpr int TILE_LDS = 32 * lds_row_bytes<AR, P>();
-    constexpr int STAGE = S * TILE_LDS;
+    constexpr int STAGE = S * 32 * lds_row_bytes<AR, P>();
     constexpr int MAXC = (S * 32 * max_row_bytes<AR, P>() / 16 + kThreads - 1) / kThreads;
-    const int tile_chunks = (32 * rb) >> 4;
+    const int row_chunks = rb >> 4;
     const int nst = (t1 - t0 + S - 1) / S;
     u32x4 slot0[MAXC], slot1[MAXC];
     Operand<AR, P> opr0[S], opr1[S];
 
-    // Loads, LDS writes and operand reads are issued unconditionally (stage indices
-    // past the end are clamped to the last stage, chunks past the end to the stage's
-    // last chunk) so that the compiler can count outstanding memory operations
-    // exactly and wait only for the oldest stage.
+    // chunks of stage k that hold real rows (k clamped)
+    auto stage_chunks = [&](int k) {
+        const int r0 = (t0 + S * k) * 32;
+        const int nr = ndb - r0 < S * 32 ? ndb - r0 : S * 32;
+        return nr * row_chunks;
+    };
     auto fetch = [&](int k, u32x4 (&st)[MAXC]) {
         k = k < nst ? k : nst - 1;
-        const int tl = t1 - (t0 + S * k);
-        const int nch = (tl < S ? tl : S) * tile_chunks;
+        const int nch = stage_chunks(k);
         const char* src = dbytes + (int64_t)(t0 + S * k) * 32 * rb;
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
@@ -527,16 +532,14 @@ __device__ __forceinline__ void stream_full(const char* __restrict__ dbytes, int
         }
     };
     auto put = [&](int k, const u32x4 (&st)[MAXC]) {
-        // chunk ch of the stage goes to LDS; chunks past the stage's end are dropped
-        const int kc = k < nst ? k : nst - 1;
-        const int tl = t1 - (t0 + S * kc);
-        const int nch = (tl < S ? tl : S) * tile_chunks;
+        const int nch = stage_chunks(k < nst ? k : nst - 1);
         char* buf = lds + (k % NB) * STAGE;
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
             const int ch = threadIdx.x + c * kThreads;
             if (ch < nch) {
                 if constexpr (AR == AR_X3) {
+                    // four fp32 components -> their h, m, l bf16 in the row's three planes
                     constexpr int D = 8 * P / 3;
                     const int r = ch / (D / 4), c0 = (ch - r * (D / 4)) * 4;
                     uint16_t a[3][4];
@@ -553,61 +556,101 @@ __device__ __forceinline__ void stream_full(const char* __restrict__ dbytes, int
             }
         }
     };
-    // a stage holds 32*S consecutive rows: fp32-split rows in their three planes,
-    // other rows as they are in the map
-    const int tile_lds = AR == AR_X3 ? TILE_LDS : 32 * rb;
+    // a stage holds 32*S consecutive rows: split rows in their three planes, other
+    // rows as they are in the map
+    const int tile_lds = AR == AR_X3 ? 32 * lds_row_bytes<AR, P>() : 32 * rb;
     auto read = [&](int k, Operand<AR, P> (&o)[S]) {
         const char* buf = lds + (k % NB) * STAGE;
 #pragma unroll
-        for (int x = 0; x < S; ++x) o[x].load(buf + x * tile_lds, jl, true, h, d, role);
+        for (int x = 0; x < S; ++x) {
+            if constexpr (AR == AR_BF16) {
+                int off[P];
+                Operand<AR, P>::db_offsets(jl, h, d, off);
+                o[x].load_db(buf + x * tile_lds, off);
+            } else {
+                o[x].load(buf + x * tile_lds, jl, true, h, d, role);
+            }
+        }
+    };
+    auto epilogue = [&](const f32x16& acc, int t, bool ragged, int j) {
+        if constexpr (EP == EP_TILE) {
+            if (ragged) tile_track<true>(acc, t, h, ndb, bv[j], bt[j]);
+            else tile_track<false>(acc, t, h, ndb, bv[j], bt[j]);
+        } else if constexpr (EP == EP_EXACT) {
+            if (ragged) tile_exact<true>(acc, t, h, ndb, bv[j], bt[j]);
+            else tile_exact<false>(acc, t, h, ndb, bv[j], bt[j]);
+        } else {
+            const int km = ragged ? tile_key<true>(acc, t, h, ndb) : tile_key<false>(acc, t, h, ndb);
+            const bool gt = km > (bk[j] | 15);   // strictly better score: earliest tile wins ties
+            bk[j] = gt ? km : bk[j];
+            bt[j] = gt ? t : bt[j];
+        }
     };
     auto compute = [&](int k, const Operand<AR, P> (&o)[S]) {
 #pragma unroll
         for (int x = 0; x < S; ++x) {
             const int t = t0 + S * k + x;
             if (S == 1 || t < t1) {
-                f32x16 acc[QT];
+                const bool ragged = (t + 1) * 32 > ndb;
+                // one query tile at a time: the epilogue of tile j overlaps the
+                // products of tile j+1
+                if (nact == QT) {
 #pragma unroll
-                for (int j = 0; j < QT; ++j) acc[j] = o[x].mfma(q[j], f32x16{});
+                    for (int j = 0; j < QT; ++j) epilogue(o[x].mfma(q[j], f32x16{}), t, ragged, j);
+                } else {
 #pragma unroll
-                for (int j = 0; j < QT; ++j) {
-                    if constexpr (EP == EP_TILE) {
-                        tile_track<false>(acc[j], t, h, 0, bv[j], bt[j]);
-                    } else {
-                        const int km = tile_key<false>(acc[j], t, h, 0);
-                        const bool gt = km > (bk[j] | 15);
-                        bk[j] = gt ? km : bk[j];
-                        bt[j] = gt ? t : bt[j];
-                    }
+                    for (int j = 0; j < QT; ++j)
+                        if (j < nact) epilogue(o[x].mfma(q[j], f32x16{}), t, ragged, j);
                 }
             }
         }
     };
 
     if (nst <= 0) return;
-    // stage k: global -> slot k&1 at iteration k-3 (prologue for k < 3), LDS buffer k%3
-    // at iteration k-2, operands at iteration k-1, multiplied at iteration k
+    // stage k: global -> slot k&1 at iteration k-3 (the prologue for k < 3), LDS
+    // buffer k%3 at iteration k-2, operands (RA) at iteration k-1, multiplied at k
     fetch(0, slot0);
     fetch(1, slot1);
     put(0, slot0);
     fetch(2, slot0);
     put(1, slot1);
     __syncthreads();
-    read(0, opr0);
+    if constexpr (RA) read(0, opr0);
     for (int k = 0; k < nst; k += 2) {
         // buffers of stages past the end are free: writing or reading them is harmless
         fetch(k + 3, slot1);
-        read(k + 1, opr1);
+        if constexpr (RA) read(k + 1, opr1);
+        else read(k, opr0);
         compute(k, opr0);
         put(k + 2, slot0);
         __syncthreads();
         if (k + 1 >= nst) break;
         fetch(k + 4, slot0);
-        read(k + 2, opr0);
-        compute(k + 1, opr1);
+        if constexpr (RA) {
+            read(k + 2, opr0);
+            compute(k + 1, opr1);
+        } else {
+            read(k + 1, opr0);
+            compute(k + 1, opr0);
+        }
         put(k + 3, slot1);
         __syncthreads();
     }
+}
+
+// The workgroup-staged stream for an arithmetic: the LDS ring for bf16 rows; the
+// plain double buffer for fp32 rows (measured faster for the long split contraction,
+// whose nine matrix-core steps per tile already cover the staging latency).
+template <int AR, int P, int EP>
+__device__ __forceinline__ void stream_db(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb, char* lds,
+                                          const Operand<AR, P> (&q)[qt_of<AR, P>()], int nact, int h, int jl, int d,
+                                          int role, int (&bk)[qt_of<AR, P>()], int (&bt)[qt_of<AR, P>()],
+                                          float (&bv)[qt_of<AR, P>()]) {
+    if constexpr (AR != AR_BF16)
+        stream_tiles<AR, P, EP>(dbytes, rb, t0, t1, ndb, lds, q, nact, h, jl, d, role, bk, bt, bv);
+    else
+        stream_staged<AR, P, EP, stage_tiles<AR>(), false>(dbytes, rb, t0, t1, ndb, lds, q, nact, h, jl, d,
+                                                                   role, bk, bt, bv);
 }
 
 // Full work items of bf16 maps, without LDS or barriers: each wave reads the
@@ -730,7 +773,7 @@ void nn_argmax_kernel(NNArgs a) {
     constexpr int QT = qt_of<AR, P>();
     constexpr bool TB = ArithTraits<AR>::tile_best;   // keys carry (score, tile), not (score, row)
     constexpr int QB = 32 * QT;          // queries per wave
-    constexpr int LDS_TILES = (TB ? 3 * stage_tiles<AR>() : 2) * 32 * lds_row_bytes<AR, P>();
+    constexpr int LDS_TILES = (AR == AR_BF16 ? 3 * stage_tiles<AR>() : 2) * 32 * lds_row_bytes<AR, P>();
     constexpr int LDS_RED = kWaves * QB * 8;
     __shared__ __attribute__((aligned(16))) char lds[LDS_TILES > LDS_RED ? LDS_TILES : LDS_RED];
     const int lane = threadIdx.x & 63;
@@ -882,12 +925,11 @@ void nn_argmax_kernel(NNArgs a) {
             if (g1 - g0 == kWaves * QT && (int64_t)t1 * 32 <= a.ndb)
                 stream_regs<AR, P, EP_TILE, 4>(dbytes, t0, t1, q, h, jl, a.d, bk, bt, bv);
             else
-                stream_tiles<AR, P, EP_TILE>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bt,
-                                             bv);
+                stream_db<AR, P, EP_TILE>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
 #pragma unroll
             for (int j = 0; j < QT; ++j) { sv[j] = bv[j]; rw[j] = bt[j]; }
         } else {
-            stream_tiles<AR, P, EP_KEY>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
+            stream_db<AR, P, EP_KEY>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
             finish(bk, bt, sv, rw);
             bool neg = false;
 #pragma unroll
@@ -898,8 +940,8 @@ void nn_argmax_kernel(NNArgs a) {
                 int bx[QT];
 #pragma unroll
                 for (int j = 0; j < QT; ++j) bx[j] = -1;
-                stream_tiles<AR, P, EP_EXACT>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bx,
-                                              bv);
+                stream_db<AR, P, EP_EXACT>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bx,
+                                           bv);
                 finish_exact(bv, bx, sv, rw);
             }
         }

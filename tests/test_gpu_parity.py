@@ -122,10 +122,13 @@ def test_mutual_full(H, W, dtype):
     log("mutual", H, W, dtype, len(gp), len(o_pairs))
 
 
-def test_mutual_planted_noise_free_ties():
+@pytest.mark.parametrize("H,W,dtype", [(40, 35, "f32"), (40, 35, "bf16"), (64, 64, "bf16")])
+def test_mutual_planted_noise_free_ties(H, W, dtype):
     """Noise-free planted field: clamped borders duplicate descriptors exactly, so the
-    lowest-index tie-break decides; the result is the closed form."""
-    p = workloads.make_pair(40, 35, 24, seed=600, warp="shift", sigma=0.0, rho=0.0)
+    lowest-index tie-break decides; the result is the closed form.  For bf16 the ties go
+    through the tile-level search and the row recovery; 64x64 (whole query groups, no
+    ragged tile) takes the direct-load stream, 40x35 the staged one."""
+    p = workloads.make_pair(H, W, 24, seed=600, warp="shift", sigma=0.0, rho=0.0, dtype=dtype)
     A, B = pair_maps(p)
     pairs, n, _, _ = mr.mutual_nn(A, B)
     torch.cuda.synchronize()
@@ -133,6 +136,35 @@ def test_mutual_planted_noise_free_ties():
     for q, s in enumerate(p.src.tolist()):
         first.setdefault(s, q)
     assert mr.matches(pairs, n).tolist() == [list(x) for x in sorted(first.items())]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nn_all_scores_negative(dtype):
+    """Every similarity negative (the maps point into opposite half-spaces): the integer
+    key order does not hold there, so this takes the exact fallback (fp32) and the
+    float comparisons of the tile-level search and the row recovery (bf16)."""
+    rng = np.random.default_rng(5)
+    d, (h1, w1), (h2, w2) = 24, (37, 29), (41, 23)
+    e = np.zeros(d)
+    e[0] = 1.0
+
+    def unit(x):
+        return (x / np.linalg.norm(x, axis=1, keepdims=True)).astype(np.float32)
+
+    A = unit(0.9 * e + 0.25 * rng.standard_normal((h1 * w1, d)) / np.sqrt(d))
+    B = unit(-0.9 * e + 0.25 * rng.standard_normal((h2 * w2, d)) / np.sqrt(d))
+    Ab = Bb = None
+    if dtype == "bf16":
+        Ab, Bb = workloads.f32_to_bf16_bits(A), workloads.f32_to_bf16_bits(B)
+        A, B = workloads.bf16_bits_to_f32(Ab), workloads.bf16_bits_to_f32(Bb)
+    gi, gs = mr.nn_argmax(dev_map(A, h1, w1, Ab), dev_map(B, h2, w2, Bb), with_score=True)
+    torch.cuda.synchronize()
+    oi, o1, o2 = oracle.nn(A, B)
+    assert o1.max() < 0
+    rep = checks.check_nn(gi.cpu().numpy(), oi, o1, o2, A, np.arange(len(A)), B, dtype)
+    s = oracle.similarity_pairs(A, B, np.arange(len(A)), gi.cpu().numpy())
+    assert np.abs(gs.cpu().numpy().astype(np.float64) - s).max() < 3e-6
+    log("negative", dtype, rep)
 
 
 def test_mutual_c2_bf16_full_size_sampled():
