@@ -59,24 +59,31 @@ def dev_maps(p, torch, dev):
 
 
 def time_steps(fn, steps, warmup, torch, prof_launches=0):
-    """Warm up, then time exactly `steps` calls between two synchronisations.
-    Returns (ms per step, summed similarity-kernel ms, launches timed)."""
+    """Warm up, then time exactly `steps` calls between two synchronisations with nothing
+    else on the stream.  With prof_launches, the same steps run once more with the
+    library's per-launch hipEvents on (they cost a few microseconds per launch, so they
+    stay out of the pass that gives the step time) for the similarity kernel's average
+    launch duration.  Returns (ms per step, summed similarity-kernel ms, launches timed)."""
     import dense_grounded_image_amd as mr
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    if prof_launches:
-        mr.profile_begin(prof_launches)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record()
     for _ in range(steps):
         fn()
     t1.record()
     torch.cuda.synchronize()
-    kms, kn = mr.profile_end() if prof_launches else (0.0, 0)
-    return t0.elapsed_time(t1) / steps, kms, kn
+    ms = t0.elapsed_time(t1) / steps
+    kms, kn = 0.0, 0
+    if prof_launches:
+        mr.profile_begin(prof_launches)
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        kms, kn = mr.profile_end()
+    return ms, kms, kn
 
 
 def fast_work(active, N, d):

@@ -249,6 +249,10 @@ template <int P> struct Operand<AR_X3, P> {
         for (int s = 0; s < P; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[s], b.x[s], acc, 0, 0, 0);
         return acc;
     }
+    // step s alone (the same instruction and order as mfma, for interleaving chains)
+    __device__ __forceinline__ f32x16 step(int s, const Operand& b, f32x16 acc) const {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[s], b.x[s], acc, 0, 0, 0);
+    }
 };
 
 template <int AR> struct ArithTraits;
@@ -447,6 +451,27 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
         const bool ragged = (t + 1) * 32 > ndb;
         Operand<AR, P> r;
         r.load(lds + (i & 1) * BUF, jl, true, h, d, role);
+        if constexpr (AR == AR_X3 && EP == EP_KEY) {
+            if (nact == QT && !ragged) {
+                // the query tiles' step chains interleaved: consecutive products are
+                // independent, so none waits for the one before it
+                f32x16 acc[QT];
+#pragma unroll
+                for (int j = 0; j < QT; ++j) acc[j] = f32x16{};
+#pragma unroll
+                for (int st = 0; st < P; ++st)
+#pragma unroll
+                    for (int j = 0; j < QT; ++j) acc[j] = r.step(st, q[j], acc[j]);
+#pragma unroll
+                for (int j = 0; j < QT; ++j) {
+                    const int km = tile_key<false>(acc[j], t, h, ndb);
+                    const bool gt = km > (bk[j] | 15);
+                    bk[j] = gt ? km : bk[j];
+                    bt[j] = gt ? t : bt[j];
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < QT; ++j) {
             if (j < nact) {
