@@ -31,6 +31,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--main-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only", choices=OTHER, default=None,
+                    help="run just this one of the other workloads and print its record (for profiling)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device copy of this many MiB (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -170,6 +172,51 @@ def cpu_baseline(p):
             "nn_queries_per_s": round(r["nn_queries"] / dt, 1), "matches": int(len(r["pairs"]))}
 
 
+def other_batch64(args, torch, dev):
+    """64 independent 512x384 fp32 pairs in one call."""
+    import workloads
+    ps = [workloads.config_pair(3, b) for b in range(64)]
+    A = torch.stack([dev_maps(q, torch, dev)[0][0] for q in ps])
+    B = torch.stack([dev_maps(q, torch, dev)[1][0] for q in ps])
+    del ps
+    print("bench: batch data ready", file=sys.stderr, flush=True)
+    rb = run_fast(workloads.config_pair(3, 0), (A, B), args, torch, dev)
+    return {"pairs_per_s": round(64000.0 / rb["ms"], 2), "ms_per_call": round(rb["ms"], 3),
+            "nn_queries_per_s": round(rb["nn_queries"] * 1000.0 / rb["ms"], 1),
+            "roofline": roofline(rb["flops"], args.steps, rb["kernel_ms"], rb["launches"], "f32")}
+
+
+def other_bf16_1024(args, torch, dev):
+    """One 1024x768 bf16 pair, fast scheme, 15 iterations."""
+    import workloads
+    p4 = workloads.config_pair(4)
+    r4 = run_fast(p4, None, args, torch, dev)
+    return {"pairs_per_s": round(1000.0 / r4["ms"], 2), "ms_per_call": round(r4["ms"], 3),
+            "nn_queries_per_s": round(r4["nn_queries"] * 1000.0 / r4["ms"], 1),
+            "iter_active": r4["active"], "matches": r4["matches"][0],
+            "roofline": roofline(r4["flops"], args.steps, r4["kernel_ms"], r4["launches"], "bf16")}
+
+
+def other_bruteforce(args, torch, dev):
+    """Brute-force mutual NN of the 512x384 pair in bf16 (both directions)."""
+    import dense_grounded_image_amd as mr
+    import workloads
+    p2 = workloads.config_pair(2)
+    A2, B2 = dev_maps(p2, torch, dev)
+    ws = torch.empty(mr.workspace_bytes(mr.MR_OP_MUTUAL_NN, A2, B2), dtype=torch.uint8, device=dev)
+    steps = max(3, args.steps // 4)
+    ms, kms, kn = time_steps(lambda: mr.mutual_nn(A2, B2, ws=ws), steps, 2, torch, 2 * steps)
+    fl = 2.0 * 2 * p2.N * p2.N * p2.d   # both directions are computed
+    return {"pairs_per_s": round(1000.0 / ms, 2), "ms_per_call": round(ms, 3),
+            "nn_queries_per_s": round(2 * p2.N * 1000.0 / ms, 1),
+            "mfma_frac_algorithmic": round(2.0 * p2.N * p2.N * p2.d / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+            "roofline": roofline(fl, steps, kms, kn, "bf16")}
+
+
+OTHER = {"batch64-512x384-f32": other_batch64, "pair-1024x768-bf16": other_bf16_1024,
+         "pair-512x384-bf16-bruteforce": other_bruteforce}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -184,6 +231,9 @@ def main():
     import workloads
     mr.load_library()
     dev = torch.device("cuda:0")
+    if args.only:
+        print(json.dumps({args.only: OTHER[args.only](args, torch, dev)}), flush=True)
+        return
 
     p = workloads.config_pair(1)
     print("bench: workload pair-512x384-f32 ready", file=sys.stderr, flush=True)
@@ -206,40 +256,7 @@ def main():
     print("bench: fast pair %.4f ms/step" % r["ms"], file=sys.stderr, flush=True)
 
     if not args.main_only:
-        other = {}
-        # 64-pair batch, fp32
-        ps = [workloads.config_pair(3, b) for b in range(64)]
-        A = torch.stack([dev_maps(q, torch, dev)[0][0] for q in ps])
-        B = torch.stack([dev_maps(q, torch, dev)[1][0] for q in ps])
-        del ps
-        print("bench: batch data ready", file=sys.stderr, flush=True)
-        rb = run_fast(workloads.config_pair(3, 0), (A, B), args, torch, dev)
-        other["batch64-512x384-f32"] = {
-            "pairs_per_s": round(64000.0 / rb["ms"], 2), "ms_per_call": round(rb["ms"], 3),
-            "nn_queries_per_s": round(rb["nn_queries"] * 1000.0 / rb["ms"], 1),
-            "roofline": roofline(rb["flops"], args.steps, rb["kernel_ms"], rb["launches"], "f32")}
-        del A, B
-        # 1024x768 bf16 pair
-        p4 = workloads.config_pair(4)
-        r4 = run_fast(p4, None, args, torch, dev)
-        other["pair-1024x768-bf16"] = {
-            "pairs_per_s": round(1000.0 / r4["ms"], 2), "ms_per_call": round(r4["ms"], 3),
-            "nn_queries_per_s": round(r4["nn_queries"] * 1000.0 / r4["ms"], 1),
-            "iter_active": r4["active"], "matches": r4["matches"][0],
-            "roofline": roofline(r4["flops"], args.steps, r4["kernel_ms"], r4["launches"], "bf16")}
-        # brute-force mutual NN, bf16
-        p2 = workloads.config_pair(2)
-        A2, B2 = dev_maps(p2, torch, dev)
-        ws = torch.empty(mr.workspace_bytes(mr.MR_OP_MUTUAL_NN, A2, B2), dtype=torch.uint8, device=dev)
-        ms, kms, kn = time_steps(lambda: mr.mutual_nn(A2, B2, ws=ws), max(3, args.steps // 4), 2, torch,
-                                 2 * max(3, args.steps // 4))
-        fl = 2.0 * 2 * p2.N * p2.N * p2.d   # both directions are computed
-        other["pair-512x384-bf16-bruteforce"] = {
-            "pairs_per_s": round(1000.0 / ms, 2), "ms_per_call": round(ms, 3),
-            "nn_queries_per_s": round(2 * p2.N * 1000.0 / ms, 1),
-            "mfma_frac_algorithmic": round(2.0 * p2.N * p2.N * p2.d / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
-            "roofline": roofline(fl, max(3, args.steps // 4), kms, kn, "bf16")}
-        out["other"] = other
+        out["other"] = {name: OTHER[name](args, torch, dev) for name in OTHER}
 
     if not args.no_cpu:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
