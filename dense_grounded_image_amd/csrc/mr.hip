@@ -88,8 +88,8 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
 // How a similarity is computed on the matrix cores.
 //  AR_F32 : fp32 maps, fp32 products, V_MFMA_F32_32X32X2_F32 (any d).
 //  AR_BF16: bf16 maps, exact bf16 products, V_MFMA_F32_32X32X16_BF16.
-//  AR_X3  : fp32 maps split exactly into three bf16 parts x = h + m + l (a
-//           preprocessing kernel writes the planes [row][h m l][d]); the six products
+//  AR_X3  : fp32 maps split exactly into three bf16 parts x = h + m + l (the
+//           workgroup writes each staged row's planes [h m l][d] to LDS); the six products
 //           hh, hm, mh, mm, hl, lh are summed on V_MFMA_F32_32X32X16_BF16.  The three
 //           dropped products are below 2^-23 |x||y|, so the result matches an fp32
 //           dot product to within its own rounding, at 2.7x the matrix-core rate.
@@ -513,24 +513,23 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
     }
 }
 
-// Database tiles per LDS stage in stream_staged.
-template <int AR> constexpr int stage_tiles() { return 2; }
+// One workgroup streams its database segment (bf16 rows) through a ring of three LDS
+// stages of S tiles: global loads are issued two stages ahead of their LDS write,
+// one barrier per stage.  Each wave multiplies the staged tiles against its own
+// nact query tiles held in registers and keeps a per-lane running best (epilogue
+// EP).  Loads and LDS writes are issued unconditionally -- stage indices past the
+// end clamp to the last stage, chunks past the map's last row to that row's last
+// chunk -- so that the compiler counts outstanding loads exactly and waits only for
+// the oldest stage.  LDS rows past the map's end hold stale (finite) data; the
+// ragged epilogue masks them.
+constexpr int kStageTiles = 2;
 
-// One workgroup streams its database segment through a ring of three LDS stages of S
-// tiles: global loads are issued two stages ahead of their LDS write, one barrier
-// per stage, and (RA) the operands of stage k+1 are read from LDS while stage k is
-// multiplied.  Each wave multiplies the staged tiles against its own nact query
-// tiles held in registers and keeps a per-lane running best (epilogue EP).  Rows
-// must be a multiple of 16 bytes.  Loads, LDS writes and operand reads are issued
-// unconditionally -- stage indices past the end clamp to the last stage, chunks past
-// the map's last row to that row's last chunk -- so that the compiler counts
-// outstanding memory operations exactly and waits only for the oldest stage.  LDS
-// rows past the map's end hold stale (finite) data; the ragged epilogue masks them.
-template <int AR, int P, int EP, int S, bool RA>
+template <int AR, int P, int EP, int S>
 __device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb,
                                               char* lds, const Operand<AR, P> (&q)[qt_of<AR, P>()], int nact,
                                               int h, int jl, int d, int role, int (&bk)[qt_of<AR, P>()],
                                               int (&bt)[qt_of<AR, P>()], float (&bv)[qt_of<AR, P>()]) {
+    static_assert(AR == AR_BF16, "the staged ring holds bf16 rows");
     constexpr int QT = qt_of<AR, P>();
     constexpr int NB = 3;
     constexpr int STAGE = S * 32 * lds_row_bytes<AR, P>();
@@ -538,9 +537,11 @@ __device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, i
     const int row_chunks = rb >> 4;
     const int nst = (t1 - t0 + S - 1) / S;
     u32x4 slot0[MAXC], slot1[MAXC];
-    Operand<AR, P> opr0[S], opr1[S];
+    Operand<AR, P> opr[S];
+    int off[P];
+    Operand<AR, P>::db_offsets(jl, h, d, off);
 
-    // chunks of stage k that hold real rows (k clamped)
+    // chunks of stage k that hold real rows
     auto stage_chunks = [&](int k) {
         const int r0 = (t0 + S * k) * 32;
         const int nr = ndb - r0 < S * 32 ? ndb - r0 : S * 32;
@@ -562,40 +563,14 @@ __device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, i
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
             const int ch = threadIdx.x + c * kThreads;
-            if (ch < nch) {
-                if constexpr (AR == AR_X3) {
-                    // four fp32 components -> their h, m, l bf16 in the row's three planes
-                    constexpr int D = 8 * P / 3;
-                    const int r = ch / (D / 4), c0 = (ch - r * (D / 4)) * 4;
-                    uint16_t a[3][4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) split3(__uint_as_float(st[c][e]), a[0][e], a[1][e], a[2][e]);
-                    char* dst = buf + r * 6 * D + c0 * 2;
-#pragma unroll
-                    for (int x = 0; x < 3; ++x)
-                        *reinterpret_cast<uint2*>(dst + x * 2 * D) =
-                            uint2{(uint32_t)a[x][0] | ((uint32_t)a[x][1] << 16), (uint32_t)a[x][2] | ((uint32_t)a[x][3] << 16)};
-                } else {
-                    *reinterpret_cast<u32x4*>(buf + ch * 16) = st[c];
-                }
-            }
+            if (ch < nch) *reinterpret_cast<u32x4*>(buf + ch * 16) = st[c];
         }
     };
-    // a stage holds 32*S consecutive rows: split rows in their three planes, other
-    // rows as they are in the map
-    const int tile_lds = AR == AR_X3 ? 32 * lds_row_bytes<AR, P>() : 32 * rb;
-    auto read = [&](int k, Operand<AR, P> (&o)[S]) {
+    // the S tiles of stage k, read into the A operands
+    auto read = [&](int k) {
         const char* buf = lds + (k % NB) * STAGE;
 #pragma unroll
-        for (int x = 0; x < S; ++x) {
-            if constexpr (AR == AR_BF16) {
-                int off[P];
-                Operand<AR, P>::db_offsets(jl, h, d, off);
-                o[x].load_db(buf + x * tile_lds, off);
-            } else {
-                o[x].load(buf + x * tile_lds, jl, true, h, d, role);
-            }
-        }
+        for (int x = 0; x < S; ++x) opr[x].load_db(buf + x * 32 * rb, off);
     };
     auto epilogue = [&](const f32x16& acc, int t, bool ragged, int j) {
         if constexpr (EP == EP_TILE) {
@@ -611,7 +586,7 @@ __device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, i
             bt[j] = gt ? t : bt[j];
         }
     };
-    auto compute = [&](int k, const Operand<AR, P> (&o)[S]) {
+    auto compute = [&](int k) {
 #pragma unroll
         for (int x = 0; x < S; ++x) {
             const int t = t0 + S * k + x;
@@ -621,11 +596,11 @@ __device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, i
                 // products of tile j+1
                 if (nact == QT) {
 #pragma unroll
-                    for (int j = 0; j < QT; ++j) epilogue(o[x].mfma(q[j], f32x16{}), t, ragged, j);
+                    for (int j = 0; j < QT; ++j) epilogue(opr[x].mfma(q[j], f32x16{}), t, ragged, j);
                 } else {
 #pragma unroll
                     for (int j = 0; j < QT; ++j)
-                        if (j < nact) epilogue(o[x].mfma(q[j], f32x16{}), t, ragged, j);
+                        if (j < nact) epilogue(opr[x].mfma(q[j], f32x16{}), t, ragged, j);
                 }
             }
         }
@@ -633,31 +608,24 @@ __device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, i
 
     if (nst <= 0) return;
     // stage k: global -> slot k&1 at iteration k-3 (the prologue for k < 3), LDS
-    // buffer k%3 at iteration k-2, operands (RA) at iteration k-1, multiplied at k
+    // buffer k%3 at iteration k-2, read and multiplied at iteration k
     fetch(0, slot0);
     fetch(1, slot1);
     put(0, slot0);
     fetch(2, slot0);
     put(1, slot1);
     __syncthreads();
-    if constexpr (RA) read(0, opr0);
     for (int k = 0; k < nst; k += 2) {
-        // buffers of stages past the end are free: writing or reading them is harmless
+        // buffers of stages past the end are free: writing them is harmless
         fetch(k + 3, slot1);
-        if constexpr (RA) read(k + 1, opr1);
-        else read(k, opr0);
-        compute(k, opr0);
+        read(k);
+        compute(k);
         put(k + 2, slot0);
         __syncthreads();
         if (k + 1 >= nst) break;
         fetch(k + 4, slot0);
-        if constexpr (RA) {
-            read(k + 2, opr0);
-            compute(k + 1, opr1);
-        } else {
-            read(k + 1, opr0);
-            compute(k + 1, opr0);
-        }
+        read(k + 1);
+        compute(k + 1);
         put(k + 3, slot1);
         __syncthreads();
     }
@@ -674,8 +642,7 @@ __device__ __forceinline__ void stream_db(const char* __restrict__ dbytes, int r
     if constexpr (AR != AR_BF16)
         stream_tiles<AR, P, EP>(dbytes, rb, t0, t1, ndb, lds, q, nact, h, jl, d, role, bk, bt, bv);
     else
-        stream_staged<AR, P, EP, stage_tiles<AR>(), false>(dbytes, rb, t0, t1, ndb, lds, q, nact, h, jl, d,
-                                                                   role, bk, bt, bv);
+        stream_staged<AR, P, EP, kStageTiles>(dbytes, rb, t0, t1, ndb, lds, q, nact, h, jl, d, role, bk, bt, bv);
 }
 
 // Full work items of bf16 maps, without LDS or barriers: each wave reads the
@@ -798,7 +765,7 @@ void nn_argmax_kernel(NNArgs a) {
     constexpr int QT = qt_of<AR, P>();
     constexpr bool TB = ArithTraits<AR>::tile_best;   // keys carry (score, tile), not (score, row)
     constexpr int QB = 32 * QT;          // queries per wave
-    constexpr int LDS_TILES = (AR == AR_BF16 ? 3 * stage_tiles<AR>() : 2) * 32 * lds_row_bytes<AR, P>();
+    constexpr int LDS_TILES = (AR == AR_BF16 ? 3 * kStageTiles : 2) * 32 * lds_row_bytes<AR, P>();
     constexpr int LDS_RED = kWaves * QB * 8;
     __shared__ __attribute__((aligned(16))) char lds[LDS_TILES > LDS_RED ? LDS_TILES : LDS_RED];
     const int lane = threadIdx.x & 63;
