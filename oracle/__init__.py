@@ -6,6 +6,10 @@ baseline may import this package; the matching library never does.
 
 Inputs are fp32 numpy arrays holding exactly the values the GPU library
 receives (bf16 maps are passed as their exact fp32 widening).
+
+``metric`` selects what "nearest" means: INNER (0, descriptor maps: largest
+inner product) or NEG_SQ_L2 (1, pointmaps: smallest Euclidean distance; the
+returned scores are minus the squared distances).
 """
 from __future__ import annotations
 
@@ -14,6 +18,8 @@ import os
 import subprocess
 
 import numpy as np
+
+INNER, NEG_SQ_L2 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -45,6 +51,15 @@ def _bind(lib):
     lib.orc_fast.argtypes = [P, i32, i32, P, i64, i32, i32, i32, i32, i32, i32, f64, P, i64, P, P,
                              P, P]
     lib.orc_fast.restype = ctypes.c_int
+    lib.orc_nn_metric.argtypes = [P, i64, P, i64, i32, i32, i32, P, P, P]
+    lib.orc_nn_metric.restype = ctypes.c_int
+    lib.orc_nn_rows_metric.argtypes = [P, P, i64, P, i64, i32, i32, i32, P, P, P]
+    lib.orc_nn_rows_metric.restype = ctypes.c_int
+    lib.orc_similarity_pairs_metric.argtypes = [P, P, i32, i32, P, P, i64, P]
+    lib.orc_similarity_pairs_metric.restype = ctypes.c_int
+    lib.orc_fast_metric.argtypes = [P, i32, i32, P, i64, i32, i32, i32, i32, i32, i32, i32, f64, P, i64,
+                                    P, P, P, P]
+    lib.orc_fast_metric.restype = ctypes.c_int
     return lib
 
 
@@ -89,8 +104,8 @@ class Oracle:
             self._own = _bind(ctypes.CDLL(self._path))
         return self._own
 
-    def nn(self, q, db, nthreads=None):
-        """Lowest-index argmax_k <q[i], db[k]> per query row; returns (idx, top1, top2)."""
+    def nn(self, q, db, nthreads=None, metric=INNER):
+        """Lowest-index argmax_k score(q[i], db[k]) per query row; returns (idx, top1, top2)."""
         lib = self.lib
         q, db = _f32(q), _f32(db)
         assert q.shape[1] == db.shape[1]
@@ -98,12 +113,12 @@ class Oracle:
         idx = np.empty(nq, np.int32)
         t1 = np.empty(nq, np.float64)
         t2 = np.empty(nq, np.float64)
-        rc = lib.orc_nn(_ptr(q), nq, _ptr(db), db.shape[0], q.shape[1], nthreads or default_threads(),
-                        _ptr(idx), _ptr(t1), _ptr(t2))
+        rc = lib.orc_nn_metric(_ptr(q), nq, _ptr(db), db.shape[0], q.shape[1], metric,
+                               nthreads or default_threads(), _ptr(idx), _ptr(t1), _ptr(t2))
         assert rc == 0, rc
         return idx, t1, t2
 
-    def nn_rows(self, qmap, rows, db, nthreads=None):
+    def nn_rows(self, qmap, rows, db, nthreads=None, metric=INNER):
         """nn() for the query rows qmap[rows]."""
         lib = self.lib
         qmap, db = _f32(qmap), _f32(db)
@@ -112,20 +127,20 @@ class Oracle:
         idx = np.empty(n, np.int32)
         t1 = np.empty(n, np.float64)
         t2 = np.empty(n, np.float64)
-        rc = lib.orc_nn_rows(_ptr(qmap), _ptr(rows), n, _ptr(db), db.shape[0], qmap.shape[1],
-                             nthreads or default_threads(), _ptr(idx), _ptr(t1), _ptr(t2))
+        rc = lib.orc_nn_rows_metric(_ptr(qmap), _ptr(rows), n, _ptr(db), db.shape[0], qmap.shape[1], metric,
+                                    nthreads or default_threads(), _ptr(idx), _ptr(t1), _ptr(t2))
         assert rc == 0, rc
         return idx, t1, t2
 
-    def similarity_pairs(self, A, B, ia, ib):
-        """binary64 <A[ia[t]], B[ib[t]]> for each t."""
+    def similarity_pairs(self, A, B, ia, ib, metric=INNER):
+        """binary64 score(A[ia[t]], B[ib[t]]) for each t."""
         lib = self.lib
         A, B = _f32(A), _f32(B)
         ia = np.ascontiguousarray(ia, dtype=np.int32)
         ib = np.ascontiguousarray(ib, dtype=np.int32)
         out = np.empty(ia.shape[0], np.float64)
-        rc = lib.orc_similarity_pairs(_ptr(A), _ptr(B), A.shape[1], _ptr(ia), _ptr(ib), ia.shape[0],
-                                      _ptr(out))
+        rc = lib.orc_similarity_pairs_metric(_ptr(A), _ptr(B), A.shape[1], metric, _ptr(ia), _ptr(ib),
+                                             ia.shape[0], _ptr(out))
         assert rc == 0, rc
         return out
 
@@ -140,13 +155,14 @@ class Oracle:
         assert m >= 0, m
         return pairs[:m].copy()
 
-    def mutual_nn(self, A, B, nthreads=None):
+    def mutual_nn(self, A, B, nthreads=None, metric=INNER):
         """Brute-force mutual NN of two maps: (pairs, nn12, top1_12, top2_12, nn21, top1_21, top2_21)."""
-        n12, a1, a2 = self.nn(A, B, nthreads)
-        n21, b1, b2 = self.nn(B, A, nthreads)
+        n12, a1, a2 = self.nn(A, B, nthreads, metric)
+        n21, b1, b2 = self.nn(B, A, nthreads, metric)
         return self.mutual(n12, n21), n12, a1, a2, n21, b1, b2
 
-    def fast(self, A, H1, W1, B, stride, offset, max_iters, seed_limit=-1, nthreads=None, eps=1e-5):
+    def fast(self, A, H1, W1, B, stride, offset, max_iters, seed_limit=-1, nthreads=None, eps=1e-5,
+             metric=INNER):
         """Fast reciprocal matching seeded on image 1's grid.
 
         Returns dict(pairs int32 [m,2] ascending in u, clean uint8 [m], active int64 [T],
@@ -163,9 +179,9 @@ class Oracle:
         active = np.zeros(max(1, max_iters), np.int64)
         npairs = ctypes.c_int64(0)
         nq = ctypes.c_int64(0)
-        rc = lib.orc_fast(_ptr(A), H1, W1, _ptr(B), B.shape[0], A.shape[1], stride, offset, max_iters,
-                          seed_limit, nthreads or default_threads(), eps, _ptr(pairs), cap,
-                          ctypes.byref(npairs), _ptr(clean), _ptr(active), ctypes.byref(nq))
+        rc = lib.orc_fast_metric(_ptr(A), H1, W1, _ptr(B), B.shape[0], A.shape[1], metric, stride, offset,
+                                 max_iters, seed_limit, nthreads or default_threads(), eps, _ptr(pairs), cap,
+                                 ctypes.byref(npairs), _ptr(clean), _ptr(active), ctypes.byref(nq))
         assert rc == 0, rc
         m = npairs.value
         return dict(pairs=pairs[:m].copy(), clean=clean[:m].copy(), active=active[:max_iters].copy(),

@@ -2,7 +2,9 @@
  * oracle.c -- TEST INFRASTRUCTURE ONLY.
  *
  * A plain, slow CPU oracle for dense nearest-neighbour (NN) search and
- * reciprocal matching between two per-pixel descriptor maps.  Only the test
+ * reciprocal matching between two per-pixel maps: descriptor maps (nearest =
+ * largest inner product) or pointmaps (nearest = smallest Euclidean distance
+ * between 3D points).  Only the test
  * suite, the smoke check and the benchmark's CPU-baseline leg load it; the
  * matching library never does, and the two share no code.
  *
@@ -11,7 +13,9 @@
  * over the descriptor components in ascending order.  fp32 x fp32 products
  * are exact in binary64 and a 24-term sum of unit-vector products errs by
  * about 1e-15, so for these inputs the oracle is exact for all practical
- * purposes.  No blocking, no reordering, no vectorisation tricks; threads only
+ * purposes.  Pointmap distances are binary64 sums of the squared binary64
+ * differences of the fp32 coordinates (each difference of two fp32 values of
+ * similar magnitude is exact in binary64).  No blocking, no reordering, no vectorisation tricks; threads only
  * split independent queries.
  *
  * Sources (the pages are cited by title and section, never by line):
@@ -26,8 +30,13 @@
  *       from a sparse grid of seed pixels, repeatedly map each one to its best
  *       match in the other image and map that match back, collecting the
  *       pairs that map onto each other.
+ *  [P3b] "DUSt3R and MASt3R explained", the paragraph on recovering the cameras:
+ *       each image's pointmap holds one 3D point per pixel, both in the first
+ *       camera's frame, and two pixels correspond when their predicted 3D
+ *       points are nearest neighbours in that shared space.
  * Readings where the pages are silent (tie-break, seed origin, what one
- * iteration is, which pair is collected) are stated at each function.
+ * iteration is, which pair is collected, which distance for pointmaps) are
+ * stated at each function.
  *
  * Parity status: every function here is pinned by tests under tests/
  * (closed forms, brute force on tiny inputs, invariants); none is unpinned.
@@ -56,6 +65,31 @@ static double orc_similarity(const float* a, const float* b, int d)
 }
 
 /* ------------------------------------------------------------------------
+ * Score of a (query, database) row pair under a metric; larger is nearer.
+ *  ORC_INNER     : the similarity above (descriptor maps).
+ *  ORC_NEG_SQ_L2 : minus the squared Euclidean distance, the differences and
+ *                  their squares summed over ascending components in binary64
+ *                  (pointmaps; [P3b]: nearest neighbours in the shared 3D space.
+ *                  The pages name no norm; the plain reading is Euclidean, and
+ *                  its square has the same nearest neighbour).
+ * ------------------------------------------------------------------------ */
+#define ORC_INNER 0
+#define ORC_NEG_SQ_L2 1
+
+static double orc_score(const float* a, const float* b, int d, int metric)
+{
+    if (metric == ORC_NEG_SQ_L2) {
+        double acc = 0.0;
+        for (int k = 0; k < d; ++k) {
+            const double diff = (double)a[k] - (double)b[k];
+            acc += diff * diff;
+        }
+        return -acc;
+    }
+    return orc_similarity(a, b, d);
+}
+
+/* ------------------------------------------------------------------------
  * NN of one query among n database rows: the first (lowest) index attaining
  * the maximum similarity, found by a scan with a strict ">" update.  Also
  * returns the best score (top1) and the best score over all other indices
@@ -63,13 +97,13 @@ static double orc_similarity(const float* a, const float* b, int d)
  * [P1] section 3: j = argmax_k <D1[i], D2[k]>.  The pages do not say how ties
  * are broken; the reading here is the lowest index.
  * ------------------------------------------------------------------------ */
-static void orc_nn_one(const float* q, const float* db, int64_t n, int d,
+static void orc_nn_one(const float* q, const float* db, int64_t n, int d, int metric,
                        int32_t* idx, double* top1, double* top2)
 {
     double best = -INFINITY, second = -INFINITY;
     int64_t arg = -1;
     for (int64_t k = 0; k < n; ++k) {
-        double s = orc_similarity(q, db + k * (int64_t)d, d);
+        double s = orc_score(q, db + k * (int64_t)d, d, metric);
         if (s > best) {
             second = best;
             best = s;
@@ -91,6 +125,7 @@ typedef struct {
     const float* db;
     int64_t ndb;
     int d;
+    int metric;
     int32_t* out_idx;
     double* out_top1;
     double* out_top2;
@@ -104,7 +139,7 @@ static void* orc_nn_worker(void* p)
         int64_t row = j->qidx ? (int64_t)j->qidx[t] : t;
         double t1, t2;
         int32_t id;
-        orc_nn_one(j->qmap + row * (int64_t)j->d, j->db, j->ndb, j->d, &id, &t1, &t2);
+        orc_nn_one(j->qmap + row * (int64_t)j->d, j->db, j->ndb, j->d, j->metric, &id, &t1, &t2);
         j->out_idx[t] = id;
         if (j->out_top1) j->out_top1[t] = t1;
         if (j->out_top2) j->out_top2[t] = t2;
@@ -113,8 +148,8 @@ static void* orc_nn_worker(void* p)
 }
 
 static int orc_nn_parallel(const float* qmap, const int32_t* qidx, int64_t nq, const float* db,
-                           int64_t ndb, int d, int nthreads, int32_t* out_idx, double* out_top1,
-                           double* out_top2)
+                           int64_t ndb, int d, int metric, int nthreads, int32_t* out_idx,
+                           double* out_top1, double* out_top2)
 {
     if (nq <= 0) return ORC_OK;
     if (nthreads < 1) nthreads = 1;
@@ -124,7 +159,7 @@ static int orc_nn_parallel(const float* qmap, const int32_t* qidx, int64_t nq, c
     pthread_t th[256];
     int started[256];
     for (int i = 0; i < nthreads; ++i) {
-        jobs[i] = (orc_nn_job){qmap, qidx, nq, db, ndb, d, out_idx, out_top1, out_top2,
+        jobs[i] = (orc_nn_job){qmap, qidx, nq, db, ndb, d, metric, out_idx, out_top1, out_top2,
                                nq * i / nthreads, nq * (i + 1) / nthreads};
         started[i] = 0;
     }
@@ -142,31 +177,54 @@ static int orc_nn_parallel(const float* qmap, const int32_t* qidx, int64_t nq, c
  * Exported entry points
  * ===================================================================== */
 
-/* NN of every query row q[0..nq) among db[0..ndb) (rows of d floats), as
- * defined by orc_nn_one.  out_top1/out_top2 may be NULL. */
-int orc_nn(const float* q, int64_t nq, const float* db, int64_t ndb, int32_t d, int32_t nthreads,
-           int32_t* out_idx, double* out_top1, double* out_top2)
+/* NN of every query row q[0..nq) among db[0..ndb) (rows of d floats) under a
+ * metric (ORC_INNER or ORC_NEG_SQ_L2), as defined by orc_nn_one.
+ * out_top1/out_top2 (the two best scores) may be NULL. */
+int orc_nn_metric(const float* q, int64_t nq, const float* db, int64_t ndb, int32_t d, int32_t metric,
+                  int32_t nthreads, int32_t* out_idx, double* out_top1, double* out_top2)
 {
-    if (!q || !db || !out_idx || nq < 0 || ndb < 0 || d < 1) return ORC_ERR_ARG;
-    return orc_nn_parallel(q, NULL, nq, db, ndb, d, nthreads, out_idx, out_top1, out_top2);
+    if (!q || !db || !out_idx || nq < 0 || ndb < 0 || d < 1 || metric < 0 || metric > 1)
+        return ORC_ERR_ARG;
+    return orc_nn_parallel(q, NULL, nq, db, ndb, d, metric, nthreads, out_idx, out_top1, out_top2);
 }
 
 /* Same, for the query rows qmap[qidx[t]], t < nq. */
+int orc_nn_rows_metric(const float* qmap, const int32_t* qidx, int64_t nq, const float* db, int64_t ndb,
+                       int32_t d, int32_t metric, int32_t nthreads, int32_t* out_idx, double* out_top1,
+                       double* out_top2)
+{
+    if (!qmap || !qidx || !db || !out_idx || nq < 0 || ndb < 0 || d < 1 || metric < 0 || metric > 1)
+        return ORC_ERR_ARG;
+    return orc_nn_parallel(qmap, qidx, nq, db, ndb, d, metric, nthreads, out_idx, out_top1, out_top2);
+}
+
+/* Score of the given row pairs: out[t] = score(A[ia[t]], B[ib[t]]). */
+int orc_similarity_pairs_metric(const float* A, const float* B, int32_t d, int32_t metric,
+                                const int32_t* ia, const int32_t* ib, int64_t n, double* out)
+{
+    if (!A || !B || !ia || !ib || !out || d < 1 || n < 0 || metric < 0 || metric > 1) return ORC_ERR_ARG;
+    for (int64_t t = 0; t < n; ++t)
+        out[t] = orc_score(A + (int64_t)ia[t] * d, B + (int64_t)ib[t] * d, d, metric);
+    return ORC_OK;
+}
+
+/* The inner-product forms of the three calls above. */
+int orc_nn(const float* q, int64_t nq, const float* db, int64_t ndb, int32_t d, int32_t nthreads,
+           int32_t* out_idx, double* out_top1, double* out_top2)
+{
+    return orc_nn_metric(q, nq, db, ndb, d, ORC_INNER, nthreads, out_idx, out_top1, out_top2);
+}
+
 int orc_nn_rows(const float* qmap, const int32_t* qidx, int64_t nq, const float* db, int64_t ndb,
                 int32_t d, int32_t nthreads, int32_t* out_idx, double* out_top1, double* out_top2)
 {
-    if (!qmap || !qidx || !db || !out_idx || nq < 0 || ndb < 0 || d < 1) return ORC_ERR_ARG;
-    return orc_nn_parallel(qmap, qidx, nq, db, ndb, d, nthreads, out_idx, out_top1, out_top2);
+    return orc_nn_rows_metric(qmap, qidx, nq, db, ndb, d, ORC_INNER, nthreads, out_idx, out_top1, out_top2);
 }
 
-/* Similarity of the given row pairs: out[t] = s(A[ia[t]], B[ib[t]]). */
 int orc_similarity_pairs(const float* A, const float* B, int32_t d, const int32_t* ia,
                          const int32_t* ib, int64_t n, double* out)
 {
-    if (!A || !B || !ia || !ib || !out || d < 1 || n < 0) return ORC_ERR_ARG;
-    for (int64_t t = 0; t < n; ++t)
-        out[t] = orc_similarity(A + (int64_t)ia[t] * d, B + (int64_t)ib[t] * d, d);
-    return ORC_OK;
+    return orc_similarity_pairs_metric(A, B, d, ORC_INNER, ia, ib, n, out);
 }
 
 /* ------------------------------------------------------------------------
@@ -207,8 +265,8 @@ int64_t orc_mutual(const int32_t* nn12, int64_t n1, const int32_t* nn21, int64_t
  *  - iterations t = 0 .. T-1; a chain that has not converged after T
  *    iterations contributes nothing;
  *  - the output is the set of collected pairs, ascending in u.
- * Every NN here is orc_nn_one (lowest index on ties); results are memoised
- * per pixel, which changes no result.
+ * Every NN here is orc_nn_one under the given metric (lowest index on ties);
+ * results are memoised per pixel, which changes no result.
  *
  * Extra records for the tests:
  *  - active[t]   : number of distinct pixels carried by live chains at the
@@ -217,13 +275,13 @@ int64_t orc_mutual(const int32_t* nn12, int64_t n1, const int32_t* nn21, int64_t
  *                  only NN decisions whose top1 - top2 margin exceeds eps;
  *  - nn_queries  : number of NN searches performed (after memoisation).
  * ------------------------------------------------------------------------ */
-int orc_fast(const float* A, int32_t H1, int32_t W1, const float* B, int64_t n2, int32_t d,
-             int32_t stride, int32_t offset, int32_t T, int32_t seed_limit, int32_t nthreads,
-             double eps, int32_t* pairs, int64_t cap, int64_t* n_pairs, uint8_t* pair_clean,
-             int64_t* active, int64_t* nn_queries)
+int orc_fast_metric(const float* A, int32_t H1, int32_t W1, const float* B, int64_t n2, int32_t d,
+                    int32_t metric, int32_t stride, int32_t offset, int32_t T, int32_t seed_limit,
+                    int32_t nthreads, double eps, int32_t* pairs, int64_t cap, int64_t* n_pairs,
+                    uint8_t* pair_clean, int64_t* active, int64_t* nn_queries)
 {
     if (!A || !B || !pairs || !n_pairs || H1 < 0 || W1 < 0 || n2 < 0 || d < 1 || stride < 1 ||
-        offset < 0 || T < 0)
+        offset < 0 || T < 0 || metric < 0 || metric > 1)
         return ORC_ERR_ARG;
     const int64_t n1 = (int64_t)H1 * W1;
     *n_pairs = 0;
@@ -282,7 +340,7 @@ int orc_fast(const float* A, int32_t H1, int32_t W1, const float* B, int64_t n2,
         for (int64_t c = 0; c < ns; ++c) if (alive[c]) seen1[cur[c]] = 0;
         if (active) active[t] = distinct;
         if (distinct == 0) break;
-        orc_nn_parallel(A, todo, nt, B, n2, d, nthreads, res, t1, t2);
+        orc_nn_parallel(A, todo, nt, B, n2, d, metric, nthreads, res, t1, t2);
         for (int64_t k = 0; k < nt; ++k) { nn12[todo[k]] = res[k]; mg12[todo[k]] = t1[k] - t2[k]; }
         if (nn_queries) *nn_queries += nt;
 
@@ -294,7 +352,7 @@ int orc_fast(const float* A, int32_t H1, int32_t W1, const float* B, int64_t n2,
             if (!seen2[v]) { seen2[v] = 1; if (nn21[v] < 0) todo[nt++] = v; }
         }
         for (int64_t c = 0; c < ns; ++c) if (alive[c]) seen2[nn12[cur[c]]] = 0;
-        orc_nn_parallel(B, todo, nt, A, n1, d, nthreads, res, t1, t2);
+        orc_nn_parallel(B, todo, nt, A, n1, d, metric, nthreads, res, t1, t2);
         for (int64_t k = 0; k < nt; ++k) { nn21[todo[k]] = res[k]; mg21[todo[k]] = t1[k] - t2[k]; }
         if (nn_queries) *nn_queries += nt;
 
@@ -332,4 +390,14 @@ done:
     free(cur); free(alive); free(clean); free(nn12); free(mg12); free(nn21); free(mg21);
     free(match); free(mclean); free(seen1); free(seen2); free(todo); free(res); free(t1); free(t2);
     return rc;
+}
+
+/* The inner-product form of orc_fast_metric. */
+int orc_fast(const float* A, int32_t H1, int32_t W1, const float* B, int64_t n2, int32_t d,
+             int32_t stride, int32_t offset, int32_t T, int32_t seed_limit, int32_t nthreads,
+             double eps, int32_t* pairs, int64_t cap, int64_t* n_pairs, uint8_t* pair_clean,
+             int64_t* active, int64_t* nn_queries)
+{
+    return orc_fast_metric(A, H1, W1, B, n2, d, ORC_INNER, stride, offset, T, seed_limit, nthreads, eps,
+                           pairs, cap, n_pairs, pair_clean, active, nn_queries);
 }

@@ -324,6 +324,85 @@ def pin_fast_clean_flag(orc):
     assert r["clean"].tolist() == [0, 1]
 
 
+# ============================================================================ pointmaps
+# Metric 1: nearest = smallest Euclidean distance between 3D points ("DUSt3R and MASt3R
+# explained", the paragraph on recovering the cameras); scores are -|a - b|^2.
+
+PT = 1
+
+
+def pin_point_closed_forms(orc):
+    """Hand-derived distances: the nearest point is not the one of largest inner product,
+    and equal distances go to the lowest index."""
+    q = np.array([[1, 0, 0], [0, 0, 0], [0.5, 0.5, 0]], np.float32)
+    db = np.array([[10, 0, 0], [1.5, 0, 0], [-1, 0, 0], [0, 1, 0], [0, 0, -1]], np.float32)
+    idx, t1, t2 = orc.nn(q, db, metric=PT)
+    # q0: squared distances 81, 0.25, 4, 2, 2 -> 1;  q1: 100, 2.25, 1, 1, 1 -> 2 (tie 2, 3, 4)
+    # q2: 90.5, 1.25, 2.5, 0.5, 1.5 -> 3
+    assert idx.tolist() == [1, 2, 3]
+    assert t1.tolist() == [-0.25, -1.0, -0.5] and t2.tolist() == [-2.0, -1.0, -1.25]
+    assert orc.nn(q, db)[0].tolist()[0] == 0          # the inner product picks (10, 0, 0)
+    s = orc.similarity_pairs(q, db, [0, 2], [4, 0], metric=PT)
+    assert s.tolist() == [-2.0, -90.5]
+
+
+def pin_point_numpy_bruteforce(orc):
+    """Against numpy's float64 pairwise distances (first index of the minimum), d = 1..4."""
+    rng = np.random.default_rng(31)
+    for d in (1, 2, 3, 4):
+        A = rng.uniform(-3, 3, size=(29, d)).astype(np.float32)
+        B = rng.uniform(-3, 3, size=(35, d)).astype(np.float32)
+        idx, t1, t2 = orc.nn(A, B, metric=PT)
+        D = ((A[:, None, :].astype(np.float64) - B[None, :, :].astype(np.float64)) ** 2).sum(-1)
+        assert (idx == D.argmin(1)).all()
+        Ds = np.sort(D, axis=1)
+        assert np.abs(-t1 - Ds[:, 0]).max() < 1e-12 and np.abs(-t2 - Ds[:, 1]).max() < 1e-12
+
+
+def pin_point_translation_invariance(orc):
+    """Shifting both maps by the same vector changes no distance (integer coordinates,
+    so every shifted value is exact)."""
+    rng = np.random.default_rng(32)
+    A = rng.integers(-100, 100, size=(40, 3)).astype(np.float32)
+    B = rng.integers(-100, 100, size=(45, 3)).astype(np.float32)
+    sh = np.array([1024, -2048, 512], np.float32)
+    r0 = orc.nn(A, B, metric=PT)
+    r1 = orc.nn(A + sh, B + sh, metric=PT)
+    for a, b in zip(r0, r1):
+        assert (a == b).all()
+
+
+def pin_point_planted_closed_form(orc):
+    """Noise-free planted pointmaps (X2[q] = X1[src(q)] exactly, distinct X1 points):
+    M* = {(p, min{q : src(q) = p})}; the fast scheme at stride 1 returns the same set and
+    every fast match (u, v) has u = src(v)."""
+    p = workloads.make_pointmaps(14, 11, seed=33, warp="shift", sigma=0.0, rho=0.0)
+    assert (p.D2 == p.D1[p.src]).all()
+    first = {}
+    for q, s in enumerate(p.src.tolist()):
+        first.setdefault(s, q)
+    expect = [list(e) for e in sorted(first.items())]
+    assert orc.mutual_nn(p.D1, p.D2, metric=PT)[0].tolist() == expect
+    assert orc.fast(p.D1, p.H, p.W, p.D2, 1, 0, 2, metric=PT)["pairs"].tolist() == expect
+    for u, v in orc.fast(p.D1, p.H, p.W, p.D2, 3, 1, 10, metric=PT)["pairs"].tolist():
+        assert p.src[v] == u
+
+
+def pin_point_fast_invariants(orc):
+    """Noisy, occluded pointmaps: fast matches are mutual, stride 1 is brute force, and the
+    output equals the set characterisation walked from the NN maps."""
+    p = workloads.make_pointmaps(18, 15, seed=34, warp="affine", sigma=0.02, rho=0.3)
+    mset = _pairs_set(orc.mutual_nn(p.D1, p.D2, metric=PT)[0])
+    assert len(mset) > 0
+    assert _pairs_set(orc.fast(p.D1, p.H, p.W, p.D2, 1, 0, 3, metric=PT)["pairs"]) == mset
+    n12 = orc.nn(p.D1, p.D2, metric=PT)[0]
+    n21 = orc.nn(p.D2, p.D1, metric=PT)[0]
+    for stride, off, T in ((4, 2, 1), (3, 1, 3), (5, 0, 10)):
+        got = _pairs_set(orc.fast(p.D1, p.H, p.W, p.D2, stride, off, T, metric=PT)["pairs"])
+        assert got <= mset
+        assert got == _chain_set(n12, n21, _grid(p.H, p.W, stride, off), T)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 
 

@@ -30,6 +30,13 @@ MUTANTS = {
     "seed_grid_column_major": ("cur[c] = (int32_t)(y * W1 + x);", "cur[c] = (int32_t)(x * H1 + y);"),
     "clean_flag_ignores_backward": ("if (!(mg12[u] > eps) || !(mg21[v] > eps)) clean[c] = 0;",
                                     "if (!(mg12[u] > eps)) clean[c] = 0;"),
+    # pointmap metric
+    "point_metric_ignored": ("if (metric == ORC_NEG_SQ_L2) {", "if (0) {"),
+    "point_farthest_instead_of_nearest": ("return -acc;", "return acc;"),
+    "point_dropped_first_coordinate": ("for (int k = 0; k < d; ++k) {", "for (int k = 1; k < d; ++k) {"),
+    "point_abs_difference": ("acc += diff * diff;", "acc += fabs(diff);"),
+    "point_backward_search_inner_product": ("orc_nn_parallel(B, todo, nt, A, n1, d, metric,",
+                                            "orc_nn_parallel(B, todo, nt, A, n1, d, ORC_INNER,"),
 }
 
 

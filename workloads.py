@@ -1,4 +1,5 @@
-"""Seeded synthetic descriptor-map pairs shaped like MASt3R's matching workloads.
+"""Seeded synthetic descriptor-map pairs shaped like MASt3R's matching workloads
+(and pointmap pairs shaped like DUSt3R's, see make_pointmaps).
 
 This module only makes inputs.  It holds none of the matching arithmetic (no
 similarity, no nearest-neighbour search, no reciprocity test): the CPU oracle
@@ -187,6 +188,61 @@ def make_pair(H: int, W: int, d: int, seed: int, warp: str = "shift", sigma: flo
         offset = stride // 2
     return Pair(name=name, H=H, W=W, d=d, dtype=dtype, D1=D1f, D2=D2f, D1_bits=b1, D2_bits=b2,
                 src=src, seed=seed, stride=stride, offset=offset, max_iters=max_iters)
+
+
+# ----------------------------------------------------------------------------- pointmaps
+
+def make_pointmaps(H: int, W: int, seed: int, warp: str = "affine", sigma: float = 0.005, rho: float = 0.3,
+                   name: str = "pointmaps", stride: int = 8, offset: Optional[int] = None,
+                   max_iters: int = 10) -> Pair:
+    """A planted pair of pointmaps (d = 3, metres, both in camera 1's frame).
+
+    After the pages (DUSt3R/MASt3R explained: a pointmap holds, per pixel, the 3D
+    point that pixel observes; both views are expressed in the first camera's frame,
+    so where the images overlap their pointmaps hold the same 3D points):
+      1. image 1 sees a smooth surface: depth z(y, x) = 3 + 0.4 sin(a) cos(b) + 0.3 (x/W - 1/2)
+         with a, b linear in the pixel coordinates (random frequencies and phases), back-
+         projected through a pinhole camera with focal length W pixels and the principal
+         point at the image centre: X1[p] = z ((x - cx)/W, (y - cy)/W, 1);
+      2. image 2 is a backward warp of it (the descriptor warps): X2[q] = X1[src(q)];
+      3. X2 += sigma * N(0, 1) per coordinate (metres);
+      4. floor(rho N) image-2 pixels are replaced by points drawn uniformly in the
+         bounding box of X1 (src = -1);
+      5. both maps are cast to fp32 (no normalisation: pointmaps are not unit vectors).
+    Draw order: surface parameters, warp, noise, occlusion subset, occluder points."""
+    N = H * W
+    rng = np.random.Generator(np.random.PCG64(seed))
+    fa, fb = rng.uniform(1.0, 3.0, size=2)
+    pa, pb = rng.uniform(0.0, 2.0 * math.pi, size=2)
+    ys, xs = np.meshgrid(np.arange(H, dtype=np.float64), np.arange(W, dtype=np.float64), indexing="ij")
+    ys, xs = ys.ravel(), xs.ravel()
+    z = 3.0 + 0.4 * np.sin(2 * math.pi * fa * xs / W + pa) * np.cos(2 * math.pi * fb * ys / H + pb) \
+        + 0.3 * (xs / W - 0.5)
+    cx, cy = (W - 1) / 2.0, (H - 1) / 2.0
+    X1 = np.stack([z * (xs - cx) / W, z * (ys - cy) / W, z], axis=1)
+    if warp == "shift":
+        src = _warp_shift(rng, H, W)
+    elif warp == "affine":
+        src = _warp_affine(rng, H, W)
+    elif warp == "identity":
+        src = np.arange(N, dtype=np.int64)
+    else:
+        raise ValueError(f"unknown warp {warp!r}")
+    X2 = X1[src].copy()
+    if sigma > 0:
+        X2 += sigma * rng.standard_normal((N, 3))
+    src = src.astype(np.int32)
+    k = int(math.floor(rho * N))
+    if k > 0:
+        occ = rng.choice(N, size=k, replace=False)
+        lo, hi = X1.min(axis=0), X1.max(axis=0)
+        X2[occ] = lo + (hi - lo) * rng.uniform(size=(k, 3))
+        src[occ] = -1
+    if offset is None:
+        offset = stride // 2
+    return Pair(name=name, H=H, W=W, d=3, dtype="f32", D1=X1.astype(np.float32), D2=X2.astype(np.float32),
+                D1_bits=None, D2_bits=None, src=src, seed=seed, stride=stride, offset=offset,
+                max_iters=max_iters)
 
 
 # ----------------------------------------------------------------------------- the five workloads
