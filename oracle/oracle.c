@@ -250,6 +250,17 @@ int64_t orc_mutual(const int32_t* nn12, int64_t n1, const int32_t* nn21, int64_t
     return m;
 }
 
+/* Margin of an NN decision from its two best scores: absolute for the inner
+ * product, relative to the second distance for pointmaps (no second candidate:
+ * infinite; a zero second distance, i.e. a tie at distance 0: zero). */
+static double orc_margin(double top1, double top2, int metric)
+{
+    if (metric != ORC_NEG_SQ_L2) return top1 - top2;
+    if (top2 == -INFINITY) return INFINITY;
+    if (top2 == 0.0) return 0.0;
+    return (top1 - top2) / -top2;
+}
+
 /* ------------------------------------------------------------------------
  * Fast reciprocal matching.  [P3], the fast-matching paragraph; [P1] section 3.
  *
@@ -272,7 +283,9 @@ int64_t orc_mutual(const int32_t* nn12, int64_t n1, const int32_t* nn21, int64_t
  *  - active[t]   : number of distinct pixels carried by live chains at the
  *                  start of iteration t (NULL to skip);
  *  - pair_clean  : per output pair, 1 if some chain that collected it made
- *                  only NN decisions whose top1 - top2 margin exceeds eps;
+ *                  only NN decisions whose margin exceeds eps: top1 - top2 for
+ *                  the inner product; for pointmaps the relative margin
+ *                  (d2 - d1) / d2 of the two smallest squared distances;
  *  - nn_queries  : number of NN searches performed (after memoisation).
  * ------------------------------------------------------------------------ */
 int orc_fast_metric(const float* A, int32_t H1, int32_t W1, const float* B, int64_t n2, int32_t d,
@@ -341,7 +354,7 @@ int orc_fast_metric(const float* A, int32_t H1, int32_t W1, const float* B, int6
         if (active) active[t] = distinct;
         if (distinct == 0) break;
         orc_nn_parallel(A, todo, nt, B, n2, d, metric, nthreads, res, t1, t2);
-        for (int64_t k = 0; k < nt; ++k) { nn12[todo[k]] = res[k]; mg12[todo[k]] = t1[k] - t2[k]; }
+        for (int64_t k = 0; k < nt; ++k) { nn12[todo[k]] = res[k]; mg12[todo[k]] = orc_margin(t1[k], t2[k], metric); }
         if (nn_queries) *nn_queries += nt;
 
         /* backward: NN21 of every distinct landing pixel not yet known */
@@ -353,7 +366,7 @@ int orc_fast_metric(const float* A, int32_t H1, int32_t W1, const float* B, int6
         }
         for (int64_t c = 0; c < ns; ++c) if (alive[c]) seen2[nn12[cur[c]]] = 0;
         orc_nn_parallel(B, todo, nt, A, n1, d, metric, nthreads, res, t1, t2);
-        for (int64_t k = 0; k < nt; ++k) { nn21[todo[k]] = res[k]; mg21[todo[k]] = t1[k] - t2[k]; }
+        for (int64_t k = 0; k < nt; ++k) { nn21[todo[k]] = res[k]; mg21[todo[k]] = orc_margin(t1[k], t2[k], metric); }
         if (nn_queries) *nn_queries += nt;
 
         /* reciprocity check: converged chains are collected, the rest restart */

@@ -4,6 +4,7 @@ Tolerance (fixed by the benchmark spec for this path): the GPU's NN index must
 equal the oracle's wherever the oracle's top-1 to top-2 similarity margin
 exceeds 1e-5; elsewhere the chosen neighbour's (binary64) similarity must be
 within 1e-5 of the maximum (fp32 maps) or within 1e-2 * |max| (bf16 maps).
+Pointmaps (nearest points) use the relative rule derived at MARGIN_PT.
 The oracle computes in binary64 on exactly the values the GPU receives.
 
 For the fast reciprocal scheme, which is an iteration rather than a closed
@@ -21,6 +22,12 @@ import numpy as np
 import oracle
 
 MARGIN = 1e-5
+# Pointmaps (metric 1, scores = -squared distance): the fp32 squared distance errs by
+# at most about 4 * 2^-24 = 2.4e-7 of itself, so the index is fixed wherever the two
+# smallest exact squared distances differ by more than 1e-6 of the second, and
+# elsewhere the chosen point lies within 1e-6 (relative) of the nearest.
+POINT = 1
+MARGIN_PT = 1e-6
 
 
 def tol_for(dtype: str, top1: np.ndarray) -> np.ndarray:
@@ -29,21 +36,37 @@ def tol_for(dtype: str, top1: np.ndarray) -> np.ndarray:
     return np.full_like(top1, 1e-5)
 
 
-def check_nn(gpu_idx, o_idx, o_top1, o_top2, qmap, rows, db, dtype):
+def margin_of(top1, top2, metric=0):
+    """Decision margin from the oracle's two best scores (relative for pointmaps)."""
+    top1, top2 = np.asarray(top1, np.float64), np.asarray(top2, np.float64)
+    if metric != POINT:
+        return top1 - top2
+    with np.errstate(divide="ignore", invalid="ignore"):
+        m = (top1 - top2) / -top2
+    m = np.where(np.isneginf(top2), np.inf, m)
+    return np.where(top2 == 0, 0.0, m)
+
+
+def _near_enough(s, top1, dtype, metric):
+    """Is score s (of the GPU's choice) within tolerance of the best score top1?"""
+    if metric == POINT:   # -s and -top1 are squared distances
+        return -s <= -top1 * (1 + MARGIN_PT) + 1e-30
+    return s >= top1 - tol_for(dtype, top1)
+
+
+def check_nn(gpu_idx, o_idx, o_top1, o_top2, qmap, rows, db, dtype, metric=0):
     """NN parity for queries qmap[rows] against db.  Returns a small report dict."""
     gpu_idx = np.asarray(gpu_idx).astype(np.int64)
     o_idx = np.asarray(o_idx).astype(np.int64)
-    margin = o_top1 - o_top2
-    sure = margin > MARGIN
+    sure = margin_of(o_top1, o_top2, metric) > (MARGIN_PT if metric == POINT else MARGIN)
     bad_exact = np.nonzero(sure & (gpu_idx != o_idx))[0]
     assert bad_exact.size == 0, f"{bad_exact.size} clear-margin NN mismatches, e.g. query {rows[bad_exact[0]]}"
     amb = np.nonzero(~sure)[0]
     if amb.size:
         assert (gpu_idx[amb] >= 0).all()
-        s = oracle.similarity_pairs(qmap, db, np.asarray(rows)[amb], gpu_idx[amb])
-        tol = tol_for(dtype, o_top1[amb])
-        worst = (o_top1[amb] - s - tol).max()
-        assert worst <= 0, f"an ambiguous NN is {worst} beyond tolerance"
+        s = oracle.similarity_pairs(qmap, db, np.asarray(rows)[amb], gpu_idx[amb], metric=metric)
+        ok = _near_enough(s, o_top1[amb], dtype, metric)
+        assert ok.all(), f"{int((~ok).sum())} ambiguous NNs beyond tolerance"
     return dict(n=len(gpu_idx), exact=int(sure.sum()), ambiguous=int(amb.size),
                 equal=int((gpu_idx == o_idx).sum()))
 
@@ -57,20 +80,20 @@ def check_one_to_one_sorted(pairs):
     assert len(np.unique(v)) == len(v), "a pixel of image 2 is matched twice"
 
 
-def check_reciprocal(pairs, A, B, dtype, nthreads=None):
+def check_reciprocal(pairs, A, B, dtype, nthreads=None, metric=0):
     """Rule (ii) for every listed GPU pair."""
     pairs = np.asarray(pairs).reshape(-1, 2)
     if len(pairs) == 0:
         return
     u, v = pairs[:, 0], pairs[:, 1]
-    _, f1, _ = oracle.nn_rows(A, u, B, nthreads)
-    _, b1, _ = oracle.nn_rows(B, v, A, nthreads)
-    s = oracle.similarity_pairs(A, B, u, v)
-    assert (s >= f1 - tol_for(dtype, f1)).all(), "a GPU pair is not a forward NN within tolerance"
-    assert (s >= b1 - tol_for(dtype, b1)).all(), "a GPU pair is not a backward NN within tolerance"
+    _, f1, _ = oracle.nn_rows(A, u, B, nthreads, metric=metric)
+    _, b1, _ = oracle.nn_rows(B, v, A, nthreads, metric=metric)
+    s = oracle.similarity_pairs(A, B, u, v, metric=metric)
+    assert _near_enough(s, f1, dtype, metric).all(), "a GPU pair is not a forward NN within tolerance"
+    assert _near_enough(s, b1, dtype, metric).all(), "a GPU pair is not a backward NN within tolerance"
 
 
-def check_fast(gpu_pairs, orc, A, B, dtype, nthreads=None):
+def check_fast(gpu_pairs, orc, A, B, dtype, nthreads=None, metric=0):
     """Rules (i)-(iii) against a full oracle run `orc` (dict from oracle.fast)."""
     gpu_pairs = np.asarray(gpu_pairs).reshape(-1, 2)
     check_one_to_one_sorted(gpu_pairs)
@@ -79,25 +102,27 @@ def check_fast(gpu_pairs, orc, A, B, dtype, nthreads=None):
     clean = {(int(a), int(b)) for (a, b), c in zip(orc["pairs"], orc["clean"]) if c}
     missing = clean - gset
     assert not missing, f"{len(missing)} clean oracle pairs missing, e.g. {sorted(missing)[:3]}"
-    check_reciprocal(gpu_pairs, A, B, dtype, nthreads)
+    check_reciprocal(gpu_pairs, A, B, dtype, nthreads, metric)
     return dict(gpu=len(gset), oracle=len(oset), clean=len(clean), common=len(gset & oset),
                 gpu_only=len(gset - oset), oracle_only=len(oset - gset))
 
 
-def oracle_chains(A, B, seeds, T, nthreads=None, eps=MARGIN):
+def oracle_chains(A, B, seeds, T, nthreads=None, eps=None, metric=0):
     """Follow the chains of the given seeds with the oracle's NN, one iteration at a time
     (for workloads too large for a full oracle run).  Returns {(u, v): clean}."""
+    if eps is None:
+        eps = MARGIN_PT if metric == POINT else MARGIN
     cur = {int(s): [int(s), True] for s in seeds}
     out = {}
     for _ in range(T):
         if not cur:
             break
         us = np.array(sorted({c[0] for c in cur.values()}), np.int32)
-        f, f1, f2 = oracle.nn_rows(A, us, B, nthreads)
-        fmap = {int(u): (int(v), m) for u, v, m in zip(us, f, f1 - f2)}
+        f, f1, f2 = oracle.nn_rows(A, us, B, nthreads, metric=metric)
+        fmap = {int(u): (int(v), m) for u, v, m in zip(us, f, margin_of(f1, f2, metric))}
         vs = np.array(sorted({fmap[c[0]][0] for c in cur.values()}), np.int32)
-        g, g1, g2 = oracle.nn_rows(B, vs, A, nthreads)
-        gmap = {int(v): (int(u), m) for v, u, m in zip(vs, g, g1 - g2)}
+        g, g1, g2 = oracle.nn_rows(B, vs, A, nthreads, metric=metric)
+        gmap = {int(v): (int(u), m) for v, u, m in zip(vs, g, margin_of(g1, g2, metric))}
         nxt = {}
         for s, (u, ok) in cur.items():
             v, m1 = fmap[u]

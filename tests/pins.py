@@ -403,6 +403,23 @@ def pin_point_fast_invariants(orc):
         assert got == _chain_set(n12, n21, _grid(p.H, p.W, stride, off), T)
 
 
+def pin_point_clean_flag_relative(orc):
+    """Noise-free planted pointmaps, stride 1, one iteration: a source pixel p is matched to
+    its first preimage at distance 0.  The decision is a tie (margin 0, not clean) when p
+    has two preimages, and otherwise has relative margin (d2 - 0) / d2 = 1 both ways, so
+    it is clean even against eps = 0.5, which the squared distances themselves (< 0.5 m^2
+    between neighbouring points here) would not pass."""
+    p = workloads.make_pointmaps(12, 10, seed=35, warp="shift", sigma=0.0, rho=0.0)
+    pre = {}
+    for q, s_ in enumerate(p.src.tolist()):
+        pre.setdefault(s_, []).append(q)
+    r = orc.fast(p.D1, p.H, p.W, p.D2, 1, 0, 1, eps=0.5, metric=PT)
+    got = {(int(u), int(v)): int(c) for (u, v), c in zip(r["pairs"].tolist(), r["clean"].tolist())}
+    want = {(s_, qs[0]): int(len(qs) == 1) for s_, qs in pre.items()}
+    assert got == want
+    assert 0 < sum(want.values()) < len(want)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 
 

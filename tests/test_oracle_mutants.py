@@ -37,6 +37,7 @@ MUTANTS = {
     "point_abs_difference": ("acc += diff * diff;", "acc += fabs(diff);"),
     "point_backward_search_inner_product": ("orc_nn_parallel(B, todo, nt, A, n1, d, metric,",
                                             "orc_nn_parallel(B, todo, nt, A, n1, d, ORC_INNER,"),
+    "point_margin_absolute": ("return (top1 - top2) / -top2;", "return top1 - top2;"),
 }
 
 
