@@ -21,11 +21,13 @@ LIB_PATH = os.path.join(_HERE, "libmr.so")
 
 MR_F32, MR_BF16 = 0, 1
 MR_OP_NN_ARGMAX, MR_OP_MUTUAL_NN, MR_OP_FAST_RECIPROCAL = 0, 1, 2
+MR_OP_POINT_NN, MR_OP_POINT_MUTUAL_NN, MR_OP_POINT_FAST_RECIPROCAL = 3, 4, 5
 STATUS = {0: "MR_OK", 1: "MR_ERR_NULL", 2: "MR_ERR_SHAPE", 3: "MR_ERR_DTYPE", 4: "MR_ERR_PARAM",
           5: "MR_ERR_WORKSPACE", 6: "MR_ERR_CAPACITY", 7: "MR_ERR_DEVICE"}
 
 EXPORTS = ("mr_workspace_bytes", "mr_status_str", "mr_seed_count", "mr_nn_argmax", "mr_mutual_nn",
-           "mr_fast_reciprocal", "mr_profile_begin", "mr_profile_end")
+           "mr_fast_reciprocal", "mr_point_nn", "mr_point_mutual_nn", "mr_point_fast_reciprocal",
+           "mr_profile_begin", "mr_profile_end")
 
 
 class MrMap(ctypes.Structure):
@@ -64,6 +66,12 @@ def load_library(path: str = LIB_PATH):
     lib.mr_mutual_nn.restype = ctypes.c_int
     lib.mr_fast_reciprocal.argtypes = [MP, MP, i32, i32, i32, P, i64, P, P, P, sz, P]
     lib.mr_fast_reciprocal.restype = ctypes.c_int
+    lib.mr_point_nn.argtypes = lib.mr_nn_argmax.argtypes
+    lib.mr_point_nn.restype = ctypes.c_int
+    lib.mr_point_mutual_nn.argtypes = lib.mr_mutual_nn.argtypes
+    lib.mr_point_mutual_nn.restype = ctypes.c_int
+    lib.mr_point_fast_reciprocal.argtypes = lib.mr_fast_reciprocal.argtypes
+    lib.mr_point_fast_reciprocal.restype = ctypes.c_int
     lib.mr_profile_begin.argtypes = [i32]
     lib.mr_profile_begin.restype = ctypes.c_int
     lib.mr_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
@@ -135,11 +143,7 @@ def workspace_bytes(op: int, a, b, n_q: int = 0, stride: int = 1, offset: int = 
 
 # ----------------------------------------------------------------------------- entry points
 
-def nn_argmax(q, db, q_idx=None, with_score: bool = False, ws=None):
-    """NN in db of every (or every listed) pixel of q, lowest index on ties.
-
-    q, db: [H, W, d] or [B, H, W, d].  q_idx: None or int32 [n] / [B, n] pixel ids of q.
-    Returns idx int32 [B, n] (and fp32 scores if with_score); B dim dropped for 3-D input."""
+def _nn(point, q, db, q_idx, with_score, ws):
     torch = _torch()
     lib = load_library()
     squeeze = q.dim() == 3
@@ -154,21 +158,33 @@ def nn_argmax(q, db, q_idx=None, with_score: bool = False, ws=None):
         qptr = q_idx.data_ptr()
     out_idx = torch.empty((B, n), dtype=torch.int32, device=q.device)
     out_score = torch.empty((B, n), dtype=torch.float32, device=q.device) if with_score else None
-    need = lib.mr_workspace_bytes(MR_OP_NN_ARGMAX, ctypes.byref(mq), ctypes.byref(mdb), n, 1, 0)
+    op, fn = (MR_OP_POINT_NN, "mr_point_nn") if point else (MR_OP_NN_ARGMAX, "mr_nn_argmax")
+    need = lib.mr_workspace_bytes(op, ctypes.byref(mq), ctypes.byref(mdb), n, 1, 0)
     ws = _workspace(need, q.device, ws)
-    rc = lib.mr_nn_argmax(ctypes.byref(mq), ctypes.byref(mdb), qptr, n, out_idx.data_ptr(),
-                          out_score.data_ptr() if with_score else None, ws.data_ptr(), ws.numel(),
-                          _stream(q))
-    _check("mr_nn_argmax", rc)
+    rc = getattr(lib, fn)(ctypes.byref(mq), ctypes.byref(mdb), qptr, n, out_idx.data_ptr(),
+                          out_score.data_ptr() if with_score else None, ws.data_ptr(), ws.numel(), _stream(q))
+    _check(fn, rc)
     if squeeze:
         out_idx = out_idx[0]
         out_score = out_score[0] if with_score else None
     return (out_idx, out_score) if with_score else out_idx
 
 
-def mutual_nn(a, b, ws=None):
-    """Brute-force reciprocal NN.  Returns (pairs int32 [B, cap, 2], n_pairs int64 [B],
-    nn_ab int32 [B, Na], nn_ba int32 [B, Nb]); pairs[b, :n_pairs[b]] ascending in i."""
+def nn_argmax(q, db, q_idx=None, with_score: bool = False, ws=None):
+    """NN in db of every (or every listed) pixel of q, lowest index on ties.
+
+    q, db: [H, W, d] or [B, H, W, d].  q_idx: None or int32 [n] / [B, n] pixel ids of q.
+    Returns idx int32 [B, n] (and fp32 scores if with_score); B dim dropped for 3-D input."""
+    return _nn(False, q, db, q_idx, with_score, ws)
+
+
+def point_nn(q, db, q_idx=None, with_dist2: bool = False, ws=None):
+    """Nearest point in pointmap db of every (or every listed) pixel of pointmap q (fp32,
+    d <= 4), lowest index on ties; with_dist2 also returns the fp32 squared distances."""
+    return _nn(True, q, db, q_idx, with_dist2, ws)
+
+
+def _mutual(point, a, b, ws):
     torch = _torch()
     lib = load_library()
     ma, mb = _as_map(a), _as_map(b)
@@ -179,12 +195,24 @@ def mutual_nn(a, b, ws=None):
     nn_ba = torch.empty((B, Nb), dtype=torch.int32, device=dev)
     pairs = torch.empty((B, cap, 2), dtype=torch.int32, device=dev)
     n_pairs = torch.empty((B,), dtype=torch.int64, device=dev)
-    need = lib.mr_workspace_bytes(MR_OP_MUTUAL_NN, ctypes.byref(ma), ctypes.byref(mb), 0, 1, 0)
+    op, fn = (MR_OP_POINT_MUTUAL_NN, "mr_point_mutual_nn") if point else (MR_OP_MUTUAL_NN, "mr_mutual_nn")
+    need = lib.mr_workspace_bytes(op, ctypes.byref(ma), ctypes.byref(mb), 0, 1, 0)
     ws = _workspace(need, dev, ws)
-    rc = lib.mr_mutual_nn(ctypes.byref(ma), ctypes.byref(mb), nn_ab.data_ptr(), nn_ba.data_ptr(),
+    rc = getattr(lib, fn)(ctypes.byref(ma), ctypes.byref(mb), nn_ab.data_ptr(), nn_ba.data_ptr(),
                           pairs.data_ptr(), cap, n_pairs.data_ptr(), ws.data_ptr(), ws.numel(), _stream(a))
-    _check("mr_mutual_nn", rc)
+    _check(fn, rc)
     return pairs, n_pairs, nn_ab, nn_ba
+
+
+def mutual_nn(a, b, ws=None):
+    """Brute-force reciprocal NN.  Returns (pairs int32 [B, cap, 2], n_pairs int64 [B],
+    nn_ab int32 [B, Na], nn_ba int32 [B, Nb]); pairs[b, :n_pairs[b]] ascending in i."""
+    return _mutual(False, a, b, ws)
+
+
+def point_mutual_nn(a, b, ws=None):
+    """Brute-force reciprocal nearest points of two pointmaps; returns as mutual_nn."""
+    return _mutual(True, a, b, ws)
 
 
 class FastReciprocal:
@@ -192,9 +220,11 @@ class FastReciprocal:
     workspace buffers are allocated once, so repeated calls allocate nothing."""
 
     def __init__(self, a, b, stride: int = 8, offset: Optional[int] = None, max_iters: int = 10,
-                 record_active: bool = True):
+                 record_active: bool = True, point: bool = False):
         torch = _torch()
         self.lib = load_library()
+        self.fn = self.lib.mr_point_fast_reciprocal if point else self.lib.mr_fast_reciprocal
+        op = MR_OP_POINT_FAST_RECIPROCAL if point else MR_OP_FAST_RECIPROCAL
         self.stride = int(stride)
         self.offset = int(stride // 2 if offset is None else offset)
         self.max_iters = int(max_iters)
@@ -206,8 +236,7 @@ class FastReciprocal:
         self.n_pairs = torch.empty((self.B,), dtype=torch.int64, device=dev)
         self.active = (torch.empty((self.B, max(1, self.max_iters)), dtype=torch.int32, device=dev)
                        if record_active else None)
-        need = self.lib.mr_workspace_bytes(MR_OP_FAST_RECIPROCAL, ctypes.byref(ma), ctypes.byref(mb), 0,
-                                           self.stride, self.offset)
+        need = self.lib.mr_workspace_bytes(op, ctypes.byref(ma), ctypes.byref(mb), 0, self.stride, self.offset)
         self.ws = _workspace(need, dev)
         self.shape = (tuple(a.shape), tuple(b.shape), a.dtype)
 
@@ -215,12 +244,11 @@ class FastReciprocal:
         if (tuple(a.shape), tuple(b.shape), a.dtype) != self.shape:
             raise ValueError("shapes differ from the ones this FastReciprocal was built for")
         ma, mb = _as_map(a), _as_map(b)
-        rc = self.lib.mr_fast_reciprocal(ctypes.byref(ma), ctypes.byref(mb), self.stride, self.offset,
-                                         self.max_iters, self.pairs.data_ptr(), self.cap,
-                                         self.n_pairs.data_ptr(),
-                                         self.active.data_ptr() if self.active is not None else None,
-                                         self.ws.data_ptr(), self.ws.numel(), _stream(a))
-        _check("mr_fast_reciprocal", rc)
+        rc = self.fn(ctypes.byref(ma), ctypes.byref(mb), self.stride, self.offset, self.max_iters,
+                     self.pairs.data_ptr(), self.cap, self.n_pairs.data_ptr(),
+                     self.active.data_ptr() if self.active is not None else None,
+                     self.ws.data_ptr(), self.ws.numel(), _stream(a))
+        _check(self.fn.__name__, rc)
         return self.pairs, self.n_pairs, self.active
 
 
@@ -228,6 +256,12 @@ def fast_reciprocal(a, b, stride: int = 8, offset: Optional[int] = None, max_ite
     """Fast reciprocal matching seeded on a's grid.  Returns (pairs int32 [B, cap, 2],
     n_pairs int64 [B], iter_active int32 [B, max_iters]); pairs ascending in the a-pixel."""
     return FastReciprocal(_batched(a), _batched(b), stride, offset, max_iters)(_batched(a), _batched(b))
+
+
+def point_fast_reciprocal(a, b, stride: int = 8, offset: Optional[int] = None, max_iters: int = 10):
+    """The fast reciprocal scheme on two pointmaps (nearest points); returns as fast_reciprocal."""
+    return FastReciprocal(_batched(a), _batched(b), stride, offset, max_iters,
+                          point=True)(_batched(a), _batched(b))
 
 
 def matches(pairs, n_pairs, b: int = 0):

@@ -1017,6 +1017,138 @@ __global__ __launch_bounds__(kThreads) void recover_rows_kernel(NNArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------- pointmaps
+
+// Nearest neighbours of 3D points ("DUSt3R and MASt3R explained", the paragraph on
+// recovering the cameras: two pixels correspond when their predicted 3D points are
+// nearest neighbours in the shared frame).  d <= 4 is too short for the matrix cores,
+// and the expanded form 2<x,y> - |y|^2 that would suit them cancels badly for points
+// far from the origin, so the distance is computed directly on the VALU.
+constexpr int kMaxPointD = 4;
+constexpr int kPointQPL = 2;      // queries per lane
+constexpr int kPointGroup = 16;   // database points per tracked group
+
+typedef const float __attribute__((address_space(4))) cfloat;   // read through the scalar cache
+
+// Squared distance with a fixed operation order and rounding (no contraction or
+// reassociation): the search and the row recovery compute it bitwise alike.
+template <int D, class T>
+__device__ __forceinline__ float point_dist2(const float (&x)[D], const T* p) {
+    float t = __fsub_rn(x[0], p[0]);
+    float acc = __fmul_rn(t, t);
+#pragma unroll
+    for (int c = 1; c < D; ++c) {
+        t = __fsub_rn(x[c], p[c]);
+        acc = __fmaf_rn(t, t, acc);
+    }
+    return acc;
+}
+
+// Work item = (block of 128 queries, segment of database points), one per wave; waves
+// never synchronise.  A lane holds two queries; the group of 16 database points it
+// compares them with is uniform across the wave, so it comes through scalar loads
+// and enters the VALU as scalar operands.  Per query and group a minimum tree folds
+// the running best; the lane remembers the first group that reached it and, at the
+// end of the segment, recomputes that group to find the lowest row at that
+// distance.  Items merge with atomicMax on (ordered(-dist2), ~row) keys.  The number
+// of segments follows the live query count (read on the device), a multiple of 8
+// when possible so that each XCD keeps the same eighth of the database in its L2.
+template <int D>
+__global__ __launch_bounds__(kThreads) void point_nn_kernel(NNArgs a) {
+    constexpr int QW = 64 * kPointQPL;   // queries per wave
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.y;
+    const int n = a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (a.active_out) a.active_out[pair * a.active_stride] = n;
+        if (a.zero_count) a.zero_count[pair * a.zero_stride] = 0;
+    }
+    const int ndb = a.ndb;
+    if (n <= 0 || ndb <= 0) return;
+    const int nqb = (n + QW - 1) / QW;
+    const int waves = (int)gridDim.x * kWaves;
+    const int seg_cap = ndb / 256 > 1 ? ndb / 256 : 1;        // segments of at least 256 points
+    int nseg = waves / nqb;
+    nseg = nseg < 1 ? 1 : (nseg > seg_cap ? seg_cap : nseg);
+    if (nseg >= 8) nseg &= ~7;
+    const float* qbase = static_cast<const float*>(a.qmap) + pair * a.q_pair_elems;
+    const float* dbase = static_cast<const float*>(a.dbmap) + pair * a.db_pair_elems;
+    uint64_t* keys = a.keys + pair * a.keys_stride;
+
+    // consecutive workgroups take consecutive items, so item % 8 (the segment's XCD
+    // share when nseg is a multiple of 8) follows blockIdx.x % 8
+    for (int item = wv * (int)gridDim.x + (int)blockIdx.x; item < nqb * nseg; item += waves) {
+        const int qb = item / nseg, sg = item - qb * nseg;
+        const int p0 = (int)((int64_t)sg * ndb / nseg), p1 = (int)((int64_t)(sg + 1) * ndb / nseg);
+        float x[kPointQPL][D], bv[kPointQPL];
+        int qp[kPointQPL], bg[kPointQPL];
+#pragma unroll
+        for (int j = 0; j < kPointQPL; ++j) {
+            qp[j] = qb * QW + j * 64 + lane;
+            int64_t row = qp[j];
+            bool valid = qp[j] < n;
+            if (valid && a.qsrc == Q_LIST)
+                row = static_cast<const int32_t*>(a.qlist)[pair * a.qlist_stride + qp[j]];
+            else if (valid && a.qsrc == Q_KEYS)
+                row = key_row(static_cast<const uint64_t*>(a.qlist)[pair * a.qlist_stride + qp[j]]);
+            valid = valid && row >= 0 && row < a.nq_rows;
+#pragma unroll
+            for (int c = 0; c < D; ++c) x[j][c] = valid ? qbase[row * D + c] : 0.0f;
+            bv[j] = INFINITY;
+            bg[j] = -1;
+        }
+        auto group = [&](int g, const auto* P, int npts) {
+#pragma unroll
+            for (int j = 0; j < kPointQPL; ++j) {
+                float dd[kPointGroup];
+#pragma unroll
+                for (int k = 0; k < kPointGroup; ++k) {
+                    dd[k] = point_dist2<D>(x[j], P + k * D);
+                    if (npts < kPointGroup && k >= npts) dd[k] = INFINITY;
+                }
+                auto mn3 = [](float u, float v, float w) {
+                    return __builtin_elementwise_minimum(__builtin_elementwise_minimum(u, v), w);
+                };
+                const float m0 = mn3(dd[0], dd[1], dd[2]), m1 = mn3(dd[3], dd[4], dd[5]);
+                const float m2 = mn3(dd[6], dd[7], dd[8]), m3 = mn3(dd[9], dd[10], dd[11]);
+                const float m4 = mn3(dd[12], dd[13], dd[14]), m5 = mn3(dd[15], bv[j], m0);
+                const float m = mn3(mn3(m1, m2, m3), m4, m5);
+                bg[j] = m != bv[j] ? g : bg[j];     // strictly nearer: the earliest group wins ties
+                bv[j] = m;
+            }
+        };
+        int g = p0;
+        for (; g + kPointGroup <= p1; g += kPointGroup)
+            group(g, (const cfloat*)(dbase + (int64_t)g * D), kPointGroup);
+        if (g < p1) {
+            // the last, partial group: its loads stay inside the segment (the first
+            // point stands in for the missing ones, whose distances are masked)
+            const int npts = p1 - g;
+            float P[kPointGroup * D];
+#pragma unroll
+            for (int k = 0; k < kPointGroup; ++k)
+#pragma unroll
+                for (int c = 0; c < D; ++c) P[k * D + c] = dbase[(int64_t)(k < npts ? g + k : g) * D + c];
+            group(g, P, npts);
+        }
+        // the lowest row of the remembered group at the best distance
+#pragma unroll
+        for (int j = 0; j < kPointQPL; ++j) {
+            int found = -1;
+            if (bg[j] >= 0) {
+                for (int k = kPointGroup - 1; k >= 0; --k) {
+                    const int pt = bg[j] + k;
+                    if (pt < p1 && point_dist2<D>(x[j], dbase + (int64_t)pt * D) == bv[j]) found = pt;
+                }
+            }
+            if (qp[j] < n && found >= 0)
+                atomicMax(reinterpret_cast<unsigned long long*>(&keys[qp[j]]),
+                          (unsigned long long)pack_key(-bv[j], (uint32_t)found));
+        }
+    }
+}
+
 __global__ void fill_u64_kernel(uint64_t* p, int64_t n, uint64_t v) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = v;
@@ -1027,12 +1159,16 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
         p[i] = v;
 }
 
-// keys -> row ids (and optionally scores)
-__global__ void decode_keys_kernel(const uint64_t* keys, int64_t n, int32_t* idx, float* score) {
+// keys -> row ids (and optionally scores; point searches store minus the squared
+// distance, which `negate` turns back into the distance)
+__global__ void decode_keys_kernel(const uint64_t* keys, int64_t n, int32_t* idx, float* score, int negate) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         const uint64_t k = keys[i];
         idx[i] = key_row(k);
-        if (score) score[i] = k ? from_ordered((uint32_t)(k >> 32)) : -INFINITY;
+        if (score) {
+            const float v = k ? from_ordered((uint32_t)(k >> 32)) : -INFINITY;
+            score[i] = negate ? -v : v;
+        }
     }
 }
 
@@ -1329,6 +1465,58 @@ int launch_nn(const NNArgs& a, int ar, int batch, hipStream_t st) {
     return MR_OK;
 }
 
+// What "nearest" means for a call: the largest inner product (descriptor maps) or
+// the smallest Euclidean distance (pointmaps).
+enum Metric { M_INNER = 0, M_POINT = 1 };
+
+template <int D>
+void launch_point_t(const NNArgs& a, int batch, hipStream_t st) {
+    static int resident = 0;
+    if (resident == 0) {
+        int dev = 0, cus = 256, per_cu = 0;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            hipDeviceProp_t prop;
+            if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
+        }
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, point_nn_kernel<D>, kThreads, 0) != hipSuccess ||
+            per_cu < 1)
+            per_cu = 1;
+        resident = cus * per_cu;
+    }
+    int g = resident / (batch > 0 ? batch : 1);
+    if (g >= 64) g &= ~7;
+    hipLaunchKernelGGL((point_nn_kernel<D>), dim3(g < 1 ? 1 : g, batch), dim3(kThreads), 0, st, a);
+}
+
+// One NN search under a metric (the similarity kernel of every entry point).
+int launch_search(const NNArgs& a, int metric, int ar, int batch, hipStream_t st) {
+    if (metric != M_POINT) return launch_nn(a, ar, batch, st);
+    const bool prof = g_prof.on && g_prof.used < g_prof.cap;
+    if (prof && hipEventRecord(g_prof.ev[2 * g_prof.used], st) != hipSuccess) return MR_ERR_DEVICE;
+    switch (a.d) {
+        case 1: launch_point_t<1>(a, batch, st); break;
+        case 2: launch_point_t<2>(a, batch, st); break;
+        case 3: launch_point_t<3>(a, batch, st); break;
+        case 4: launch_point_t<4>(a, batch, st); break;
+        default: return MR_ERR_SHAPE;
+    }
+    if (dev_err()) return MR_ERR_DEVICE;
+    if (prof) {
+        if (hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st) != hipSuccess) return MR_ERR_DEVICE;
+        ++g_prof.used;
+    }
+    return MR_OK;
+}
+
+// Maps valid for a metric: pointmaps are fp32 with at most 4 coordinates.
+int validate_for(const mr_map* a, const mr_map* b, int metric) {
+    const int rc = validate_pair(a, b);
+    if (rc || metric != M_POINT) return rc;
+    if (a->dtype != MR_F32) return MR_ERR_DTYPE;
+    if (a->d > kMaxPointD) return MR_ERR_SHAPE;
+    return MR_OK;
+}
+
 // Kernel arguments for queries taken from map q (role q_role) against map db.
 NNArgs nn_args(const mr_map* q, const void* qdata, int q_role, const mr_map* db, const void* dbdata, int db_role) {
     NNArgs a;
@@ -1398,51 +1586,10 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 template <class T> T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
-}  // namespace
-
-// ============================================================================ C ABI
-
-extern "C" {
-
-const char* mr_status_str(int status) {
-    switch (status) {
-        case MR_OK: return "ok";
-        case MR_ERR_NULL: return "a required pointer is NULL";
-        case MR_ERR_SHAPE: return "map sizes out of range or inconsistent";
-        case MR_ERR_DTYPE: return "unsupported or mismatched dtype";
-        case MR_ERR_PARAM: return "invalid parameter";
-        case MR_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
-        case MR_ERR_CAPACITY: return "output capacity below the bound";
-        case MR_ERR_DEVICE: return "HIP call failed";
-        default: return "unknown status";
-    }
-}
-
-int64_t mr_seed_count(int32_t h, int32_t w, int32_t stride, int32_t offset) {
-    return seed_count(h, w, stride, offset);
-}
-
-size_t mr_workspace_bytes(int op, const mr_map* a, const mr_map* b, int64_t n_q, int32_t stride,
-                          int32_t offset) {
-    if (validate_pair(a, b) != MR_OK) return 0;
-    switch (op) {
-        case MR_OP_NN_ARGMAX:
-            if (n_q < 0) return 0;
-            return nn_layout(a, b, n_q).total;
-        case MR_OP_MUTUAL_NN:
-            return mutual_layout(a, b).total;
-        case MR_OP_FAST_RECIPROCAL: {
-            const int64_t ns = seed_count(a->h, a->w, stride, offset);
-            if (ns < 0) return 0;
-            return fast_layout(a, b, ns).total;
-        }
-        default: return 0;
-    }
-}
-
-int mr_nn_argmax(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q, int32_t* out_idx,
-                 float* out_score, void* ws, size_t ws_bytes, void* stream) {
-    int rc = validate_pair(q, db);
+// The three calls, for either metric (the extern "C" entry points below name one).
+int nn_impl(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q, int32_t* out_idx,
+            float* out_score, void* ws, size_t ws_bytes, void* stream, int metric) {
+    int rc = validate_for(q, db, metric);
     if (rc) return rc;
     if (n_q < 0 || n_q > (int64_t(1) << 28)) return MR_ERR_PARAM;
     if (!q_idx && n_q != npix(q)) return MR_ERR_PARAM;
@@ -1463,14 +1610,15 @@ int mr_nn_argmax(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_
     a.host_count = (int32_t)n_q;
     a.keys = keys;
     a.keys_stride = n_q;
-    if ((rc = launch_nn(a, choose_arith(q->dtype, q->d), q->batch, st))) return rc;
-    hipLaunchKernelGGL(decode_keys_kernel, dim3(grid_1d(tot)), dim3(256), 0, st, keys, tot, out_idx, out_score);
+    if ((rc = launch_search(a, metric, choose_arith(q->dtype, q->d), q->batch, st))) return rc;
+    hipLaunchKernelGGL(decode_keys_kernel, dim3(grid_1d(tot)), dim3(256), 0, st, keys, tot, out_idx, out_score,
+                       (int)(metric == M_POINT));
     return dev_err();
 }
 
-int mr_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba, int32_t* pairs, int64_t cap,
-                 int64_t* n_pairs, void* ws, size_t ws_bytes, void* stream) {
-    int rc = validate_pair(a, b);
+int mutual_impl(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba, int32_t* pairs, int64_t cap,
+                int64_t* n_pairs, void* ws, size_t ws_bytes, void* stream, int metric) {
+    int rc = validate_for(a, b, metric);
     if (rc) return rc;
     if (!nn_ab || !nn_ba || !pairs || !n_pairs) return MR_ERR_NULL;
     const int64_t na = npix(a), nb = npix(b);
@@ -1493,17 +1641,17 @@ int mr_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_b
     f.host_count = (int32_t)na;
     f.keys = kab;
     f.keys_stride = na;
-    if ((rc = launch_nn(f, ar, batch, st))) return rc;
+    if ((rc = launch_search(f, metric, ar, batch, st))) return rc;
     NNArgs r = nn_args(b, bd, 2, a, ad, 1);
     r.qsrc = Q_ALL;
     r.host_count = (int32_t)nb;
     r.keys = kba;
     r.keys_stride = nb;
-    if ((rc = launch_nn(r, ar, batch, st))) return rc;
+    if ((rc = launch_search(r, metric, ar, batch, st))) return rc;
     hipLaunchKernelGGL(decode_keys_kernel, dim3(grid_1d(batch * na)), dim3(256), 0, st, kab, batch * na, nn_ab,
-                       (float*)nullptr);
+                       (float*)nullptr, 0);
     hipLaunchKernelGGL(decode_keys_kernel, dim3(grid_1d(batch * nb)), dim3(256), 0, st, kba, batch * nb, nn_ba,
-                       (float*)nullptr);
+                       (float*)nullptr, 0);
     if (dev_err()) return MR_ERR_DEVICE;
     const int nblk = nblk_of(na) > 0 ? nblk_of(na) : 1;
     MutualPred pr{nn_ab, nn_ba, na, nb};
@@ -1513,10 +1661,10 @@ int mr_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_b
     return dev_err();
 }
 
-int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, int32_t max_iters,
-                       int32_t* pairs, int64_t cap, int64_t* n_pairs, int32_t* iter_active, void* ws,
-                       size_t ws_bytes, void* stream) {
-    int rc = validate_pair(a, b);
+int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, int32_t max_iters, int32_t* pairs,
+              int64_t cap, int64_t* n_pairs, int32_t* iter_active, void* ws, size_t ws_bytes, void* stream,
+              int metric) {
+    int rc = validate_for(a, b, metric);
     if (rc) return rc;
     if (stride < 1 || offset < 0 || max_iters < 0) return MR_ERR_PARAM;
     if (!pairs || !n_pairs) return MR_ERR_NULL;
@@ -1557,12 +1705,12 @@ int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t
             f.keys = kf[c]; f.keys_stride = slot;
             if (iter_active) { f.active_out = iter_active + t; f.active_stride = max_iters; }
             f.zero_count = cnt[x]; f.zero_stride = 1;
-            if ((rc = launch_nn(f, ar, batch, st))) return rc;
+            if ((rc = launch_search(f, metric, ar, batch, st))) return rc;
             NNArgs r = nn_args(b, bd, 2, a, ad, 1);
             r.qsrc = Q_KEYS; r.qlist = kf[c]; r.qlist_stride = slot;
             r.dev_count = cnt[c]; r.count_stride = 1;
             r.keys = kb[c]; r.keys_stride = slot;
-            if ((rc = launch_nn(r, ar, batch, st))) return rc;
+            if ((rc = launch_search(r, metric, ar, batch, st))) return rc;
             CycleArgs ca;
             ca.front = fr[c]; ca.keys_f = kf[c]; ca.keys_b = kb[c];
             ca.keys_f_next = kf[x]; ca.keys_b_next = kb[x]; ca.front_next = fr[x];
@@ -1583,6 +1731,84 @@ int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t
     hipLaunchKernelGGL(compact_scatter_kernel<FastPred>, dim3(nblk, batch), dim3(256), 0, st, pr, n1,
                        (const int32_t*)blk, nblk, pairs, cap, n_pairs);
     return dev_err();
+}
+
+}  // namespace
+
+// ============================================================================ C ABI
+
+extern "C" {
+
+const char* mr_status_str(int status) {
+    switch (status) {
+        case MR_OK: return "ok";
+        case MR_ERR_NULL: return "a required pointer is NULL";
+        case MR_ERR_SHAPE: return "map sizes out of range or inconsistent";
+        case MR_ERR_DTYPE: return "unsupported or mismatched dtype";
+        case MR_ERR_PARAM: return "invalid parameter";
+        case MR_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case MR_ERR_CAPACITY: return "output capacity below the bound";
+        case MR_ERR_DEVICE: return "HIP call failed";
+        default: return "unknown status";
+    }
+}
+
+int64_t mr_seed_count(int32_t h, int32_t w, int32_t stride, int32_t offset) {
+    return seed_count(h, w, stride, offset);
+}
+
+size_t mr_workspace_bytes(int op, const mr_map* a, const mr_map* b, int64_t n_q, int32_t stride,
+                          int32_t offset) {
+    const bool point = op == MR_OP_POINT_NN || op == MR_OP_POINT_MUTUAL_NN || op == MR_OP_POINT_FAST_RECIPROCAL;
+    if (validate_for(a, b, point ? M_POINT : M_INNER) != MR_OK) return 0;
+    switch (op) {
+        case MR_OP_NN_ARGMAX:
+        case MR_OP_POINT_NN:
+            if (n_q < 0) return 0;
+            return nn_layout(a, b, n_q).total;
+        case MR_OP_MUTUAL_NN:
+        case MR_OP_POINT_MUTUAL_NN:
+            return mutual_layout(a, b).total;
+        case MR_OP_FAST_RECIPROCAL:
+        case MR_OP_POINT_FAST_RECIPROCAL: {
+            const int64_t ns = seed_count(a->h, a->w, stride, offset);
+            if (ns < 0) return 0;
+            return fast_layout(a, b, ns).total;
+        }
+        default: return 0;
+    }
+}
+
+int mr_nn_argmax(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q, int32_t* out_idx,
+                 float* out_score, void* ws, size_t ws_bytes, void* stream) {
+    return nn_impl(q, db, q_idx, n_q, out_idx, out_score, ws, ws_bytes, stream, M_INNER);
+}
+
+int mr_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba, int32_t* pairs, int64_t cap,
+                 int64_t* n_pairs, void* ws, size_t ws_bytes, void* stream) {
+    return mutual_impl(a, b, nn_ab, nn_ba, pairs, cap, n_pairs, ws, ws_bytes, stream, M_INNER);
+}
+
+int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, int32_t max_iters,
+                       int32_t* pairs, int64_t cap, int64_t* n_pairs, int32_t* iter_active, void* ws,
+                       size_t ws_bytes, void* stream) {
+    return fast_impl(a, b, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, ws_bytes, stream, M_INNER);
+}
+
+int mr_point_nn(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q, int32_t* out_idx,
+                float* out_dist2, void* ws, size_t ws_bytes, void* stream) {
+    return nn_impl(q, db, q_idx, n_q, out_idx, out_dist2, ws, ws_bytes, stream, M_POINT);
+}
+
+int mr_point_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba, int32_t* pairs,
+                       int64_t cap, int64_t* n_pairs, void* ws, size_t ws_bytes, void* stream) {
+    return mutual_impl(a, b, nn_ab, nn_ba, pairs, cap, n_pairs, ws, ws_bytes, stream, M_POINT);
+}
+
+int mr_point_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, int32_t max_iters,
+                             int32_t* pairs, int64_t cap, int64_t* n_pairs, int32_t* iter_active, void* ws,
+                             size_t ws_bytes, void* stream) {
+    return fast_impl(a, b, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, ws_bytes, stream, M_POINT);
 }
 
 int mr_profile_begin(int32_t max_launches) {

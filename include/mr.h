@@ -74,7 +74,10 @@ typedef struct {
     int32_t dtype;    /* mr_dtype */
 } mr_map;
 
-enum { MR_OP_NN_ARGMAX = 0, MR_OP_MUTUAL_NN = 1, MR_OP_FAST_RECIPROCAL = 2 };
+enum {
+    MR_OP_NN_ARGMAX = 0, MR_OP_MUTUAL_NN = 1, MR_OP_FAST_RECIPROCAL = 2,
+    MR_OP_POINT_NN = 3, MR_OP_POINT_MUTUAL_NN = 4, MR_OP_POINT_FAST_RECIPROCAL = 5
+};
 
 /* Workspace bytes that entry point `op` needs for these maps and parameters
  * (n_q: queries per pair for MR_OP_NN_ARGMAX; stride/offset for
@@ -138,6 +141,35 @@ int mr_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_b
 int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset,
                        int32_t max_iters, int32_t* pairs, int64_t cap, int64_t* n_pairs,
                        int32_t* iter_active, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Pointmaps.  A pointmap holds, for every pixel, the 3D point that pixel
+ * observes; both maps of a pair are expressed in the first camera's frame, and
+ * two pixels correspond when their points are nearest neighbours in that shared
+ * space ("DUSt3R and MASt3R explained", the paragraph on recovering the
+ * cameras).  Nearest = smallest squared Euclidean distance, computed in fp32 as
+ * t0*t0 + t1*t1 + ... with t_c = x_c - y_c, in ascending c, each step rounded
+ * once (a fused multiply-add after the first product); equal fp32 distances go
+ * to the lowest row.  Against binary64 the distance errs by at most about
+ * 2^-21 of itself.
+ * The three calls mirror the descriptor calls above -- same arguments, workspace
+ * (from mr_workspace_bytes with the MR_OP_POINT_* codes), outputs, ordering and
+ * error behaviour -- with nearest-point search in place of the largest inner
+ * product.  Maps: dtype MR_F32 (else MR_ERR_DTYPE), 1 <= d <= 4 (else
+ * MR_ERR_SHAPE); d = 3 for pointmaps.  Finite coordinates of any scale.
+ *   mr_point_nn       : out_dist2 NULL or [batch][n_q] fp32 squared distance
+ *                       of the chosen row (+INF when db has no rows).
+ *   mr_point_mutual_nn: reciprocal nearest points, as mr_mutual_nn.
+ *   mr_point_fast_reciprocal: the fast scheme of mr_fast_reciprocal with
+ *                       nearest points.
+ * --------------------------------------------------------------------------- */
+int mr_point_nn(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q, int32_t* out_idx,
+                float* out_dist2, void* ws, size_t ws_bytes, void* stream);
+int mr_point_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba, int32_t* pairs,
+                       int64_t cap, int64_t* n_pairs, void* ws, size_t ws_bytes, void* stream);
+int mr_point_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset,
+                             int32_t max_iters, int32_t* pairs, int64_t cap, int64_t* n_pairs,
+                             int32_t* iter_active, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Measurement aid (not thread-safe; one profiling window per process).

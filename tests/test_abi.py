@@ -145,3 +145,28 @@ def test_profile_end_without_begin(lib):
     ms = ctypes.c_double()
     n = ctypes.c_int64()
     assert lib.mr_profile_end(ctypes.byref(ms), ctypes.byref(n)) == PARAM
+
+
+def test_point_validation(lib):
+    """Pointmaps are fp32 with at most 4 coordinates; their workspace op codes size like
+    the descriptor ones."""
+    out = ctypes.c_void_p(FAKE)
+    a, b = M(10, 10, d=3), M(7, 9, d=3)
+    for op, ref in ((3, 0), (4, 1), (5, 2)):
+        need = lib.mr_workspace_bytes(op, R(a), R(b), 100, 8, 4)
+        assert need > 0 and need == lib.mr_workspace_bytes(ref, R(a), R(b), 100, 8, 4)
+        assert lib.mr_workspace_bytes(op, R(M(10, 10, d=8, dtype=1)), R(M(7, 9, d=8, dtype=1)), 100, 8, 4) == 0
+        assert lib.mr_workspace_bytes(op, R(M(10, 10, d=5)), R(M(7, 9, d=5)), 100, 8, 4) == 0
+    ws = ctypes.c_void_p(FAKE)
+    bf = M(10, 10, d=8, dtype=1)
+    assert lib.mr_point_nn(R(bf), R(bf), None, 100, out, None, ws, 1 << 30, None) == DTYPE
+    assert lib.mr_point_mutual_nn(R(bf), R(bf), out, out, out, 1 << 20, out, ws, 1 << 30, None) == DTYPE
+    assert lib.mr_point_fast_reciprocal(R(bf), R(bf), 8, 4, 10, out, 1 << 20, out, None, ws, 1 << 30,
+                                        None) == DTYPE
+    d5 = M(10, 10, d=5)
+    assert lib.mr_point_nn(R(d5), R(d5), None, 100, out, None, ws, 1 << 30, None) == SHAPE
+    assert lib.mr_seed_count(10, 10, 8, 4) == 1
+    assert lib.mr_point_fast_reciprocal(R(a), R(b), 8, 4, 10, out, 0, out, None, ws, 1 << 30, None) == CAP
+    need = lib.mr_workspace_bytes(3, R(a), R(b), 100, 1, 0)
+    assert lib.mr_point_nn(R(a), R(b), None, 100, out, None, out, need - 8, None) == WS
+

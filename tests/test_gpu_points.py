@@ -1,0 +1,165 @@
+"""GPU parity of the pointmap calls (nearest 3D points) against the CPU oracle.
+
+A pointmap holds one 3D point per pixel, both maps in the first camera's frame;
+two pixels correspond when their points are nearest neighbours ("DUSt3R and
+MASt3R explained", the paragraph on recovering the cameras).  The rules are those
+of tests/checks.py with the pointmap metric: the index is exact wherever the
+oracle's relative margin exceeds 1e-6; elsewhere the chosen point is within 1e-6
+(relative) of the nearest.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import checks
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import dense_grounded_image_amd as mr  # noqa: E402
+
+DEV = torch.device("cuda:0")
+PT = checks.POINT
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def dev(arr, H, W):
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32).reshape(H, W, -1)).to(DEV)
+
+
+def check_dist2(gd, A, B, rows, gi):
+    """The reported squared distance is the GPU's fp32 value for its own choice."""
+    s = -oracle.similarity_pairs(A, B, rows, gi, metric=PT)
+    gd = gd.astype(np.float64)
+    assert (np.abs(gd - s) <= 1e-6 * s + 1e-30).all()
+
+
+@pytest.mark.parametrize("d", [1, 2, 3, 4])
+def test_point_nn_ragged(d):
+    """All queries, 37x29 points against 41x23 (no multiple of the 16-point group)."""
+    rng = np.random.default_rng(700 + d)
+    A = rng.uniform(-3, 3, size=(37 * 29, d)).astype(np.float32)
+    B = rng.uniform(-3, 3, size=(41 * 23, d)).astype(np.float32)
+    gi, gd = mr.point_nn(dev(A, 37, 29), dev(B, 41, 23), with_dist2=True)
+    torch.cuda.synchronize()
+    gi, gd = gi.cpu().numpy(), gd.cpu().numpy()
+    oi, o1, o2 = oracle.nn(A, B, metric=PT)
+    rep = checks.check_nn(gi, oi, o1, o2, A, np.arange(len(A)), B, "f32", metric=PT)
+    check_dist2(gd, A, B, np.arange(len(A)), gi)
+    log("point nn", d, rep)
+
+
+def test_point_nn_far_from_origin():
+    """Pointmaps shifted a kilometre away: the distance is computed from coordinate
+    differences, so precision follows the points' spacing, not their distance from 0."""
+    p = workloads.make_pointmaps(40, 30, seed=701, warp="affine", sigma=0.005, rho=0.2)
+    sh = np.array([1000.0, -500.0, 2000.0])
+    A = (p.D1.astype(np.float64) + sh).astype(np.float32)
+    B = (p.D2.astype(np.float64) + sh).astype(np.float32)
+    gi = mr.point_nn(dev(A, p.H, p.W), dev(B, p.H, p.W)).cpu().numpy()
+    oi, o1, o2 = oracle.nn(A, B, metric=PT)
+    rep = checks.check_nn(gi, oi, o1, o2, A, np.arange(p.N), B, "f32", metric=PT)
+    assert rep["exact"] > 0.9 * p.N
+    log("point far", rep)
+
+
+def test_point_nn_query_list_batch():
+    """Batched pointmaps, explicit query lists with repeats and out-of-order ids."""
+    B_, H, W = 3, 19, 21
+    ps = [workloads.make_pointmaps(H, W, seed=710 + b, warp="shift", sigma=0.01, rho=0.2) for b in range(B_)]
+    A = torch.stack([dev(p.D1, H, W) for p in ps])
+    Bm = torch.stack([dev(p.D2, H, W) for p in ps])
+    rng = np.random.default_rng(711)
+    rows = rng.integers(0, H * W, size=(B_, 150)).astype(np.int32)
+    rows[:, 5] = rows[:, 6]
+    gi = mr.point_nn(A, Bm, q_idx=torch.from_numpy(rows)).cpu().numpy()
+    for b, p in enumerate(ps):
+        oi, o1, o2 = oracle.nn_rows(p.D1, rows[b], p.D2, metric=PT)
+        checks.check_nn(gi[b], oi, o1, o2, p.D1, rows[b], p.D2, "f32", metric=PT)
+
+
+@pytest.mark.parametrize("H,W", [(64, 48), (37, 29)])
+def test_point_mutual_full(H, W):
+    p = workloads.make_pointmaps(H, W, seed=720 + H, warp="affine", sigma=0.005, rho=0.3)
+    pairs, n, nn_ab, nn_ba = mr.point_mutual_nn(dev(p.D1, H, W), dev(p.D2, H, W))
+    torch.cuda.synchronize()
+    o_pairs, o12, a1, a2, o21, b1, b2 = oracle.mutual_nn(p.D1, p.D2, metric=PT)
+    g12, g21 = nn_ab[0].cpu().numpy(), nn_ba[0].cpu().numpy()
+    checks.check_nn(g12, o12, a1, a2, p.D1, np.arange(p.N), p.D2, "f32", metric=PT)
+    checks.check_nn(g21, o21, b1, b2, p.D2, np.arange(p.N), p.D1, "f32", metric=PT)
+    gp = mr.matches(pairs, n)
+    checks.check_one_to_one_sorted(gp)
+    i = np.nonzero(g21[g12] == np.arange(p.N))[0]
+    assert (gp[:, 0] == i).all() and (gp[:, 1] == g12[i]).all()
+    clean = (checks.margin_of(a1, a2, PT) > checks.MARGIN_PT) & (checks.margin_of(b1, b2, PT)[o12] > checks.MARGIN_PT)
+    if clean.all():
+        assert gp.tolist() == o_pairs.tolist()
+    log("point mutual", H, W, len(gp), len(o_pairs))
+
+
+@pytest.mark.parametrize("H,W", [(40, 35), (64, 64)])
+def test_point_planted_noise_free_ties(H, W):
+    """Noise-free planted pointmaps: clamped borders plant exact duplicates (distance 0),
+    so the lowest-index rule decides; the mutual set is the closed form, and so is the
+    fast scheme's output at stride 1."""
+    p = workloads.make_pointmaps(H, W, seed=730, warp="shift", sigma=0.0, rho=0.0)
+    first = {}
+    for q, s in enumerate(p.src.tolist()):
+        first.setdefault(s, q)
+    want = [list(x) for x in sorted(first.items())]
+    A, B = dev(p.D1, H, W), dev(p.D2, H, W)
+    pairs, n, _, _ = mr.point_mutual_nn(A, B)
+    assert mr.matches(pairs, n).tolist() == want
+    fp, fn, _ = mr.point_fast_reciprocal(A, B, 1, 0, 2)
+    assert mr.matches(fp, fn).tolist() == want
+
+
+@pytest.mark.parametrize("H,W,stride,offset,T", [(64, 48, 8, 4, 10), (96, 72, 4, 1, 5), (33, 50, 3, 0, 7)])
+def test_point_fast_full(H, W, stride, offset, T):
+    p = workloads.make_pointmaps(H, W, seed=740 + H, warp="affine", sigma=0.005, rho=0.3)
+    gp, gn, act = mr.point_fast_reciprocal(dev(p.D1, H, W), dev(p.D2, H, W), stride, offset, T)
+    torch.cuda.synchronize()
+    orc = oracle.fast(p.D1, H, W, p.D2, stride, offset, T, eps=checks.MARGIN_PT, metric=PT)
+    rep = checks.check_fast(mr.matches(gp, gn), orc, p.D1, p.D2, "f32", metric=PT)
+    # the library drops chains that land on a pixel visited in an earlier iteration (its
+    # future is already followed); the oracle keeps walking them, so it counts at least as many
+    assert (act[0].cpu().numpy()[:T] <= orc["active"][:T]).all()
+    log("point fast", H, W, rep)
+
+
+def test_point_fast_stride1_equals_gpu_mutual():
+    """Stride 1 seeds every pixel: the fast scheme returns the GPU's own mutual set."""
+    p = workloads.make_pointmaps(40, 30, seed=750, warp="affine", sigma=0.01, rho=0.3)
+    A, B = dev(p.D1, p.H, p.W), dev(p.D2, p.H, p.W)
+    mp, mn, _, _ = mr.point_mutual_nn(A, B)
+    fp, fn, _ = mr.point_fast_reciprocal(A, B, 1, 0, 3)
+    assert mr.matches(fp, fn).tolist() == mr.matches(mp, mn).tolist()
+
+
+def test_point_fast_full_size():
+    """512x384 pointmaps, stride 8 (3072 seeds), 10 iterations, against a full oracle run."""
+    p = workloads.make_pointmaps(512, 384, seed=11)
+    gp, gn, act = mr.point_fast_reciprocal(dev(p.D1, p.H, p.W), dev(p.D2, p.H, p.W), 8, 4, 10)
+    torch.cuda.synchronize()
+    orc = oracle.fast(p.D1, p.H, p.W, p.D2, 8, 4, 10, eps=checks.MARGIN_PT, metric=PT)
+    rep = checks.check_fast(mr.matches(gp, gn), orc, p.D1, p.D2, "f32", metric=PT)
+    log("point fast 512x384", rep, act[0].cpu().tolist())
+
+
+def test_point_edges():
+    """T = 0 gives nothing; a 1x1 image; a stride beyond the image leaves one seed."""
+    p = workloads.make_pointmaps(12, 9, seed=760, warp="shift", sigma=0.01, rho=0.2)
+    A, B = dev(p.D1, p.H, p.W), dev(p.D2, p.H, p.W)
+    fp, fn, act = mr.point_fast_reciprocal(A, B, 3, 1, 0)
+    assert int(fn[0]) == 0
+    one = dev(p.D1[:1], 1, 1)
+    fp, fn, _ = mr.point_fast_reciprocal(one, B, 8, 0, 4)
+    orc = oracle.fast(p.D1[:1], 1, 1, p.D2, 8, 0, 4, metric=PT)
+    assert mr.matches(fp, fn).tolist() == orc["pairs"].tolist()
+    fp, fn, _ = mr.point_fast_reciprocal(A, B, 100, 2, 3)
+    orc = oracle.fast(p.D1, p.H, p.W, p.D2, 100, 2, 3, metric=PT)
+    assert mr.matches(fp, fn).tolist() == orc["pairs"].tolist()
