@@ -22,6 +22,15 @@ sys.path.insert(0, ROOT)
 
 METRIC = "image pairs/sec fast reciprocal NN @512×384 d=24; NN-queries/sec; %MFMA peak"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense matrix-core peaks
+# fp32 VALU lane-operations per second: the published fp32 vector peak, 157.3 TFLOP/s,
+# is 78.6 T fused multiply-adds per second (32 fp32 lanes per SIMD per clock, 256 CUs x
+# 4 SIMDs x 2.4 GHz, twice the fp64 rate); a plain fp32 VALU operation (subtract,
+# multiply, minimum) counts as one lane-operation like an FMA.
+PEAK_VALU_TOPS = 157.3 / 2
+# Algorithmic VALU work of one (query, point) pair of 3D pointmaps: 3 subtractions, a
+# multiply and 2 fused multiply-adds for the squared distance, and half of a 3-input
+# minimum for the selection.
+POINT_OPS_PER_PAIR = 6.5
 
 
 def parse():
@@ -95,13 +104,13 @@ def fast_work(active, N, d):
     return q, 2.0 * N * d * q
 
 
-def run_fast(p, batch_pairs, args, torch, dev, prof=True):
+def run_fast(p, batch_pairs, args, torch, dev, prof=True, point=False):
     import dense_grounded_image_amd as mr
     if batch_pairs is None:
         A, B = dev_maps(p, torch, dev)
     else:
         A, B = batch_pairs
-    f = mr.FastReciprocal(A, B, p.stride, p.offset, p.max_iters)
+    f = mr.FastReciprocal(A, B, p.stride, p.offset, p.max_iters, point=point)
     launches = 2 * p.max_iters * args.steps
     ms, kms, kn = time_steps(lambda: f(A, B), args.steps, args.warmup, torch, launches if prof else 0)
     pairs, n_pairs, active = f(A, B)
@@ -148,6 +157,20 @@ def roofline(flops_per_step, steps, kernel_ms, launches, dtype, traffic=None):
                            "achieved_bf16_TFLOPs": round(6 * achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                            "frac": round(6 * achieved / PEAK_TFLOPS["bf16"], 4)}
     return out
+
+
+def roofline_alu(pairs_per_step, steps, kernel_ms, launches):
+    """VALU-bound kernels (pointmaps): algorithmic lane-operations per launch over its
+    average launch time, against the chip's VALU lane-operation rate."""
+    if not launches:
+        return None
+    per_launch = pairs_per_step * POINT_OPS_PER_PAIR * steps / launches
+    avg_ms = kernel_ms / launches
+    achieved = per_launch / (avg_ms * 1e-3) / 1e12
+    return {"bound": "alu", "achieved": round(achieved, 3), "peak": round(PEAK_VALU_TOPS, 2),
+            "unit": "T VALU lane-ops/s", "frac": round(achieved / PEAK_VALU_TOPS, 4), "traffic": None,
+            "kernel": "point_nn_kernel", "avg_launch_us": round(avg_ms * 1e3, 2),
+            "ops_per_launch": per_launch, "ops_per_pair": POINT_OPS_PER_PAIR}
 
 
 def cpu_baseline(p):
@@ -213,7 +236,40 @@ def other_bruteforce(args, torch, dev):
             "roofline": roofline(fl, steps, kms, kn, "bf16")}
 
 
+def point_maps(p, torch, dev):
+    A = torch.from_numpy(p.D1.reshape(p.H, p.W, 3)).to(dev).unsqueeze(0)
+    B = torch.from_numpy(p.D2.reshape(p.H, p.W, 3)).to(dev).unsqueeze(0)
+    return A, B
+
+
+def other_points_fast(args, torch, dev):
+    """Fast reciprocal matching of one 512x384 pointmap pair (nearest 3D points)."""
+    import workloads
+    p = workloads.make_pointmaps(512, 384, seed=11)
+    r = run_fast(p, point_maps(p, torch, dev), args, torch, dev, point=True)
+    pairs_per_step = r["nn_queries"] * p.N            # each query against every point
+    return {"pairs_per_s": round(1000.0 / r["ms"], 2), "ms_per_call": round(r["ms"], 3),
+            "nn_queries_per_s": round(r["nn_queries"] * 1000.0 / r["ms"], 1),
+            "iter_active": r["active"], "matches": r["matches"][0],
+            "roofline": roofline_alu(pairs_per_step, args.steps, r["kernel_ms"], r["launches"])}
+
+
+def other_points_bruteforce(args, torch, dev):
+    """Brute-force reciprocal nearest points of one 512x384 pointmap pair."""
+    import dense_grounded_image_amd as mr
+    import workloads
+    p = workloads.make_pointmaps(512, 384, seed=11)
+    A, B = point_maps(p, torch, dev)
+    ws = torch.empty(mr.workspace_bytes(mr.MR_OP_POINT_MUTUAL_NN, A, B), dtype=torch.uint8, device=dev)
+    steps = max(3, args.steps // 4)
+    ms, kms, kn = time_steps(lambda: mr.point_mutual_nn(A, B, ws=ws), steps, 2, torch, 2 * steps)
+    return {"pairs_per_s": round(1000.0 / ms, 2), "ms_per_call": round(ms, 3),
+            "nn_queries_per_s": round(2 * p.N * 1000.0 / ms, 1),
+            "roofline": roofline_alu(2.0 * p.N * p.N, steps, kms, kn)}
+
+
 OTHER = {"batch64-512x384-f32": other_batch64, "pair-1024x768-bf16": other_bf16_1024,
+         "pointmaps-512x384-f32": other_points_fast, "pointmaps-512x384-f32-bruteforce": other_points_bruteforce,
          "pair-512x384-bf16-bruteforce": other_bruteforce}
 
 
