@@ -1,6 +1,7 @@
 // mr.hip -- dense NN search and reciprocal matching for MI355X (gfx950, CDNA4).
 //
-// One similarity/argmax kernel serves every entry point: a block of queries
+// One similarity/argmax kernel serves every descriptor entry point (pointmaps have
+// their own VALU kernel, point_nn_kernel, further down): a block of queries
 // (gathered rows of one map, held in registers as the MFMA B operand) against
 // a contiguous range of rows of the other map (streamed as the MFMA A
 // operand), d-component contraction on the matrix cores, a running per-lane

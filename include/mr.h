@@ -1,6 +1,7 @@
 /*
  * mr.h -- dense nearest-neighbour search and reciprocal matching between two
- * per-pixel descriptor maps, on AMD Instinct MI355X (gfx950).
+ * per-pixel descriptor maps (or two pointmaps, see the mr_point_* calls), on AMD
+ * Instinct MI355X (gfx950).
  *
  * What is computed (the pages are cited by title and section):
  *  - Similarity of two descriptors is their inner product; the maps hold one
