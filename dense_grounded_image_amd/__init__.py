@@ -22,11 +22,13 @@ LIB_PATH = os.path.join(_HERE, "libmr.so")
 MR_F32, MR_BF16 = 0, 1
 MR_OP_NN_ARGMAX, MR_OP_MUTUAL_NN, MR_OP_FAST_RECIPROCAL = 0, 1, 2
 MR_OP_POINT_NN, MR_OP_POINT_MUTUAL_NN, MR_OP_POINT_FAST_RECIPROCAL = 3, 4, 5
+MR_OP_FAST_RECIPROCAL_GRAPH = 6
 STATUS = {0: "MR_OK", 1: "MR_ERR_NULL", 2: "MR_ERR_SHAPE", 3: "MR_ERR_DTYPE", 4: "MR_ERR_PARAM",
           5: "MR_ERR_WORKSPACE", 6: "MR_ERR_CAPACITY", 7: "MR_ERR_DEVICE"}
 
 EXPORTS = ("mr_workspace_bytes", "mr_status_str", "mr_seed_count", "mr_nn_argmax", "mr_mutual_nn",
-           "mr_fast_reciprocal", "mr_point_nn", "mr_point_mutual_nn", "mr_point_fast_reciprocal",
+           "mr_fast_reciprocal", "mr_fast_reciprocal_graph", "mr_point_nn", "mr_point_mutual_nn",
+           "mr_point_fast_reciprocal",
            "mr_profile_begin", "mr_profile_end")
 
 
@@ -66,6 +68,8 @@ def load_library(path: str = LIB_PATH):
     lib.mr_mutual_nn.restype = ctypes.c_int
     lib.mr_fast_reciprocal.argtypes = [MP, MP, i32, i32, i32, P, i64, P, P, P, sz, P]
     lib.mr_fast_reciprocal.restype = ctypes.c_int
+    lib.mr_fast_reciprocal_graph.argtypes = [MP, P, i32, i32, i32, i32, P, i64, P, P, P, sz, P]
+    lib.mr_fast_reciprocal_graph.restype = ctypes.c_int
     lib.mr_point_nn.argtypes = lib.mr_nn_argmax.argtypes
     lib.mr_point_nn.restype = ctypes.c_int
     lib.mr_point_mutual_nn.argtypes = lib.mr_mutual_nn.argtypes
@@ -256,6 +260,50 @@ def fast_reciprocal(a, b, stride: int = 8, offset: Optional[int] = None, max_ite
     """Fast reciprocal matching seeded on a's grid.  Returns (pairs int32 [B, cap, 2],
     n_pairs int64 [B], iter_active int32 [B, max_iters]); pairs ascending in the a-pixel."""
     return FastReciprocal(_batched(a), _batched(b), stride, offset, max_iters)(_batched(a), _batched(b))
+
+
+class FastReciprocalGraph:
+    """Reusable fast reciprocal matching over the edges of a pair graph on one image
+    collection (images [n, H, W, d]; edges: host int array [E, 2] of image ids)."""
+
+    def __init__(self, images, edges, stride: int = 8, offset: Optional[int] = None, max_iters: int = 10):
+        import numpy as np
+        torch = _torch()
+        self.lib = load_library()
+        self.stride = int(stride)
+        self.offset = int(stride // 2 if offset is None else offset)
+        self.max_iters = int(max_iters)
+        self.edges = np.ascontiguousarray(np.asarray(edges, dtype=np.int32).reshape(-1, 2))
+        E = self.edges.shape[0]
+        m = _as_map(images)
+        self.cap = max(1, seed_count(m.h, m.w, self.stride, self.offset))
+        dev = images.device
+        self.pairs = torch.empty((E, self.cap, 2), dtype=torch.int32, device=dev)
+        self.n_pairs = torch.empty((E,), dtype=torch.int64, device=dev)
+        self.active = torch.empty((E, max(1, self.max_iters)), dtype=torch.int32, device=dev)
+        need = self.lib.mr_workspace_bytes(MR_OP_FAST_RECIPROCAL_GRAPH, ctypes.byref(m), ctypes.byref(m), E,
+                                           self.stride, self.offset)
+        if need == 0:
+            raise MrError("mr_workspace_bytes", 4)
+        self.ws = _workspace(need, dev)
+        self.shape = (tuple(images.shape), images.dtype)
+
+    def __call__(self, images):
+        if (tuple(images.shape), images.dtype) != self.shape:
+            raise ValueError("shapes differ from the ones this FastReciprocalGraph was built for")
+        m = _as_map(images)
+        rc = self.lib.mr_fast_reciprocal_graph(
+            ctypes.byref(m), self.edges.ctypes.data_as(ctypes.c_void_p), self.edges.shape[0], self.stride,
+            self.offset, self.max_iters, self.pairs.data_ptr(), self.cap, self.n_pairs.data_ptr(),
+            self.active.data_ptr(), self.ws.data_ptr(), self.ws.numel(), _stream(images))
+        _check("mr_fast_reciprocal_graph", rc)
+        return self.pairs, self.n_pairs, self.active
+
+
+def fast_reciprocal_graph(images, edges, stride: int = 8, offset: Optional[int] = None, max_iters: int = 10):
+    """Fast reciprocal matching on every edge (i, j) of a pair graph over images [n, H, W, d];
+    returns (pairs [E, cap, 2], n_pairs [E], iter_active [E, max_iters]) like fast_reciprocal."""
+    return FastReciprocalGraph(images, edges, stride, offset, max_iters)(images)
 
 
 def point_fast_reciprocal(a, b, stride: int = 8, offset: Optional[int] = None, max_iters: int = 10):

@@ -302,7 +302,16 @@ struct NNArgs {
     int32_t* zero_count;       // optional: set this per-pair counter to 0
     int64_t zero_stride;
     int32_t q_role, db_role;   // 1 = image 1, 2 = image 2 (fixes the split product order)
+    // pair graph: the query (database) map of pair b is map q_img[2b] (db_img[2b]) of
+    // qmap (dbmap); NULL: map b
+    const int32_t* q_img;
+    const int32_t* db_img;
 };
+
+// Map index of pair b in a stacked collection (a pair graph's edge table, or b itself).
+__device__ __forceinline__ int64_t map_of(const int32_t* img, int pair) {
+    return img ? (int64_t)img[2 * pair] : (int64_t)pair;
+}
 
 // Scores are compared after clearing their 4 lowest fp32 bits; that order, with
 // the lowest row winning ties, is the NN rule of every kernel (both directions use
@@ -365,8 +374,8 @@ __device__ __forceinline__ void tile_track(const f32x16& acc, int t, int h, int 
     bv = m;
 }
 
-template <int AR> __device__ __forceinline__ const void* pair_base(const void* p, int64_t elems, int pair) {
-    return static_cast<const typename ArithTraits<AR>::elem*>(p) + pair * elems * ArithTraits<AR>::row_mult;
+template <int AR> __device__ __forceinline__ const void* pair_base(const void* p, int64_t elems, int64_t map) {
+    return static_cast<const typename ArithTraits<AR>::elem*>(p) + map * elems * ArithTraits<AR>::row_mult;
 }
 
 // Bytes of one map row as the kernel reads it, and an upper bound for the template.
@@ -788,8 +797,8 @@ void nn_argmax_kernel(NNArgs a) {
     nsg = nsg < 1 ? 1 : (nsg > sg_cap ? sg_cap : nsg);
     if (nsg >= 8) nsg &= ~7;
     const int items = qgroups * nsg;
-    const void* qbase = pair_base<AR>(a.qmap, a.q_pair_elems, pair);
-    const char* dbytes = static_cast<const char*>(pair_base<AR>(a.dbmap, a.db_pair_elems, pair));
+    const void* qbase = pair_base<AR>(a.qmap, a.q_pair_elems, map_of(a.q_img, pair));
+    const char* dbytes = static_cast<const char*>(pair_base<AR>(a.dbmap, a.db_pair_elems, map_of(a.db_img, pair)));
     const int rb = row_bytes<AR>(a.d);
 
     // query tile j of a wave is tile (tb + j*ts) of the query list
@@ -969,8 +978,8 @@ __global__ __launch_bounds__(kThreads) void recover_rows_kernel(NNArgs a) {
     const int pair = blockIdx.y;
     const int n = a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count;
     const int nqt = (n + 31) >> 5;
-    const void* qbase = pair_base<AR>(a.qmap, a.q_pair_elems, pair);
-    const void* dbase = pair_base<AR>(a.dbmap, a.db_pair_elems, pair);
+    const void* qbase = pair_base<AR>(a.qmap, a.q_pair_elems, map_of(a.q_img, pair));
+    const void* dbase = pair_base<AR>(a.dbmap, a.db_pair_elems, map_of(a.db_img, pair));
     uint64_t* keys = a.keys + pair * a.keys_stride;
     for (int g = blockIdx.x; g < nqt; g += gridDim.x) {
         const int qp = g * 32 + jl;
@@ -1073,8 +1082,8 @@ __global__ __launch_bounds__(kThreads) void point_nn_kernel(NNArgs a) {
     int nseg = waves / nqb;
     nseg = nseg < 1 ? 1 : (nseg > seg_cap ? seg_cap : nseg);
     if (nseg >= 8) nseg &= ~7;
-    const float* qbase = static_cast<const float*>(a.qmap) + pair * a.q_pair_elems;
-    const float* dbase = static_cast<const float*>(a.dbmap) + pair * a.db_pair_elems;
+    const float* qbase = static_cast<const float*>(a.qmap) + map_of(a.q_img, pair) * a.q_pair_elems;
+    const float* dbase = static_cast<const float*>(a.dbmap) + map_of(a.db_img, pair) * a.db_pair_elems;
     uint64_t* keys = a.keys + pair * a.keys_stride;
 
     // consecutive workgroups take consecutive items, so item % 8 (the segment's XCD
@@ -1587,6 +1596,24 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
 
 template <class T> T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
+// A pair graph over a collection of maps: the collection with its batch replaced by
+// the number of edges (the per-edge state is laid out like a batch of pairs), and
+// the workspace bytes of the fast scheme over it plus the device copy of the edges.
+mr_map graph_map(const mr_map* images, int32_t n_edges) {
+    mr_map m = *images;
+    m.batch = n_edges;
+    return m;
+}
+
+size_t graph_edges_offset(const mr_map* g, int32_t stride, int32_t offset) {
+    return fast_layout(g, g, seed_count(g->h, g->w, stride, offset)).total;
+}
+
+size_t graph_ws_bytes(const mr_map* images, int32_t n_edges, int32_t stride, int32_t offset) {
+    const mr_map g = graph_map(images, n_edges);
+    return align256(graph_edges_offset(&g, stride, offset) + (size_t)n_edges * 2 * sizeof(int32_t));
+}
+
 // The three calls, for either metric (the extern "C" entry points below name one).
 int nn_impl(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q, int32_t* out_idx,
             float* out_score, void* ws, size_t ws_bytes, void* stream, int metric) {
@@ -1662,9 +1689,12 @@ int mutual_impl(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba
     return dev_err();
 }
 
+// edges: NULL, or the device edge table of a pair graph ([batch][2] map ids into a and
+// b, which then hold the whole collection at their base while their batch counts the
+// edges); the caller has validated it and its workspace region.
 int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, int32_t max_iters, int32_t* pairs,
               int64_t cap, int64_t* n_pairs, int32_t* iter_active, void* ws, size_t ws_bytes, void* stream,
-              int metric) {
+              int metric, const int32_t* edges = nullptr) {
     int rc = validate_for(a, b, metric);
     if (rc) return rc;
     if (stride < 1 || offset < 0 || max_iters < 0) return MR_ERR_PARAM;
@@ -1701,6 +1731,7 @@ int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, 
         for (int t = 0; t < max_iters; ++t) {
             const int c = t & 1, x = c ^ 1;
             NNArgs f = nn_args(a, ad, 1, b, bd, 2);
+            if (edges) { f.q_img = edges; f.db_img = edges + 1; }
             f.qsrc = Q_LIST; f.qlist = fr[c]; f.qlist_stride = slot;
             f.dev_count = cnt[c]; f.count_stride = 1;
             f.keys = kf[c]; f.keys_stride = slot;
@@ -1708,6 +1739,7 @@ int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, 
             f.zero_count = cnt[x]; f.zero_stride = 1;
             if ((rc = launch_search(f, metric, ar, batch, st))) return rc;
             NNArgs r = nn_args(b, bd, 2, a, ad, 1);
+            if (edges) { r.q_img = edges + 1; r.db_img = edges; }
             r.qsrc = Q_KEYS; r.qlist = kf[c]; r.qlist_stride = slot;
             r.dev_count = cnt[c]; r.count_stride = 1;
             r.keys = kb[c]; r.keys_stride = slot;
@@ -1770,6 +1802,9 @@ size_t mr_workspace_bytes(int op, const mr_map* a, const mr_map* b, int64_t n_q,
         case MR_OP_MUTUAL_NN:
         case MR_OP_POINT_MUTUAL_NN:
             return mutual_layout(a, b).total;
+        case MR_OP_FAST_RECIPROCAL_GRAPH:
+            if (n_q < 1 || n_q > 65535 || seed_count(a->h, a->w, stride, offset) < 0) return 0;
+            return graph_ws_bytes(a, (int32_t)n_q, stride, offset);
         case MR_OP_FAST_RECIPROCAL:
         case MR_OP_POINT_FAST_RECIPROCAL: {
             const int64_t ns = seed_count(a->h, a->w, stride, offset);
@@ -1810,6 +1845,30 @@ int mr_point_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, i
                              int32_t* pairs, int64_t cap, int64_t* n_pairs, int32_t* iter_active, void* ws,
                              size_t ws_bytes, void* stream) {
     return fast_impl(a, b, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, ws_bytes, stream, M_POINT);
+}
+
+int mr_fast_reciprocal_graph(const mr_map* images, const int32_t* edges, int32_t n_edges, int32_t stride,
+                             int32_t offset, int32_t max_iters, int32_t* pairs, int64_t cap, int64_t* n_pairs,
+                             int32_t* iter_active, void* ws, size_t ws_bytes, void* stream) {
+    int rc = validate_map(images);
+    if (rc) return rc;
+    if (!edges) return MR_ERR_NULL;
+    if (n_edges < 1 || n_edges > 65535) return MR_ERR_PARAM;
+    for (int64_t e = 0; e < 2 * (int64_t)n_edges; ++e)
+        if (edges[e] < 0 || edges[e] >= images->batch) return MR_ERR_PARAM;
+    if (stride < 1 || offset < 0 || max_iters < 0) return MR_ERR_PARAM;
+    const mr_map g = graph_map(images, n_edges);
+    const size_t at_edges = graph_edges_offset(&g, stride, offset);
+    if ((rc = check_ws(ws, ws_bytes, graph_ws_bytes(images, n_edges, stride, offset)))) return rc;
+    if (!pairs || !n_pairs) return MR_ERR_NULL;
+    if (cap < seed_count(g.h, g.w, stride, offset)) return MR_ERR_CAPACITY;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t* dev_edges = at<int32_t>(ws, at_edges);
+    if (hipMemcpyAsync(dev_edges, edges, (size_t)n_edges * 2 * sizeof(int32_t), hipMemcpyHostToDevice, st) !=
+        hipSuccess)
+        return MR_ERR_DEVICE;
+    return fast_impl(&g, &g, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, ws_bytes, stream,
+                     M_INNER, dev_edges);
 }
 
 int mr_profile_begin(int32_t max_launches) {

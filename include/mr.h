@@ -77,7 +77,8 @@ typedef struct {
 
 enum {
     MR_OP_NN_ARGMAX = 0, MR_OP_MUTUAL_NN = 1, MR_OP_FAST_RECIPROCAL = 2,
-    MR_OP_POINT_NN = 3, MR_OP_POINT_MUTUAL_NN = 4, MR_OP_POINT_FAST_RECIPROCAL = 5
+    MR_OP_POINT_NN = 3, MR_OP_POINT_MUTUAL_NN = 4, MR_OP_POINT_FAST_RECIPROCAL = 5,
+    MR_OP_FAST_RECIPROCAL_GRAPH = 6   /* a = b = the image collection, n_q = number of edges */
 };
 
 /* Workspace bytes that entry point `op` needs for these maps and parameters
@@ -142,6 +143,25 @@ int mr_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_b
 int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset,
                        int32_t max_iters, int32_t* pairs, int64_t cap, int64_t* n_pairs,
                        int32_t* iter_active, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mr_fast_reciprocal_graph: the fast scheme on many pairs of one collection of
+ * images (a reconstruction runs the pair model on every useful pair of a
+ * collection, organised as a graph: "DUSt3R and MASt3R explained", the
+ * paragraph on reconstructing a collection).  Each map is stored once.
+ *   images : the collection, batch = number of images (one map per image).
+ *   edges  : HOST int32 [n_edges][2]: edge e matches image edges[e][0] (seeded,
+ *            "image a") against image edges[e][1] ("image b"); ids must lie in
+ *            [0, images->batch) (else MR_ERR_PARAM); 1 <= n_edges <= 65535.
+ *            Copied into the workspace on `stream` before the call returns.
+ *   pairs, n_pairs, iter_active: per edge, as mr_fast_reciprocal's per pair.
+ *   ws     : mr_workspace_bytes(MR_OP_FAST_RECIPROCAL_GRAPH, images, images,
+ *            n_edges, stride, offset) bytes.
+ * Results equal mr_fast_reciprocal on each edge's two maps.
+ * --------------------------------------------------------------------------- */
+int mr_fast_reciprocal_graph(const mr_map* images, const int32_t* edges, int32_t n_edges, int32_t stride,
+                             int32_t offset, int32_t max_iters, int32_t* pairs, int64_t cap, int64_t* n_pairs,
+                             int32_t* iter_active, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Pointmaps.  A pointmap holds, for every pixel, the 3D point that pixel

@@ -170,3 +170,25 @@ def test_point_validation(lib):
     need = lib.mr_workspace_bytes(3, R(a), R(b), 100, 1, 0)
     assert lib.mr_point_nn(R(a), R(b), None, 100, out, None, out, need - 8, None) == WS
 
+
+def test_graph_validation(lib):
+    """Edge ids outside the collection, an empty graph and a short workspace are rejected
+    before anything runs."""
+    out = ctypes.c_void_p(FAKE)
+    imgs = M(8, 6, d=24, batch=4)
+    E = (ctypes.c_int32 * 6)(0, 1, 1, 3, 2, 0)
+    need = lib.mr_workspace_bytes(6, R(imgs), R(imgs), 3, 8, 4)
+    assert need > 0 and lib.mr_workspace_bytes(6, R(imgs), R(imgs), 0, 8, 4) == 0
+    assert lib.mr_workspace_bytes(6, R(imgs), R(imgs), 5, 8, 4) >= need
+    ws = ctypes.c_void_p(FAKE)
+    call = lambda edges, n, wsb=need, cap=1: lib.mr_fast_reciprocal_graph(
+        R(imgs), edges, n, 8, 4, 10, out, cap, out, None, ws, wsb, None)
+    bad = (ctypes.c_int32 * 6)(0, 1, 1, 4, 2, 0)     # image 4 of 4
+    neg = (ctypes.c_int32 * 6)(0, 1, -1, 3, 2, 0)
+    assert call(bad, 3) == PARAM
+    assert call(neg, 3) == PARAM
+    assert call(E, 0) == PARAM
+    assert call(None, 3) == NULL
+    assert call(E, 3, wsb=need - 1) == WS
+    assert call(E, 3, cap=0) == CAP
+

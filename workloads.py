@@ -190,6 +190,49 @@ def make_pair(H: int, W: int, d: int, seed: int, warp: str = "shift", sigma: flo
                 src=src, seed=seed, stride=stride, offset=offset, max_iters=max_iters)
 
 
+# ----------------------------------------------------------------------------- image collections
+
+def make_collection(n_images: int, H: int, W: int, d: int, seed: int, sigma: float = 0.15, rho: float = 0.3,
+                    dtype: str = "f32"):
+    """A collection of n_images maps that all view one scene: a base map D0 of unit rows,
+    and image k = D0 warped by its own random affine field (the pair recipe's warp), plus
+    sigma noise and rho occlusion, renormalised.  Any two images therefore share content,
+    as the pairs of a reconstruction's pair graph do.  Returns (maps float32 [n, N, d],
+    bf16 bits [n, N, d] or None, src int32 [n, N]: the D0 pixel each pixel shows, -1 if
+    occluded).  Draw order: D0, then per image: warp, noise, occlusion subset, occluders."""
+    N = H * W
+    rng = np.random.Generator(np.random.PCG64(seed))
+    D0 = unit_rows(rng, N, d)
+    maps = np.empty((n_images, N, d), np.float32)
+    srcs = np.empty((n_images, N), np.int32)
+    for k in range(n_images):
+        src = _warp_affine(rng, H, W)
+        X = D0[src]
+        if sigma > 0:
+            X = X + sigma * rng.standard_normal((N, d))
+        src = src.astype(np.int32)
+        m = int(math.floor(rho * N))
+        if m > 0:
+            occ = rng.choice(N, size=m, replace=False)
+            X[occ] = unit_rows(rng, m, d)
+            src[occ] = -1
+        X /= np.linalg.norm(X, axis=1, keepdims=True)
+        maps[k] = X.astype(np.float32)
+        srcs[k] = src
+    bits = None
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(maps)
+        maps = bf16_bits_to_f32(bits)
+    elif dtype != "f32":
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return maps, bits, srcs
+
+
+def all_edges(n_images: int):
+    """Every unordered pair (i, j), i < j, in lexicographic order (the complete pair graph)."""
+    return np.array([(i, j) for i in range(n_images) for j in range(i + 1, n_images)], np.int32)
+
+
 # ----------------------------------------------------------------------------- pointmaps
 
 def make_pointmaps(H: int, W: int, seed: int, warp: str = "affine", sigma: float = 0.005, rho: float = 0.3,
