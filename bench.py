@@ -268,7 +268,31 @@ def other_points_bruteforce(args, torch, dev):
             "roofline": roofline_alu(2.0 * p.N * p.N, steps, kms, kn)}
 
 
+def other_graph(args, torch, dev):
+    """The complete pair graph of 50 images of 512x384 fp32 (1225 edges) in one call."""
+    import dense_grounded_image_amd as mr
+    import workloads
+    n = 50
+    maps, _, _ = workloads.make_collection(n, 512, 384, 24, seed=2000)
+    imgs = torch.from_numpy(maps.reshape(n, 512, 384, 24)).to(dev)
+    del maps
+    edges = workloads.all_edges(n)
+    print("bench: collection ready", file=sys.stderr, flush=True)
+    g = mr.FastReciprocalGraph(imgs, edges, 8, 4, 10)
+    steps, warm = max(2, args.steps // 10), 1
+    ms, kms, kn = time_steps(lambda: g(imgs), steps, warm, torch, 20 * steps)
+    _, npairs, active = g(imgs)
+    torch.cuda.synchronize()
+    act = active.cpu().numpy()
+    q, flops = fast_work(act, 512 * 384, 24)
+    return {"pairs_per_s": round(len(edges) * 1000.0 / ms, 2), "ms_per_call": round(ms, 3),
+            "edges": int(len(edges)), "images": n, "images_bytes": int(imgs.numel() * 4),
+            "nn_queries_per_s": round(q * 1000.0 / ms, 1), "matches_total": int(npairs.sum()),
+            "roofline": roofline(flops, steps, kms, kn, "f32")}
+
+
 OTHER = {"batch64-512x384-f32": other_batch64, "pair-1024x768-bf16": other_bf16_1024,
+         "graph-50x512x384-f32": other_graph,
          "pointmaps-512x384-f32": other_points_fast, "pointmaps-512x384-f32-bruteforce": other_points_bruteforce,
          "pair-512x384-bf16-bruteforce": other_bruteforce}
 
