@@ -60,6 +60,8 @@ def _bind(lib):
     lib.orc_fast_metric.argtypes = [P, i32, i32, P, i64, i32, i32, i32, i32, i32, i32, i32, f64, P, i64,
                                     P, P, P, P]
     lib.orc_fast_metric.restype = ctypes.c_int
+    lib.orc_infonce.argtypes = [P, i64, P, i64, i32, P, i64, f64, i32, P, P]
+    lib.orc_infonce.restype = ctypes.c_int
     return lib
 
 
@@ -188,6 +190,20 @@ class Oracle:
                     nn_queries=nq.value)
 
 
+    def infonce(self, A, B, gt, tau, nthreads=None):
+        """Matching loss terms LSE_i - <A[i], B[j]> / tau per ground-truth pair (i, j), the
+        log-sum-exp over every row of B; returns (terms float64 [n_gt], total)."""
+        lib = self.lib
+        A, B = _f32(A), _f32(B)
+        gt = np.ascontiguousarray(np.asarray(gt, dtype=np.int32).reshape(-1, 2))
+        terms = np.empty(gt.shape[0], np.float64)
+        total = ctypes.c_double(0.0)
+        rc = lib.orc_infonce(_ptr(A), A.shape[0], _ptr(B), B.shape[0], A.shape[1], _ptr(gt), gt.shape[0],
+                             float(tau), nthreads or default_threads(), _ptr(terms), ctypes.byref(total))
+        assert rc == 0, rc
+        return terms, total.value
+
+
 _default = Oracle()
 nn = _default.nn
 nn_rows = _default.nn_rows
@@ -195,3 +211,4 @@ similarity_pairs = _default.similarity_pairs
 mutual = _default.mutual
 mutual_nn = _default.mutual_nn
 fast = _default.fast
+infonce = _default.infonce

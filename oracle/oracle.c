@@ -414,3 +414,68 @@ int orc_fast(const float* A, int32_t H1, int32_t W1, const float* B, int64_t n2,
     return orc_fast_metric(A, H1, W1, B, n2, d, ORC_INNER, stride, offset, T, seed_limit, nthreads, eps,
                            pairs, cap, n_pairs, pair_clean, active, nn_queries);
 }
+
+/* ------------------------------------------------------------------------
+ * Matching loss (InfoNCE).  [P1] section 3 ("Napkin Formula"): over the
+ * ground-truth matches M_gt,
+ *     L = - sum_{(i,j) in M_gt} log( exp(<D1[i], D2[j]> / tau)
+ *                                    / sum_k exp(<D1[i], D2[k]> / tau) ),
+ * the softmax running over every pixel k of image 2.  Term (i, j) is
+ * LSE_i - <D1[i], D2[j]> / tau with LSE_i = log sum_k exp(<D1[i], D2[k]> / tau),
+ * evaluated here in binary64 as m + log sum_k exp(s_k / tau - m), m the largest
+ * s_k / tau (exact algebra; it only keeps the exponentials finite).
+ * gt: int32 [n_gt][2] pairs (i, j); out_terms[t] = term of pair t; *out_total =
+ * their sum.  Pairs with an index out of range are rejected.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    const float* A; const float* B; int64_t n2; int d; double tau;
+    const int32_t* gt; double* terms; int64_t begin, end;
+} orc_nce_job;
+
+static void* orc_nce_worker(void* p)
+{
+    orc_nce_job* j = (orc_nce_job*)p;
+    for (int64_t t = j->begin; t < j->end; ++t) {
+        const float* q = j->A + (int64_t)j->gt[2 * t] * j->d;
+        double m = -INFINITY;
+        for (int64_t k = 0; k < j->n2; ++k) {
+            const double z = orc_similarity(q, j->B + k * (int64_t)j->d, j->d) / j->tau;
+            if (z > m) m = z;
+        }
+        double sum = 0.0;
+        for (int64_t k = 0; k < j->n2; ++k)
+            sum += exp(orc_similarity(q, j->B + k * (int64_t)j->d, j->d) / j->tau - m);
+        const double pos = orc_similarity(q, j->B + (int64_t)j->gt[2 * t + 1] * j->d, j->d) / j->tau;
+        j->terms[t] = m + log(sum) - pos;
+    }
+    return NULL;
+}
+
+int orc_infonce(const float* A, int64_t n1, const float* B, int64_t n2, int32_t d, const int32_t* gt,
+                int64_t n_gt, double tau, int32_t nthreads, double* out_terms, double* out_total)
+{
+    if (!A || !B || !gt || !out_terms || !out_total || n1 < 0 || n2 < 1 || d < 1 || n_gt < 0 || !(tau > 0))
+        return ORC_ERR_ARG;
+    for (int64_t t = 0; t < n_gt; ++t)
+        if (gt[2 * t] < 0 || gt[2 * t] >= n1 || gt[2 * t + 1] < 0 || gt[2 * t + 1] >= n2) return ORC_ERR_ARG;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (n_gt > 0 && nthreads > n_gt) nthreads = (int)n_gt;
+    orc_nce_job jobs[256];
+    pthread_t th[256];
+    int started[256];
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i] = (orc_nce_job){A, B, n2, d, tau, gt, out_terms, n_gt * i / nthreads, n_gt * (i + 1) / nthreads};
+        started[i] = 0;
+    }
+    for (int i = 1; i < nthreads; ++i) started[i] = pthread_create(&th[i], NULL, orc_nce_worker, &jobs[i]) == 0;
+    if (nthreads > 0) orc_nce_worker(&jobs[0]);
+    for (int i = 1; i < nthreads; ++i) {
+        if (started[i]) pthread_join(th[i], NULL);
+        else orc_nce_worker(&jobs[i]);
+    }
+    double total = 0.0;
+    for (int64_t t = 0; t < n_gt; ++t) total += out_terms[t];
+    *out_total = total;
+    return ORC_OK;
+}

@@ -420,6 +420,43 @@ def pin_point_clean_flag_relative(orc):
     assert 0 < sum(want.values()) < len(want)
 
 
+# ============================================================================ matching loss
+# "MASt3R dissection", section 3: term (i, j) = log sum_k exp(<D1[i], D2[k]> / tau) - <D1[i], D2[j]> / tau.
+
+
+def pin_infonce_closed_forms(orc):
+    """Two database rows e0, e1 and the query e0 at tau = 0.5: the scores are 1 and 0, so the
+    terms are softplus(-2) = log(1 + e^-2) for the true pair and softplus(2) for the other;
+    identical database rows give log(n) whatever the query; a pair's term is never negative."""
+    A = np.array([[1, 0], [0.6, 0.8]], np.float32)
+    B = np.array([[1, 0], [0, 1]], np.float32)
+    t, tot = orc.infonce(A, B, [[0, 0], [0, 1]], 0.5)
+    assert abs(t[0] - math.log1p(math.exp(-2.0))) < 1e-13 and abs(t[1] - math.log1p(math.exp(2.0))) < 1e-13
+    assert abs(tot - t.sum()) < 1e-13
+    Bsame = np.tile(np.array([[0.6, 0.8]], np.float32), (7, 1))
+    t2, _ = orc.infonce(A, Bsame, [[0, 3], [1, 6]], 0.1)
+    assert np.abs(t2 - math.log(7)).max() < 1e-12
+    assert (t >= 0).all() and (t2 >= 0).all()
+
+
+def pin_infonce_scipy(orc):
+    """Against scipy's log-sum-exp of numpy's float64 score matrix, several temperatures,
+    including one small enough that exp(s / tau) overflows binary64 without a shift."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(41)
+    A = _rand_unit(rng, 23, 24).astype(np.float32)
+    B = _rand_unit(rng, 31, 24).astype(np.float32)
+    B[3:8] = A[:5]            # scores of about 1: exp(s / 0.001) overflows binary64 unshifted
+    gt = np.stack([rng.integers(0, 23, 40), rng.integers(0, 31, 40)], 1).astype(np.int32)
+    gt[:5, 0] = np.arange(5)
+    S = A.astype(np.float64) @ B.astype(np.float64).T
+    for tau in (1.0, 0.1, 0.001):
+        t, tot = orc.infonce(A, B, gt, tau)
+        ref = logsumexp(S[gt[:, 0]] / tau, axis=1) - S[gt[:, 0], gt[:, 1]] / tau
+        assert np.abs(t - ref).max() < 1e-9 * max(1.0, np.abs(ref).max())
+        assert abs(tot - ref.sum()) < 1e-9 * max(1.0, np.abs(ref).sum())
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 
 

@@ -38,6 +38,13 @@ MUTANTS = {
     "point_backward_search_inner_product": ("orc_nn_parallel(B, todo, nt, A, n1, d, metric,",
                                             "orc_nn_parallel(B, todo, nt, A, n1, d, ORC_INNER,"),
     "point_margin_absolute": ("return (top1 - top2) / -top2;", "return top1 - top2;"),
+    # matching loss
+    "nce_shift_dropped": ("sum += exp(orc_similarity(q, j->B + k * (int64_t)j->d, j->d) / j->tau - m);",
+                          "sum += exp(orc_similarity(q, j->B + k * (int64_t)j->d, j->d) / j->tau);"),
+    "nce_positive_from_query_index": ("j->B + (int64_t)j->gt[2 * t + 1] * j->d", "j->B + (int64_t)j->gt[2 * t] * j->d"),
+    "nce_temperature_ignored": ("const double z = orc_similarity(q, j->B + k * (int64_t)j->d, j->d) / j->tau;",
+                                "const double z = orc_similarity(q, j->B + k * (int64_t)j->d, j->d);"),
+    "nce_sign_flipped": ("j->terms[t] = m + log(sum) - pos;", "j->terms[t] = pos - m - log(sum);"),
 }
 
 
