@@ -156,6 +156,11 @@ def roofline(flops_per_step, steps, kernel_ms, launches, dtype, traffic=None):
         out["executed"] = {"arith": "bf16 x3 split, 6 bf16 products per fp32 product",
                            "achieved_bf16_TFLOPs": round(6 * achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                            "frac": round(6 * achieved / PEAK_TFLOPS["bf16"], 4)}
+    elif dtype == "bf16":
+        pad = 32.0 / 24.0   # d = 24 runs as K = 32 on the 32x32x16 bf16 instruction
+        out["executed"] = {"arith": "d = 24 padded to K = 32 on the bf16 matrix cores",
+                           "achieved_bf16_TFLOPs": round(pad * achieved, 2), "peak": PEAK_TFLOPS["bf16"],
+                           "frac": round(pad * achieved / PEAK_TFLOPS["bf16"], 4)}
     return out
 
 
