@@ -35,6 +35,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "mr.h"
 
 namespace {
@@ -374,6 +376,125 @@ __device__ __forceinline__ void tile_track(const f32x16& acc, int t, int h, int 
     bv = m;
 }
 
+// Per-lane running state of a streamed database segment: one entry per query tile
+// j, updated once per 32-row database tile t (RAGGED: rows at or past ndb are
+// masked).  step() takes the ragged flag at run time.
+enum Epilogue { EP_KEY = 0, EP_EXACT = 1, EP_TILE = 2, EP_LSE = 3 };
+
+// Keyed row maximum: (score, row) of the NN while the lane's best score is >= 0.
+template <int QT> struct KeyBest {
+    static constexpr int kind = EP_KEY;
+    int bk[QT], bt[QT];
+    __device__ __forceinline__ KeyBest() {
+#pragma unroll
+        for (int j = 0; j < QT; ++j) { bk[j] = INT_MIN; bt[j] = -1; }
+    }
+    __device__ __forceinline__ void keep(int km, int t, int j) {
+        const bool gt = km > (bk[j] | 15);   // strictly better score: earliest tile wins ties
+        bk[j] = gt ? km : bk[j];
+        bt[j] = gt ? t : bt[j];
+    }
+    template <bool RAGGED>
+    __device__ __forceinline__ void tile(const f32x16& acc, int t, int h, int ndb, int j) {
+        keep(tile_key<RAGGED>(acc, t, h, ndb), t, j);
+    }
+    __device__ __forceinline__ void step(const f32x16& acc, int t, int h, int ndb, int j, bool ragged) {
+        keep(ragged ? tile_key<true>(acc, t, h, ndb) : tile_key<false>(acc, t, h, ndb), t, j);
+    }
+};
+
+// Exact row maximum (any sign); bx = 16 * tile + accumulator register.
+template <int QT> struct ExactBest {
+    static constexpr int kind = EP_EXACT;
+    float bv[QT];
+    int bx[QT];
+    __device__ __forceinline__ ExactBest() {
+#pragma unroll
+        for (int j = 0; j < QT; ++j) { bv[j] = -INFINITY; bx[j] = -1; }
+    }
+    template <bool RAGGED>
+    __device__ __forceinline__ void tile(const f32x16& acc, int t, int h, int ndb, int j) {
+        tile_exact<RAGGED>(acc, t, h, ndb, bv[j], bx[j]);
+    }
+    __device__ __forceinline__ void step(const f32x16& acc, int t, int h, int ndb, int j, bool ragged) {
+        if (ragged) tile<true>(acc, t, h, ndb, j);
+        else tile<false>(acc, t, h, ndb, j);
+    }
+};
+
+// Tile-level maximum: best compared score and the first tile reaching it.
+template <int QT> struct TileBest {
+    static constexpr int kind = EP_TILE;
+    float bv[QT];
+    int bt[QT];
+    __device__ __forceinline__ TileBest() {
+#pragma unroll
+        for (int j = 0; j < QT; ++j) { bv[j] = -INFINITY; bt[j] = -1; }
+    }
+    template <bool RAGGED>
+    __device__ __forceinline__ void tile(const f32x16& acc, int t, int h, int ndb, int j) {
+        tile_track<RAGGED>(acc, t, h, ndb, bv[j], bt[j]);
+    }
+    __device__ __forceinline__ void step(const f32x16& acc, int t, int h, int ndb, int j, bool ragged) {
+        if (ragged) tile<true>(acc, t, h, ndb, j);
+        else tile<false>(acc, t, h, ndb, j);
+    }
+};
+
+// Online log-sum-exp of a query's scores over the database rows (the softmax
+// normaliser of the matching loss), in base 2: with k2 = log2(e) / tau and
+// z = score * k2, the state is m = the largest z seen (each z rounded once to fp32)
+// and s = the sum over the rows seen of 2^(z - m), each exponent formed as
+// fma(score, k2, -m) (one rounding, at most 0 up to that rounding, so no term
+// overflows; a term below the fp32 range is below 2^-126 of the largest).  When a
+// tile raises m, s is rescaled by 2^(m_old - m_new), which is exactly 1 while m
+// stays (a rescale by the rounding error of score * k2 at every tile would bias s
+// over thousands of tiles).  s is a compensated (Kahan) sum with compensation c,
+// so its error stays at a few units of fp32 rounding however long the segment.
+template <int QT> struct LseSum {
+    static constexpr int kind = EP_LSE;
+    float m[QT], s[QT], c[QT];
+    float k2;
+    __device__ __forceinline__ explicit LseSum(float k2_) : k2(k2_) {
+#pragma unroll
+        for (int j = 0; j < QT; ++j) { m[j] = -INFINITY; s[j] = 0.0f; c[j] = 0.0f; }
+    }
+    template <bool RAGGED>
+    __device__ __forceinline__ void tile(const f32x16& acc, int t, int h, int ndb, int j) {
+        float k[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) k[v] = (RAGGED && t * 32 + tile_row(v, h) >= ndb) ? -INFINITY : acc[v];
+        auto mx3 = [](float a, float b, float c) {
+            return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+        };
+        const float m0 = mx3(k[0], k[1], k[2]), m1 = mx3(k[3], k[4], k[5]), m2 = mx3(k[6], k[7], k[8]);
+        const float m3 = mx3(k[9], k[10], k[11]), m4 = mx3(k[12], k[13], k[14]);
+        const float mt = mx3(mx3(m1, m2, m3), m4, __builtin_elementwise_maximum(k[15], m0));
+        const float mn = __builtin_elementwise_maximum(m[j], mt * k2);   // rounding is monotone
+        // a lane with no row yet (possible in ragged tiles only) keeps m = -inf and
+        // s = c = 0: with offset 0 its exponents are all -inf (v_exp gives 0)
+        const float off = (RAGGED && mn == -INFINITY) ? 0.0f : -mn;
+        float e[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) e[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(k[v], k2, off));
+#pragma unroll
+        for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+            for (int v = 0; v < w; ++v) e[v] += e[v + w];
+        const float f = __builtin_amdgcn_exp2f(m[j] + off);   // 1 unless m rises
+        const float sf = s[j] * f;
+        const float y = e[0] - c[j] * f;
+        const float tot = sf + y;
+        c[j] = (tot - sf) - y;
+        s[j] = tot;
+        m[j] = mn;
+    }
+    __device__ __forceinline__ void step(const f32x16& acc, int t, int h, int ndb, int j, bool ragged) {
+        if (ragged) tile<true>(acc, t, h, ndb, j);
+        else tile<false>(acc, t, h, ndb, j);
+    }
+};
+
 template <int AR> __device__ __forceinline__ const void* pair_base(const void* p, int64_t elems, int64_t map) {
     return static_cast<const typename ArithTraits<AR>::elem*>(p) + map * elems * ArithTraits<AR>::row_mult;
 }
@@ -393,16 +514,11 @@ template <int AR, int P> constexpr int lds_row_bytes() {        // a staged row 
 // (one cooperative 16-byte-chunk copy per tile, one barrier per tile); each of its
 // four waves multiplies the staged tile against its own QT query tiles held in
 // registers and keeps a per-lane running best.
-// Epilogue of a streamed tile: keyed row maximum, exact row maximum (for negative
-// bests), or tile-level maximum.
-enum Epilogue { EP_KEY = 0, EP_EXACT = 1, EP_TILE = 2 };
-
-template <int AR, int P, int EP>
+// The per-lane state ep (one of the epilogue states above) takes each product tile.
+template <int AR, int P, class Ep>
 __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb,
                                              char* lds, const Operand<AR, P> (&q)[qt_of<AR, P>()],
-                                             int nact, int h, int jl, int d, int role,
-                                             int (&bk)[qt_of<AR, P>()], int (&bt)[qt_of<AR, P>()],
-                                             float (&bv)[qt_of<AR, P>()]) {
+                                             int nact, int h, int jl, int d, int role, Ep& ep) {
     constexpr int QT = qt_of<AR, P>();
     constexpr int MAXC = (32 * max_row_bytes<AR, P>() / 16 + kThreads - 1) / kThreads;
     constexpr int BUF = 32 * lds_row_bytes<AR, P>();
@@ -461,7 +577,7 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
         const bool ragged = (t + 1) * 32 > ndb;
         Operand<AR, P> r;
         r.load(lds + (i & 1) * BUF, jl, true, h, d, role);
-        if constexpr (AR == AR_X3 && EP == EP_KEY) {
+        if constexpr (AR == AR_X3 && Ep::kind == EP_KEY) {
             if (nact == QT && !ragged) {
                 // the query tiles' step chains interleaved: consecutive products are
                 // independent, so none waits for the one before it
@@ -473,12 +589,7 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
 #pragma unroll
                     for (int j = 0; j < QT; ++j) acc[j] = r.step(st, q[j], acc[j]);
 #pragma unroll
-                for (int j = 0; j < QT; ++j) {
-                    const int km = tile_key<false>(acc[j], t, h, ndb);
-                    const bool gt = km > (bk[j] | 15);
-                    bk[j] = gt ? km : bk[j];
-                    bt[j] = gt ? t : bt[j];
-                }
+                for (int j = 0; j < QT; ++j) ep.template tile<false>(acc[j], t, h, ndb, j);
                 return;
             }
         }
@@ -487,18 +598,7 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
             if (j < nact) {
                 f32x16 acc = {};
                 acc = r.mfma(q[j], acc);
-                if constexpr (EP == EP_TILE) {
-                    if (ragged) tile_track<true>(acc, t, h, ndb, bv[j], bt[j]);
-                    else tile_track<false>(acc, t, h, ndb, bv[j], bt[j]);
-                } else if constexpr (EP == EP_EXACT) {
-                    if (ragged) tile_exact<true>(acc, t, h, ndb, bv[j], bt[j]);
-                    else tile_exact<false>(acc, t, h, ndb, bv[j], bt[j]);
-                } else {
-                    const int km = ragged ? tile_key<true>(acc, t, h, ndb) : tile_key<false>(acc, t, h, ndb);
-                    const bool gt = km > (bk[j] | 15);   // strictly better score: earliest tile wins ties
-                    bk[j] = gt ? km : bk[j];
-                    bt[j] = gt ? t : bt[j];
-                }
+                ep.step(acc, t, h, ndb, j, ragged);
             }
         }
     };
@@ -534,11 +634,10 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
 // ragged epilogue masks them.
 constexpr int kStageTiles = 2;
 
-template <int AR, int P, int EP, int S>
+template <int AR, int P, int S, class Ep>
 __device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb,
                                               char* lds, const Operand<AR, P> (&q)[qt_of<AR, P>()], int nact,
-                                              int h, int jl, int d, int role, int (&bk)[qt_of<AR, P>()],
-                                              int (&bt)[qt_of<AR, P>()], float (&bv)[qt_of<AR, P>()]) {
+                                              int h, int jl, int d, int role, Ep& ep) {
     static_assert(AR == AR_BF16, "the staged ring holds bf16 rows");
     constexpr int QT = qt_of<AR, P>();
     constexpr int NB = 3;
@@ -582,20 +681,7 @@ __device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, i
 #pragma unroll
         for (int x = 0; x < S; ++x) opr[x].load_db(buf + x * 32 * rb, off);
     };
-    auto epilogue = [&](const f32x16& acc, int t, bool ragged, int j) {
-        if constexpr (EP == EP_TILE) {
-            if (ragged) tile_track<true>(acc, t, h, ndb, bv[j], bt[j]);
-            else tile_track<false>(acc, t, h, ndb, bv[j], bt[j]);
-        } else if constexpr (EP == EP_EXACT) {
-            if (ragged) tile_exact<true>(acc, t, h, ndb, bv[j], bt[j]);
-            else tile_exact<false>(acc, t, h, ndb, bv[j], bt[j]);
-        } else {
-            const int km = ragged ? tile_key<true>(acc, t, h, ndb) : tile_key<false>(acc, t, h, ndb);
-            const bool gt = km > (bk[j] | 15);   // strictly better score: earliest tile wins ties
-            bk[j] = gt ? km : bk[j];
-            bt[j] = gt ? t : bt[j];
-        }
-    };
+    auto epilogue = [&](const f32x16& acc, int t, bool ragged, int j) { ep.step(acc, t, h, ndb, j, ragged); };
     auto compute = [&](int k) {
 #pragma unroll
         for (int x = 0; x < S; ++x) {
@@ -644,26 +730,24 @@ __device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, i
 // The workgroup-staged stream for an arithmetic: the LDS ring for bf16 rows; the
 // plain double buffer for fp32 rows (measured faster for the long split contraction,
 // whose nine matrix-core steps per tile already cover the staging latency).
-template <int AR, int P, int EP>
+template <int AR, int P, class Ep>
 __device__ __forceinline__ void stream_db(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb, char* lds,
                                           const Operand<AR, P> (&q)[qt_of<AR, P>()], int nact, int h, int jl, int d,
-                                          int role, int (&bk)[qt_of<AR, P>()], int (&bt)[qt_of<AR, P>()],
-                                          float (&bv)[qt_of<AR, P>()]) {
+                                          int role, Ep& ep) {
     if constexpr (AR != AR_BF16)
-        stream_tiles<AR, P, EP>(dbytes, rb, t0, t1, ndb, lds, q, nact, h, jl, d, role, bk, bt, bv);
+        stream_tiles<AR, P>(dbytes, rb, t0, t1, ndb, lds, q, nact, h, jl, d, role, ep);
     else
-        stream_staged<AR, P, EP, kStageTiles>(dbytes, rb, t0, t1, ndb, lds, q, nact, h, jl, d, role, bk, bt, bv);
+        stream_staged<AR, P, kStageTiles>(dbytes, rb, t0, t1, ndb, lds, q, nact, h, jl, d, role, ep);
 }
 
 // Full work items of bf16 maps, without LDS or barriers: each wave reads the
 // database operand straight from global memory (the four waves of a workgroup read
 // the same tiles, so L1 serves all but the first) into a ring of D tiles issued D
 // tiles ahead of their use.
-template <int AR, int P, int EP, int D>
+template <int AR, int P, int D, class Ep>
 __device__ __forceinline__ void stream_regs(const void* dbase, int t0, int t1,
                                             const Operand<AR, P> (&q)[qt_of<AR, P>()], int h, int jl, int d,
-                                            int (&bk)[qt_of<AR, P>()], int (&bt)[qt_of<AR, P>()],
-                                            float (&bv)[qt_of<AR, P>()]) {
+                                            Ep& ep) {
     constexpr int QT = qt_of<AR, P>();
     static_assert(AR == AR_BF16, "direct database operands are bf16 only");
     Operand<AR, P> r[D];
@@ -682,16 +766,7 @@ __device__ __forceinline__ void stream_regs(const void* dbase, int t0, int t1,
 #pragma unroll
         for (int j = 0; j < QT; ++j) acc[j] = rr.mfma(q[j], f32x16{});
 #pragma unroll
-        for (int j = 0; j < QT; ++j) {
-            if constexpr (EP == EP_TILE) {
-                tile_track<false>(acc[j], tt, h, 0, bv[j], bt[j]);
-            } else {
-                const int km = tile_key<false>(acc[j], tt, h, 0);
-                const bool gt = km > (bk[j] | 15);
-                bk[j] = gt ? km : bk[j];
-                bt[j] = gt ? tt : bt[j];
-            }
-        }
+        for (int j = 0; j < QT; ++j) ep.template tile<false>(acc[j], tt, h, 0, j);
     };
     // whole groups of D tiles: no branch inside, refills clamped, so the compiler
     // counts outstanding loads exactly
@@ -713,12 +788,10 @@ __device__ __forceinline__ void stream_regs(const void* dbase, int t0, int t1,
 // Small frontiers (all live queries fit in one wave): every wave of the workgroup
 // holds the same queries and streams its own database segment straight from global
 // memory, one tile ahead in registers, with no LDS staging and no barriers.
-template <int AR, int P, int EP>
+template <int AR, int P, class Ep>
 __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1, int ndb,
                                               const Operand<AR, P> (&q)[qt_of<AR, P>()],
-                                              int nact, int h, int jl, int d, int role,
-                                              int (&bk)[qt_of<AR, P>()], int (&bt)[qt_of<AR, P>()],
-                                              float (&bv)[qt_of<AR, P>()]) {
+                                              int nact, int h, int jl, int d, int role, Ep& ep) {
     constexpr int QT = qt_of<AR, P>();
     if (t0 >= t1) return;
     auto row_of = [&](int t) { return (int64_t)t * 32 + jl; };
@@ -739,18 +812,7 @@ __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1,
             if (j < nact) {
                 f32x16 acc = {};
                 acc = r.mfma(q[j], acc);
-                if constexpr (EP == EP_TILE) {
-                    if (ragged) tile_track<true>(acc, t, h, ndb, bv[j], bt[j]);
-                    else tile_track<false>(acc, t, h, ndb, bv[j], bt[j]);
-                } else if constexpr (EP == EP_EXACT) {
-                    if (ragged) tile_exact<true>(acc, t, h, ndb, bv[j], bt[j]);
-                    else tile_exact<false>(acc, t, h, ndb, bv[j], bt[j]);
-                } else {
-                    const int km = ragged ? tile_key<true>(acc, t, h, ndb) : tile_key<false>(acc, t, h, ndb);
-                    const bool gt = km > (bk[j] | 15);
-                    bk[j] = gt ? km : bk[j];
-                    bt[j] = gt ? t : bt[j];
-                }
+                ep.step(acc, t, h, ndb, j, ragged);
             }
         }
     }
@@ -821,18 +883,18 @@ void nn_argmax_kernel(NNArgs a) {
             }
         }
     };
-    auto finish = [&](int (&bk)[QT], int (&bt)[QT], float (&sv)[QT], int (&rw)[QT]) {
+    auto finish = [&](const KeyBest<QT>& b, float (&sv)[QT], int (&rw)[QT]) {
 #pragma unroll
         for (int j = 0; j < QT; ++j) {
-            sv[j] = __int_as_float(bk[j] & ~15);
-            rw[j] = bt[j] >= 0 ? bt[j] * 32 + tile_row(15 - (bk[j] & 15), h) : -1;
+            sv[j] = __int_as_float(b.bk[j] & ~15);
+            rw[j] = b.bt[j] >= 0 ? b.bt[j] * 32 + tile_row(15 - (b.bk[j] & 15), h) : -1;
         }
     };
-    auto finish_exact = [&](const float (&bv)[QT], const int (&bx)[QT], float (&sv)[QT], int (&rw)[QT]) {
+    auto finish_exact = [&](const ExactBest<QT>& b, float (&sv)[QT], int (&rw)[QT]) {
 #pragma unroll
         for (int j = 0; j < QT; ++j) {
-            sv[j] = bv[j];
-            rw[j] = bx[j] >= 0 ? (bx[j] >> 4) * 32 + tile_row(bx[j] & 15, h) : -1;
+            sv[j] = b.bv[j];
+            rw[j] = b.bx[j] >= 0 ? (b.bx[j] >> 4) * 32 + tile_row(b.bx[j] & 15, h) : -1;
         }
     };
 
@@ -854,28 +916,24 @@ void nn_argmax_kernel(NNArgs a) {
             const int seg = grp * kWaves + wv, nseg = ngroups * kWaves;
             const int t0 = (int)((int64_t)seg * ntiles / nseg);
             const int t1 = (int)((int64_t)(seg + 1) * ntiles / nseg);
-            int bk[QT], bt[QT];
-            float bv[QT];
-#pragma unroll
-            for (int j = 0; j < QT; ++j) { bk[j] = INT_MIN; bt[j] = -1; bv[j] = -INFINITY; }
             float sv[QT];
             int rw[QT];   // row, or tile with TB
             if constexpr (TB) {
-                stream_direct<AR, P, EP_TILE>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
+                TileBest<QT> best;
+                stream_direct<AR, P>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, best);
 #pragma unroll
-                for (int j = 0; j < QT; ++j) { sv[j] = bv[j]; rw[j] = bt[j]; }
+                for (int j = 0; j < QT; ++j) { sv[j] = best.bv[j]; rw[j] = best.bt[j]; }
             } else {
-                stream_direct<AR, P, EP_KEY>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
-                finish(bk, bt, sv, rw);
+                KeyBest<QT> best;
+                stream_direct<AR, P>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, best);
+                finish(best, sv, rw);
                 bool neg = false;
 #pragma unroll
-                for (int j = 0; j < QT; ++j) neg = neg || (j < nact && bk[j] < 0 && t0 < t1);
+                for (int j = 0; j < QT; ++j) neg = neg || (j < nact && best.bk[j] < 0 && t0 < t1);
                 if (__ballot(neg) != 0) {
-                    int bx[QT];
-#pragma unroll
-                    for (int j = 0; j < QT; ++j) bx[j] = -1;
-                    stream_direct<AR, P, EP_EXACT>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, bk, bx, bv);
-                    finish_exact(bv, bx, sv, rw);
+                    ExactBest<QT> exact;
+                    stream_direct<AR, P>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, exact);
+                    finish_exact(exact, sv, rw);
                 }
             }
 #pragma unroll
@@ -914,37 +972,32 @@ void nn_argmax_kernel(NNArgs a) {
         const int t0 = (int)((int64_t)sg * ntiles / nsg);
         const int t1 = (int)((int64_t)(sg + 1) * ntiles / nsg);
 
-        int bk[QT], bt[QT];
-        float bv[QT];
-#pragma unroll
-        for (int j = 0; j < QT; ++j) { bk[j] = INT_MIN; bt[j] = -1; bv[j] = -INFINITY; }
         // (score, row) -- or (score, tile) with TB -- per lane and query tile
         float sv[QT];
         int rw[QT];
         if constexpr (TB) {
+            TileBest<QT> best;
             // the choice must be the same for all four waves: both paths stage tiles
             // cooperatively, with workgroup barriers
             if (g1 - g0 == kWaves * QT && (int64_t)t1 * 32 <= a.ndb)
-                stream_regs<AR, P, EP_TILE, 4>(dbytes, t0, t1, q, h, jl, a.d, bk, bt, bv);
+                stream_regs<AR, P, 4>(dbytes, t0, t1, q, h, jl, a.d, best);
             else
-                stream_db<AR, P, EP_TILE>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
+                stream_db<AR, P>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, best);
 #pragma unroll
-            for (int j = 0; j < QT; ++j) { sv[j] = bv[j]; rw[j] = bt[j]; }
+            for (int j = 0; j < QT; ++j) { sv[j] = best.bv[j]; rw[j] = best.bt[j]; }
         } else {
-            stream_db<AR, P, EP_KEY>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bt, bv);
-            finish(bk, bt, sv, rw);
+            KeyBest<QT> best;
+            stream_db<AR, P>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, best);
+            finish(best, sv, rw);
             bool neg = false;
 #pragma unroll
-            for (int j = 0; j < QT; ++j) neg = neg || (j < nact && bk[j] < 0);
+            for (int j = 0; j < QT; ++j) neg = neg || (j < nact && best.bk[j] < 0);
             if (__syncthreads_or(neg)) {
                 // some lane's best score is negative, where float bits do not order as
                 // integers: the workgroup streams its segment again with the exact comparison
-                int bx[QT];
-#pragma unroll
-                for (int j = 0; j < QT; ++j) bx[j] = -1;
-                stream_db<AR, P, EP_EXACT>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, bk, bx,
-                                           bv);
-                finish_exact(bv, bx, sv, rw);
+                ExactBest<QT> exact;
+                stream_db<AR, P>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, exact);
+                finish_exact(exact, sv, rw);
             }
         }
 
@@ -1339,6 +1392,160 @@ __global__ __launch_bounds__(256) void compact_scatter_kernel(Pred pr, int64_t n
     if (blockIdx.x == nblk - 1 && threadIdx.x == 0) n_pairs[pair] = run;
 }
 
+// ---------------------------------------------------------------------------- matching loss
+
+// The InfoNCE matching loss over ground-truth pairs M_gt of an image pair
+// ("MASt3R dissection", section 3 "Napkin Formula"): pair (i, j) contributes
+//     LSE_i - <a_i, b_j> / tau,   LSE_i = log sum_k exp(<a_i, b_k> / tau),
+// the softmax running over every row k of map b.  lse_partial_kernel streams b
+// against the rows i named by the ground truth with the similarity kernel's tiles
+// and an online log-sum-exp epilogue (LseSum); nce_terms_kernel merges the
+// partials of each pair in a fixed order and forms its term; nce_loss_kernel adds
+// the terms of each image pair in a fixed order (in binary64).
+struct NceArgs {
+    const void* amap;        // [batch][n1][d] (image 1: the rows i)
+    const void* bmap;        // [batch][n2][d] (image 2: the rows j and k)
+    int64_t a_pair_elems;    // n1 * d
+    int64_t b_pair_elems;    // n2 * d
+    int32_t n1, n2, d;
+    const int32_t* gt;       // [batch][n_gt][2] (i, j)
+    int32_t n_gt;
+    int32_t nseg;            // database segments, i.e. partials per ground-truth pair
+    int32_t nblk;            // blocks of nce_terms_kernel per image pair
+    float k2;                // log2(e) / tau
+    float2* partial;         // [batch][n_gt][nseg] (m, s) of LseSum (base 2), merged over the lane halves
+    float* terms;            // [batch][n_gt]
+    double* block_sums;      // [batch][nblk]
+    double* loss;            // [batch]
+};
+
+// Work item = (query group, database segment) as in nn_argmax_kernel, with the
+// segment count fixed by the host so that partial[pair][t][segment] is written
+// exactly once for every ground-truth pair t.  A ground-truth row out of range
+// streams as a zero query (its term is set to NaN later).
+template <int AR, int P>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(min_waves<AR, P>())))
+void lse_partial_kernel(NceArgs a) {
+    constexpr int QT = qt_of<AR, P>();
+    constexpr int LDS_TILES = (AR == AR_BF16 ? 3 * kStageTiles : 2) * 32 * lds_row_bytes<AR, P>();
+    __shared__ __attribute__((aligned(16))) char lds[LDS_TILES];
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5;
+    const int jl = lane & 31;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.y;
+    const int n = a.n_gt;
+    const int ntiles = (a.n2 + 31) >> 5;
+    const int nqt = (n + 31) >> 5;
+    const int qgroups = (nqt + kWaves * QT - 1) / (kWaves * QT);
+    const int nsg = a.nseg;
+    const int items = qgroups * nsg;
+    const void* qbase = pair_base<AR>(a.amap, a.a_pair_elems, pair);
+    const char* dbytes = static_cast<const char*>(pair_base<AR>(a.bmap, a.b_pair_elems, pair));
+    const int rb = row_bytes<AR>(a.d);
+    const int32_t* gt = a.gt + (int64_t)pair * n * 2;
+
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int qg = item / nsg;
+        const int sg = item - qg * nsg;
+        const int g0 = (int)((int64_t)qg * nqt / qgroups);
+        const int g1 = (int)((int64_t)(qg + 1) * nqt / qgroups);
+        const int nact = g0 + wv < g1 ? (g1 - g0 - wv + kWaves - 1) / kWaves : 0;
+        Operand<AR, P> q[QT];
+#pragma unroll
+        for (int j = 0; j < QT; ++j) {
+            if (j < nact) {
+                const int qp = (g0 + wv + j * kWaves) * 32 + jl;
+                const int64_t row = qp < n ? gt[2 * qp] : -1;
+                const bool valid = row >= 0 && row < a.n1;
+                if constexpr (AR == AR_X3)
+                    q[j].load_f32(static_cast<const float*>(qbase) + (valid ? row : 0) * a.d, valid, h, 1);
+                else
+                    q[j].load(qbase, valid ? row : 0, valid, h, a.d, 1);
+            }
+        }
+        const int t0 = (int)((int64_t)sg * ntiles / nsg);
+        const int t1 = (int)((int64_t)(sg + 1) * ntiles / nsg);
+        LseSum<QT> ep(a.k2);
+        stream_db<AR, P>(dbytes, rb, t0, t1, a.n2, lds, q, nact, h, jl, a.d, 2, ep);
+        // merge the two lane halves (disjoint rows of the same query)
+#pragma unroll
+        for (int j = 0; j < QT; ++j) {
+            if (j < nact) {
+                const float sj = ep.s[j] - ep.c[j];
+                const float mo = __shfl_xor(ep.m[j], 32), so = __shfl_xor(sj, 32);
+                const float m = __builtin_elementwise_maximum(ep.m[j], mo);
+                const float off = m == -INFINITY ? 0.0f : -m;
+                const float s = sj * __builtin_amdgcn_exp2f(ep.m[j] + off) + so * __builtin_amdgcn_exp2f(mo + off);
+                const int qp = (g0 + wv + j * kWaves) * 32 + jl;
+                if (h == 0 && qp < n) a.partial[((int64_t)pair * n + qp) * nsg + sg] = make_float2(m, s);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float elem_f32(float x) { return x; }
+__device__ __forceinline__ float elem_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// Per ground-truth pair t = (i, j), from the base-2 partials (m_seg, s_seg):
+// m = max m_seg, S = sum over segments (in order, compensated) of s_seg 2^(m_seg - m),
+//     term = ln 2 * (m - <a_i, b_j> * k2) + ln S,
+// the positive score an fp32 dot product (components in order).  NaN when i or j is
+// out of range.  Each block also leaves the binary64 sum of its terms.
+template <typename T>
+__global__ __launch_bounds__(256) void nce_terms_kernel(NceArgs a) {
+    __shared__ double red[256];
+    const int pair = blockIdx.y;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    double contrib = 0.0;
+    if (t < a.n_gt) {
+        const int64_t pt = (int64_t)pair * a.n_gt + t;
+        const int i = a.gt[2 * pt], j = a.gt[2 * pt + 1];
+        const float2* p = a.partial + pt * a.nseg;
+        float m = -INFINITY;
+        for (int k = 0; k < a.nseg; ++k) m = __builtin_elementwise_maximum(m, p[k].x);
+        float S = 0.0f, c = 0.0f;
+        for (int k = 0; k < a.nseg; ++k) {
+            const float y = p[k].y * __builtin_amdgcn_exp2f(p[k].x - m) - c;
+            const float tot = S + y;
+            c = (tot - S) - y;
+            S = tot;
+        }
+        float term = __builtin_nanf("");
+        if (i >= 0 && i < a.n1 && j >= 0 && j < a.n2) {
+            const T* x = static_cast<const T*>(a.amap) + pair * a.a_pair_elems + (int64_t)i * a.d;
+            const T* y = static_cast<const T*>(a.bmap) + pair * a.b_pair_elems + (int64_t)j * a.d;
+            float pos = 0.0f;
+            for (int c = 0; c < a.d; ++c) pos = __builtin_fmaf(elem_f32(x[c]), elem_f32(y[c]), pos);
+            term = 0.69314718055994531f * __builtin_fmaf(-pos, a.k2, m) + logf(S);
+        }
+        a.terms[pt] = term;
+        contrib = term;
+    }
+    red[threadIdx.x] = contrib;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) a.block_sums[(int64_t)pair * a.nblk + blockIdx.x] = red[0];
+}
+
+// loss[pair] = sum of the pair's block sums (fixed order: strided, then a tree).
+__global__ __launch_bounds__(256) void nce_loss_kernel(NceArgs a) {
+    __shared__ double red[256];
+    const int pair = blockIdx.x;
+    double s = 0.0;
+    for (int k = threadIdx.x; k < a.nblk; k += 256) s += a.block_sums[(int64_t)pair * a.nblk + k];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) a.loss[pair] = red[0];
+}
+
 // ---------------------------------------------------------------------------- host helpers
 
 struct Profiler {
@@ -1388,14 +1595,9 @@ int grid_1d(int64_t n, int threads = 256, int cap = 1 << 24) {
 
 int dev_err() { return hipGetLastError() == hipSuccess ? MR_OK : MR_ERR_DEVICE; }
 
-// Workgroups per pair: as many as the GPU holds at once (all pairs together); a
-// multiple of 8 when large, so that work items keep to one XCD's share of the
-// database rows.
-// Workgroups per pair: as many as the GPU holds at once (all pairs together); a
-// multiple of 8 when large, so that work items keep to one XCD's share of the
-// database rows.
-template <int AR, int P>
-int nn_grid_x(int batch) {
+// Workgroups of kernel K (kThreads each) that the GPU holds at once.
+template <auto K>
+int resident_blocks() {
     static int resident = 0;
     if (resident == 0) {
         int dev = 0, cus = 256, per_cu = 0;
@@ -1403,14 +1605,25 @@ int nn_grid_x(int batch) {
             hipDeviceProp_t prop;
             if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
         }
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, nn_argmax_kernel<AR, P>, kThreads, 0) !=
-                hipSuccess || per_cu < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, kThreads, 0) != hipSuccess || per_cu < 1)
             per_cu = 1;
         resident = cus * per_cu;
     }
+    return resident;
+}
+
+// Workgroups per pair: as many as the GPU holds at once (all pairs together); a
+// multiple of 8 when large, so that work items keep to one XCD's share of the
+// database rows.
+inline int grid_per_pair(int resident, int batch) {
     int g = resident / (batch > 0 ? batch : 1);
     if (g >= 64) g &= ~7;
     return g < 1 ? 1 : g;
+}
+
+template <int AR, int P>
+int nn_grid_x(int batch) {
+    return grid_per_pair(resident_blocks<nn_argmax_kernel<AR, P>>(), batch);
 }
 
 template <int AR, int P>
@@ -1481,21 +1694,8 @@ enum Metric { M_INNER = 0, M_POINT = 1 };
 
 template <int D>
 void launch_point_t(const NNArgs& a, int batch, hipStream_t st) {
-    static int resident = 0;
-    if (resident == 0) {
-        int dev = 0, cus = 256, per_cu = 0;
-        if (hipGetDevice(&dev) == hipSuccess) {
-            hipDeviceProp_t prop;
-            if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
-        }
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, point_nn_kernel<D>, kThreads, 0) != hipSuccess ||
-            per_cu < 1)
-            per_cu = 1;
-        resident = cus * per_cu;
-    }
-    int g = resident / (batch > 0 ? batch : 1);
-    if (g >= 64) g &= ~7;
-    hipLaunchKernelGGL((point_nn_kernel<D>), dim3(g < 1 ? 1 : g, batch), dim3(kThreads), 0, st, a);
+    const int g = grid_per_pair(resident_blocks<point_nn_kernel<D>>(), batch);
+    hipLaunchKernelGGL((point_nn_kernel<D>), dim3(g, batch), dim3(kThreads), 0, st, a);
 }
 
 // One NN search under a metric (the similarity kernel of every entry point).
@@ -1766,6 +1966,129 @@ int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, 
     return dev_err();
 }
 
+
+// ---------------------------------------------------------------------------- matching loss (host)
+
+// The kernel instance for a map dtype and d: bf16 maps on the bf16 products, fp32
+// maps on the exact three-way split (d a multiple of 8, at most 32).  f receives
+// the arithmetic and the step count as integral constants.
+template <class F>
+int with_lse_arith(int dtype, int d, F&& f) {
+    using std::integral_constant;
+    if (dtype == MR_BF16) {
+        switch ((d + 15) / 16) {
+            case 1: return f(integral_constant<int, AR_BF16>{}, integral_constant<int, 1>{});
+            case 2: return f(integral_constant<int, AR_BF16>{}, integral_constant<int, 2>{});
+            case 3: return f(integral_constant<int, AR_BF16>{}, integral_constant<int, 3>{});
+            case 4: return f(integral_constant<int, AR_BF16>{}, integral_constant<int, 4>{});
+            default: return MR_ERR_SHAPE;
+        }
+    }
+    switch (d) {
+        case 8: return f(integral_constant<int, AR_X3>{}, integral_constant<int, 3>{});
+        case 16: return f(integral_constant<int, AR_X3>{}, integral_constant<int, 6>{});
+        case 24: return f(integral_constant<int, AR_X3>{}, integral_constant<int, 9>{});
+        case 32: return f(integral_constant<int, AR_X3>{}, integral_constant<int, 12>{});
+        default: return MR_ERR_SHAPE;
+    }
+}
+
+struct NceLayout {
+    int grid = 0, nseg = 0, nblk = 0;
+    size_t partial = 0, sums = 0, total = 0;
+};
+
+// Launch shape and workspace of the matching loss: segments per query group as
+// for the NN search (the resident workgroups spread over the query groups, a
+// multiple of 8 when large, at most one per database tile).
+int nce_layout(const mr_map* a, const mr_map* b, int64_t n_gt, NceLayout& L) {
+    return with_lse_arith(a->dtype, a->d, [&](auto ar, auto p) {
+        constexpr int AR = decltype(ar)::value, P = decltype(p)::value;
+        constexpr int QT = qt_of<AR, P>();
+        const int g = grid_per_pair(resident_blocks<lse_partial_kernel<AR, P>>(), a->batch);
+        const int64_t ntiles = (npix(b) + 31) / 32;
+        const int64_t qgroups = ((n_gt + 31) / 32 + kWaves * QT - 1) / (kWaves * QT);
+        int64_t nseg = qgroups > 0 ? g / qgroups : 1;
+        const int64_t cap = ntiles < kMaxSegGroups ? ntiles : kMaxSegGroups;
+        nseg = nseg < 1 ? 1 : (nseg > cap ? cap : nseg);
+        if (nseg >= 8) nseg &= ~int64_t(7);
+        L.nseg = (int)nseg;
+        L.grid = (int)(qgroups * nseg < g ? qgroups * nseg : g);
+        L.nblk = (int)((n_gt + 255) / 256);
+        size_t off = 0;
+        const size_t rows = (size_t)a->batch * (size_t)(n_gt > 0 ? n_gt : 1);
+        L.partial = off; off = align256(off + rows * (size_t)nseg * sizeof(float2));
+        L.sums = off; off = align256(off + (size_t)a->batch * (size_t)(L.nblk > 0 ? L.nblk : 1) * sizeof(double));
+        L.total = off;
+        return (int)MR_OK;
+    });
+}
+
+int validate_nce(const mr_map* a, const mr_map* b, int64_t n_gt) {
+    const int rc = validate_pair(a, b);
+    if (rc) return rc;
+    if (n_gt < 0 || n_gt > (int64_t(1) << 28)) return MR_ERR_PARAM;
+    if (npix(b) == 0) return MR_ERR_SHAPE;   // the softmax needs at least one row
+    if (a->dtype == MR_F32 && (a->d % 8 != 0 || a->d > 32)) return MR_ERR_SHAPE;
+    return MR_OK;
+}
+
+int infonce_impl(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau, float* out_terms,
+                 double* out_loss, void* ws, size_t ws_bytes, void* stream) {
+    int rc = validate_nce(a, b, n_gt);
+    if (rc) return rc;
+    if (!(tau > 0.0f) || !(tau < INFINITY)) return MR_ERR_PARAM;
+    if (!out_loss) return MR_ERR_NULL;
+    if (n_gt > 0 && (!gt || !out_terms)) return MR_ERR_NULL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int batch = a->batch;
+    if (n_gt == 0) {
+        hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(batch)), dim3(256), 0, st,
+                           reinterpret_cast<uint64_t*>(out_loss), (int64_t)batch, (uint64_t)0);   // +0.0
+        return dev_err();
+    }
+    NceLayout L;
+    if ((rc = nce_layout(a, b, n_gt, L))) return rc;
+    if ((rc = check_ws(ws, ws_bytes, L.total))) return rc;
+    NceArgs x;
+    memset(&x, 0, sizeof(x));
+    x.amap = a->data;
+    x.bmap = b->data;
+    x.a_pair_elems = npix(a) * a->d;
+    x.b_pair_elems = npix(b) * b->d;
+    x.n1 = (int32_t)npix(a);
+    x.n2 = (int32_t)npix(b);
+    x.d = a->d;
+    x.gt = gt;
+    x.n_gt = (int32_t)n_gt;
+    x.nseg = L.nseg;
+    x.nblk = L.nblk;
+    x.k2 = (float)(1.4426950408889634 / (double)tau);
+    x.partial = at<float2>(ws, L.partial);
+    x.terms = out_terms;
+    x.block_sums = at<double>(ws, L.sums);
+    x.loss = out_loss;
+    const bool prof = g_prof.on && g_prof.used < g_prof.cap;
+    if (prof && hipEventRecord(g_prof.ev[2 * g_prof.used], st) != hipSuccess) return MR_ERR_DEVICE;
+    rc = with_lse_arith(a->dtype, a->d, [&](auto ar, auto p) {
+        constexpr int AR = decltype(ar)::value, P = decltype(p)::value;
+        hipLaunchKernelGGL((lse_partial_kernel<AR, P>), dim3(L.grid, batch), dim3(kThreads), 0, st, x);
+        return dev_err();
+    });
+    if (rc) return rc;
+    if (prof) {
+        if (hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st) != hipSuccess) return MR_ERR_DEVICE;
+        ++g_prof.used;
+    }
+    if (a->dtype == MR_BF16)
+        hipLaunchKernelGGL(nce_terms_kernel<uint16_t>, dim3(L.nblk, batch), dim3(256), 0, st, x);
+    else
+        hipLaunchKernelGGL(nce_terms_kernel<float>, dim3(L.nblk, batch), dim3(256), 0, st, x);
+    if (dev_err()) return MR_ERR_DEVICE;
+    hipLaunchKernelGGL(nce_loss_kernel, dim3(batch), dim3(256), 0, st, x);
+    return dev_err();
+}
+
 }  // namespace
 
 // ============================================================================ C ABI
@@ -1811,8 +2134,18 @@ size_t mr_workspace_bytes(int op, const mr_map* a, const mr_map* b, int64_t n_q,
             if (ns < 0) return 0;
             return fast_layout(a, b, ns).total;
         }
+        case MR_OP_INFONCE: {
+            NceLayout L;
+            if (validate_nce(a, b, n_q) != MR_OK || nce_layout(a, b, n_q, L) != MR_OK) return 0;
+            return L.total;
+        }
         default: return 0;
     }
+}
+
+int mr_infonce_forward(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau,
+                       float* out_terms, double* out_loss, void* ws, size_t ws_bytes, void* stream) {
+    return infonce_impl(a, b, gt, n_gt, tau, out_terms, out_loss, ws, ws_bytes, stream);
 }
 
 int mr_nn_argmax(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q, int32_t* out_idx,

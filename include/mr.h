@@ -78,7 +78,8 @@ typedef struct {
 enum {
     MR_OP_NN_ARGMAX = 0, MR_OP_MUTUAL_NN = 1, MR_OP_FAST_RECIPROCAL = 2,
     MR_OP_POINT_NN = 3, MR_OP_POINT_MUTUAL_NN = 4, MR_OP_POINT_FAST_RECIPROCAL = 5,
-    MR_OP_FAST_RECIPROCAL_GRAPH = 6   /* a = b = the image collection, n_q = number of edges */
+    MR_OP_FAST_RECIPROCAL_GRAPH = 6,  /* a = b = the image collection, n_q = number of edges */
+    MR_OP_INFONCE = 7                 /* n_q = ground-truth pairs per image pair */
 };
 
 /* Workspace bytes that entry point `op` needs for these maps and parameters
@@ -191,6 +192,33 @@ int mr_point_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t
 int mr_point_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset,
                              int32_t max_iters, int32_t* pairs, int64_t cap, int64_t* n_pairs,
                              int32_t* iter_active, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mr_infonce_forward: the matching loss of a descriptor pair over its
+ * ground-truth correspondences ("MASt3R dissection", section 3 "Napkin
+ * Formula": the InfoNCE objective with temperature tau, negatives taken from
+ * every pixel of the second image).  For ground-truth pair t = (i, j):
+ *     term[t] = log sum_k exp(<a_i, b_k> / tau) - <a_i, b_j> / tau,
+ * k over all rows of b; loss = sum_t term[t] (a sum, not a mean).
+ * Scores use the similarity kernel's arithmetic (see the top of this file);
+ * the log-sum-exp is accumulated online in fp32 with the largest score as its
+ * shift, so no exponential overflows for any finite input; the positive score
+ * is an fp32 dot product in component order.
+ *   a, b     : maps of equal batch, d and dtype; b has at least one row (else
+ *              MR_ERR_SHAPE).  bf16 maps: any supported d; fp32 maps: d in
+ *              {8, 16, 24, 32} (else MR_ERR_SHAPE).
+ *   gt       : DEVICE int32 [batch][n_gt][2] rows (i in a, j in b) of each
+ *              pair; an out-of-range pair is not an error: its term is NaN
+ *              (and so is that pair's loss).  0 <= n_gt <= 2^28.
+ *   tau      : > 0 and finite (else MR_ERR_PARAM).
+ *   out_terms: [batch][n_gt] fp32 (may be NULL only when n_gt = 0).
+ *   out_loss : [batch] binary64: per image pair, the terms added in binary64
+ *              in a fixed order (deterministic); 0 when n_gt = 0.
+ *   ws       : mr_workspace_bytes(MR_OP_INFONCE, a, b, n_gt, 0, 0) bytes
+ *              (unused when n_gt = 0).
+ * --------------------------------------------------------------------------- */
+int mr_infonce_forward(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau,
+                       float* out_terms, double* out_loss, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Measurement aid (not thread-safe; one profiling window per process).

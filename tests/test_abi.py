@@ -138,7 +138,7 @@ def test_mutual_and_nn_validation(lib):
     assert lib.mr_nn_argmax(R(a), R(b), None, 0, None, None, None, 0, None) == PARAM
     empty = M(0, 5, data=None)
     assert lib.mr_nn_argmax(R(empty), R(b), out, 3, out, None, out, 1 << 20, None) == SHAPE
-    assert lib.mr_workspace_bytes(7, R(a), R(b), 0, 1, 0) == 0
+    assert lib.mr_workspace_bytes(99, R(a), R(b), 0, 1, 0) == 0
 
 
 def test_profile_end_without_begin(lib):
@@ -192,3 +192,29 @@ def test_graph_validation(lib):
     assert call(E, 3, wsb=need - 1) == WS
     assert call(E, 3, cap=0) == CAP
 
+
+
+def test_infonce_validation(lib):
+    """The matching loss rejects a bad temperature, count, pointer, shape or workspace
+    before anything runs."""
+    out = ctypes.c_void_p(FAKE)
+    a, b = M(10, 10), M(7, 9)
+    need = lib.mr_workspace_bytes(7, R(a), R(b), 50, 0, 0)
+    assert need > 0 and lib.mr_workspace_bytes(7, R(a), R(b), 5000, 0, 0) >= need
+    assert lib.mr_workspace_bytes(7, R(M(10, 10, d=20)), R(M(7, 9, d=20)), 50, 0, 0) == 0
+    assert lib.mr_workspace_bytes(7, R(M(10, 10, d=40, dtype=1)), R(M(7, 9, d=40, dtype=1)), 50, 0, 0) > 0
+    assert lib.mr_workspace_bytes(7, R(a), R(b), -1, 0, 0) == 0
+    ws = ctypes.c_void_p(FAKE)
+    call = lambda a_=a, b_=b, gt=out, n=50, tau=0.1, terms=out, loss=out, wsb=need: lib.mr_infonce_forward(
+        R(a_), R(b_), gt, n, tau, terms, loss, ws, wsb, None)
+    for tau in (0.0, -0.1, float("inf"), float("nan")):
+        assert call(tau=tau) == PARAM
+    assert call(n=-1) == PARAM
+    assert call(n=(1 << 28) + 1) == PARAM
+    assert call(gt=None) == NULL
+    assert call(terms=None) == NULL
+    assert call(loss=None) == NULL
+    assert call(a_=M(10, 10, d=20), b_=M(7, 9, d=20)) == SHAPE
+    assert call(b_=M(0, 9, data=None)) == SHAPE
+    assert call(b_=M(7, 9, d=24, dtype=1)) == DTYPE
+    assert call(wsb=need - 1) == WS

@@ -312,6 +312,14 @@ def config_pair(cfg: int, b: int = 0, d: int = D_DEFAULT) -> Pair:
                      dtype=c["dtype"], name=c["name"], stride=c["stride"], max_iters=c["max_iters"])
 
 
+def gt_pairs(p: Pair) -> np.ndarray:
+    """Ground-truth correspondences of a planted pair: (src[j], j) for every pixel j of
+    image 2 that is not occluded, int32 [n_gt, 2] ascending in j (several j may share
+    one source pixel)."""
+    j = np.nonzero(p.src >= 0)[0]
+    return np.stack([p.src[j], j], axis=1).astype(np.int32)
+
+
 def stack_pairs(pairs):
     """Stack pairs into [B, N, d] fp32 arrays (and bf16 bits if any)."""
     D1 = np.stack([p.D1 for p in pairs])
