@@ -31,6 +31,9 @@ PEAK_VALU_TOPS = 157.3 / 2
 # multiply and 2 fused multiply-adds for the squared distance, and half of a 3-input
 # minimum for the selection.
 POINT_OPS_PER_PAIR = 6.5
+# Transcendental (v_exp_f32) lane-operations per second: a quarter of the plain VALU
+# lane-operation rate.
+PEAK_EXP_TOPS = PEAK_VALU_TOPS / 4
 
 
 def parse():
@@ -95,6 +98,34 @@ def time_steps(fn, steps, warmup, torch, prof_launches=0):
         torch.cuda.synchronize()
         kms, kn = mr.profile_end()
     return ms, kms, kn
+
+
+def step_percentiles(fn, steps, torch):
+    """Per-step times (one hipEvent pair around each call, nothing else on the stream):
+    p10, median and p90 in ms over `steps` calls."""
+    import numpy as np
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return [round(float(x), 4) for x in np.percentile(t, [10, 50, 90])]
+
+
+def oracle_host():
+    """CPU model string and the core count the host shows."""
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cpu, os.cpu_count() or 0
 
 
 def fast_work(active, N, d):
@@ -178,26 +209,63 @@ def roofline_alu(pairs_per_step, steps, kernel_ms, launches):
             "ops_per_launch": per_launch, "ops_per_pair": POINT_OPS_PER_PAIR}
 
 
+def roofline_lse(scores_per_step, d, steps, kernel_ms, launches):
+    """The matching loss's log-sum-exp kernel: one exponential per score on the VALU's
+    transcendental unit, next to 2*d flops per score on the bf16 matrix cores."""
+    if not launches:
+        return None
+    per_launch = scores_per_step * steps / launches
+    avg_ms = kernel_ms / launches
+    exps = per_launch / (avg_ms * 1e-3) / 1e12
+    flops = 2.0 * d * exps
+    return {"bound": "alu", "achieved": round(exps, 3), "peak": round(PEAK_EXP_TOPS, 2),
+            "unit": "T exp/s", "frac": round(exps / PEAK_EXP_TOPS, 4), "traffic": None,
+            "kernel": "lse_partial_kernel", "avg_launch_us": round(avg_ms * 1e3, 2),
+            "scores_per_launch": per_launch,
+            "mfma": {"achieved_TFLOPs": round(flops, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "frac": round(flops / PEAK_TFLOPS["bf16"], 4)}}
+
+
 def cpu_baseline(p):
     import oracle
     threads = oracle.default_threads()
     t = time.perf_counter()
     r = oracle.fast(p.D1, p.H, p.W, p.D2, p.stride, p.offset, p.max_iters, nthreads=threads)
     dt = time.perf_counter() - t
-    cpu = platform.processor() or platform.machine()
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
+    cpu, ncpu = oracle_host()
     return {"value": round(1.0 / dt, 4), "unit": "pairs/s", "cores": threads, "kind": "oracle",
             "sample": "the whole 512x384 pair (3072 seeds, 10 iterations), binary64 C oracle, %d threads, "
-                      "%.2f s, %d NN queries, CPU %s, nproc %d" % (threads, dt, r["nn_queries"], cpu,
-                                                                   os.cpu_count() or 0),
+                      "%.2f s, %d NN queries, CPU %s, nproc %d" % (threads, dt, r["nn_queries"], cpu, ncpu),
             "nn_queries_per_s": round(r["nn_queries"] / dt, 1), "matches": int(len(r["pairs"]))}
+
+
+def cpu_samples():
+    """The oracle on bounded samples of two of the other workloads (brute-force bf16
+    mutual NN, the matching loss), with the full-size time extrapolated from them."""
+    import numpy as np
+    import oracle
+    import workloads
+    threads = oracle.default_threads()
+    out = {}
+    p2 = workloads.config_pair(2)
+    rows = np.sort(np.random.default_rng(2).choice(p2.N, 4096, replace=False)).astype(np.int32)
+    t = time.perf_counter()
+    oracle.nn_rows(p2.D1, rows, p2.D2, nthreads=threads)
+    oracle.nn_rows(p2.D2, rows, p2.D1, nthreads=threads)
+    dt = time.perf_counter() - t
+    out["pair-512x384-bf16-bruteforce"] = {
+        "sample": "4096 + 4096 query rows (both directions)", "seconds": round(dt, 3), "threads": threads,
+        "nn_queries_per_s": round(8192 / dt, 1),
+        "full_call_seconds_extrapolated": round(dt * p2.N / 4096, 1)}
+    g = workloads.gt_pairs(p2)
+    pick = np.sort(np.random.default_rng(3).choice(len(g), 1024, replace=False))
+    t = time.perf_counter()
+    oracle.infonce(p2.D1, p2.D2, g[pick], float(np.float32(0.1)), nthreads=threads)
+    dt = time.perf_counter() - t
+    out["infonce-512x384-bf16"] = {
+        "sample": "1024 of the 137626 ground-truth terms", "seconds": round(dt, 3), "threads": threads,
+        "terms_per_s": round(1024 / dt, 1), "full_loss_seconds_extrapolated": round(dt * len(g) / 1024, 1)}
+    return out
 
 
 def other_batch64(args, torch, dev):
@@ -235,10 +303,11 @@ def other_bruteforce(args, torch, dev):
     steps = max(3, args.steps // 4)
     ms, kms, kn = time_steps(lambda: mr.mutual_nn(A2, B2, ws=ws), steps, 2, torch, 2 * steps)
     fl = 2.0 * 2 * p2.N * p2.N * p2.d   # both directions are computed
-    return {"pairs_per_s": round(1000.0 / ms, 2), "ms_per_call": round(ms, 3),
-            "nn_queries_per_s": round(2 * p2.N * 1000.0 / ms, 1),
-            "mfma_frac_algorithmic": round(2.0 * p2.N * p2.N * p2.d / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
-            "roofline": roofline(fl, steps, kms, kn, "bf16")}
+    out = {"pairs_per_s": round(1000.0 / ms, 2), "ms_per_call": round(ms, 3),
+           "nn_queries_per_s": round(2 * p2.N * 1000.0 / ms, 1),
+           "mfma_frac_algorithmic": round(2.0 * p2.N * p2.N * p2.d / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+           "roofline": roofline(fl, steps, kms, kn, "bf16")}
+    return out
 
 
 def point_maps(p, torch, dev):
@@ -296,10 +365,30 @@ def other_graph(args, torch, dev):
             "roofline": roofline(flops, steps, kms, kn, "f32")}
 
 
+def other_infonce(args, torch, dev):
+    """Matching loss (InfoNCE forward, tau = 0.1) of the 512x384 bf16 planted pair over its
+    ground-truth correspondences (every non-occluded pixel of image 2: 137626 terms, each a
+    log-sum-exp over all 196608 pixels of image 2)."""
+    import dense_grounded_image_amd as mr
+    import workloads
+    p = workloads.config_pair(2)
+    A, B = dev_maps(p, torch, dev)
+    gt = torch.from_numpy(workloads.gt_pairs(p)).to(dev).unsqueeze(0)
+    n_gt = int(gt.shape[1])
+    f = mr.InfoNCE(A, B, n_gt, 0.1)
+    steps = max(3, args.steps // 4)
+    ms, kms, kn = time_steps(lambda: f(A, B, gt), steps, 2, torch, steps)
+    scores = n_gt * p.N
+    out = {"loss_evals_per_s": round(1000.0 / ms, 2), "ms_per_call": round(ms, 3), "n_gt": n_gt,
+           "scores_per_s": round(scores * 1000.0 / ms, 1), "loss": float(f.loss[0].cpu()),
+           "roofline": roofline_lse(scores, p.d, steps, kms, kn)}
+    return out
+
+
 OTHER = {"batch64-512x384-f32": other_batch64, "pair-1024x768-bf16": other_bf16_1024,
          "graph-50x512x384-f32": other_graph,
          "pointmaps-512x384-f32": other_points_fast, "pointmaps-512x384-f32-bruteforce": other_points_bruteforce,
-         "pair-512x384-bf16-bruteforce": other_bruteforce}
+         "pair-512x384-bf16-bruteforce": other_bruteforce, "infonce-512x384-bf16": other_infonce}
 
 
 def main():
@@ -338,6 +427,9 @@ def main():
                              measured_traffic("nn_argmax_pair512x384_f32_traffic.json")),
         "step_mfma_frac": round(r["flops"] / (r["ms"] * 1e-3) / 1e12 / PEAK_TFLOPS["f32"], 4),
     }
+    f1 = mr.FastReciprocal(*dev_maps(p, torch, dev), p.stride, p.offset, p.max_iters)
+    A1, B1 = dev_maps(p, torch, dev)
+    out["step_ms_p10_p50_p90"] = step_percentiles(lambda: f1(A1, B1), max(args.steps, 20), torch)
     print("bench: fast pair %.4f ms/step" % r["ms"], file=sys.stderr, flush=True)
 
     if not args.main_only:
@@ -346,6 +438,8 @@ def main():
     if not args.no_cpu:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(p)
+        if not args.main_only:
+            out["cpu_baseline"]["other_samples"] = cpu_samples()
     print(json.dumps(out), flush=True)
 
 

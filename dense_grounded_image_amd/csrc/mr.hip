@@ -1467,7 +1467,15 @@ void lse_partial_kernel(NceArgs a) {
         const int t0 = (int)((int64_t)sg * ntiles / nsg);
         const int t1 = (int)((int64_t)(sg + 1) * ntiles / nsg);
         LseSum<QT> ep(a.k2);
-        stream_db<AR, P>(dbytes, rb, t0, t1, a.n2, lds, q, nact, h, jl, a.d, 2, ep);
+        bool direct = false;
+        if constexpr (AR == AR_BF16) direct = g1 - g0 == kWaves * QT && (int64_t)t1 * 32 <= a.n2;
+        // full bf16 items stream without LDS (the choice is uniform over the workgroup,
+        // whose staged path has barriers)
+        if (direct) {
+            if constexpr (AR == AR_BF16) stream_regs<AR, P, 4>(dbytes, t0, t1, q, h, jl, a.d, ep);
+        } else {
+            stream_db<AR, P>(dbytes, rb, t0, t1, a.n2, lds, q, nact, h, jl, a.d, 2, ep);
+        }
         // merge the two lane halves (disjoint rows of the same query)
 #pragma unroll
         for (int j = 0; j < QT; ++j) {

@@ -150,6 +150,25 @@ def test_point_fast_full_size():
     log("point fast 512x384", rep, act[0].cpu().tolist())
 
 
+def test_point_mutual_full_size_sampled():
+    """512x384 pointmaps, full 196608^2 brute force in both directions (the bench's
+    launch shape); the oracle checks 2048 random rows of each direction."""
+    p = workloads.make_pointmaps(512, 384, seed=11)
+    pairs, n, nn_ab, nn_ba = mr.point_mutual_nn(dev(p.D1, p.H, p.W), dev(p.D2, p.H, p.W))
+    torch.cuda.synchronize()
+    g12, g21 = nn_ab[0].cpu().numpy(), nn_ba[0].cpu().numpy()
+    rng = np.random.default_rng(12)
+    rows = np.sort(rng.choice(p.N, 2048, replace=False)).astype(np.int32)
+    oi, o1, o2 = oracle.nn_rows(p.D1, rows, p.D2, metric=PT)
+    r1 = checks.check_nn(g12[rows], oi, o1, o2, p.D1, rows, p.D2, "f32", metric=PT)
+    oj, q1, q2 = oracle.nn_rows(p.D2, rows, p.D1, metric=PT)
+    r2 = checks.check_nn(g21[rows], oj, q1, q2, p.D2, rows, p.D1, "f32", metric=PT)
+    gp = mr.matches(pairs, n)
+    i = np.nonzero(g21[g12] == np.arange(p.N))[0]
+    assert (gp[:, 0] == i).all() and (gp[:, 1] == g12[i]).all()
+    log("point mutual 512x384", r1, r2, len(gp))
+
+
 def test_point_edges():
     """T = 0 gives nothing; a 1x1 image; a stride beyond the image leaves one seed."""
     p = workloads.make_pointmaps(12, 9, seed=760, warp="shift", sigma=0.01, rho=0.2)
