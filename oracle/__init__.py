@@ -62,6 +62,8 @@ def _bind(lib):
     lib.orc_fast_metric.restype = ctypes.c_int
     lib.orc_infonce.argtypes = [P, i64, P, i64, i32, P, i64, f64, i32, P, P]
     lib.orc_infonce.restype = ctypes.c_int
+    lib.orc_infonce_grad.argtypes = [P, i64, P, i64, i32, P, i64, f64, P, i64, i32, P, P, P]
+    lib.orc_infonce_grad.restype = ctypes.c_int
     return lib
 
 
@@ -204,6 +206,26 @@ class Oracle:
         return terms, total.value
 
 
+    def infonce_grad(self, A, B, gt, tau, b_rows=None, nthreads=None):
+        """Gradient of the summed matching loss: (dA float64 [n1, d], dB float64 [len(b_rows), d],
+        colmass float64 [len(b_rows)] = sum_t softmax_t[k]) for the listed rows k of B (all
+        rows when b_rows is None)."""
+        lib = self.lib
+        A, B = _f32(A), _f32(B)
+        gt = np.ascontiguousarray(np.asarray(gt, dtype=np.int32).reshape(-1, 2))
+        rows = np.arange(B.shape[0], dtype=np.int32) if b_rows is None else \
+            np.ascontiguousarray(b_rows, dtype=np.int32)
+        d = A.shape[1]
+        dA = np.empty((A.shape[0], d), np.float64)
+        dB = np.empty((max(1, rows.shape[0]), d), np.float64)
+        mass = np.empty(max(1, rows.shape[0]), np.float64)
+        rc = lib.orc_infonce_grad(_ptr(A), A.shape[0], _ptr(B), B.shape[0], d, _ptr(gt), gt.shape[0], float(tau),
+                                  _ptr(rows), rows.shape[0], nthreads or default_threads(), _ptr(dA), _ptr(dB),
+                                  _ptr(mass))
+        assert rc == 0, rc
+        return dA, dB[:rows.shape[0]], mass[:rows.shape[0]]
+
+
 _default = Oracle()
 nn = _default.nn
 nn_rows = _default.nn_rows
@@ -212,3 +234,4 @@ mutual = _default.mutual
 mutual_nn = _default.mutual_nn
 fast = _default.fast
 infonce = _default.infonce
+infonce_grad = _default.infonce_grad

@@ -479,3 +479,123 @@ int orc_infonce(const float* A, int64_t n1, const float* B, int64_t n2, int32_t 
     *out_total = total;
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------
+ * Gradient of the matching loss L = sum_t term_t (orc_infonce) with respect to
+ * both descriptor maps.  The derivative of a log-sum-exp is the softmax, so with
+ *     p[t][k] = exp(<D1[i_t], D2[k]> / tau - LSE_t)
+ * (term t's softmax over the rows k of image 2),
+ *     dL/dD1[i] = (1/tau) sum_{t: i_t = i} ( sum_k p[t][k] D2[k] - D2[j_t] ),
+ *     dL/dD2[k] = (1/tau) sum_t p[t][k] D1[i_t] - (1/tau) sum_{t: j_t = k} D1[i_t].
+ * Steps, in binary64: (1) LSE_t for every t, as orc_infonce does (threads over
+ * t); (2) for every t the vector sum_k p[t][k] D2[k] - D2[j_t] (threads over t);
+ * (3) dA[i] = sum of those vectors over t with i_t = i, ascending t, times 1/tau;
+ * (4) for every listed row k of image 2 (threads over the list): dB = the sum over
+ * t ascending of p[t][k] D1[i_t], minus D1[i_t] for each t with j_t = k, times
+ * 1/tau, and colmass = sum_t p[t][k] (the scale of that row's gradient).
+ * dA: [n1][d], fully written; dB, colmass: one row per entry of b_rows.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    const float* A; const float* B; int64_t n2; int d; double tau; const int32_t* gt; int64_t n_gt;
+    double* lse; double* g; const int32_t* rows; double* dB; double* colmass; int64_t begin, end;
+} orc_grad_job;
+
+static void* orc_grad_rows_worker(void* p)
+{
+    orc_grad_job* j = (orc_grad_job*)p;
+    const int d = j->d;
+    for (int64_t t = j->begin; t < j->end; ++t) {
+        const float* q = j->A + (int64_t)j->gt[2 * t] * d;
+        double m = -INFINITY;
+        for (int64_t k = 0; k < j->n2; ++k) {
+            const double z = orc_similarity(q, j->B + k * (int64_t)d, d) / j->tau;
+            if (z > m) m = z;
+        }
+        double sum = 0.0;
+        for (int64_t k = 0; k < j->n2; ++k) sum += exp(orc_similarity(q, j->B + k * (int64_t)d, d) / j->tau - m);
+        const double lse = m + log(sum);
+        j->lse[t] = lse;
+        double* g = j->g + t * (int64_t)d;
+        for (int e = 0; e < d; ++e) g[e] = 0.0;
+        for (int64_t k = 0; k < j->n2; ++k) {
+            const double pk = exp(orc_similarity(q, j->B + k * (int64_t)d, d) / j->tau - lse);
+            for (int e = 0; e < d; ++e) g[e] += pk * (double)j->B[k * (int64_t)d + e];
+        }
+        const float* bj = j->B + (int64_t)j->gt[2 * t + 1] * d;
+        for (int e = 0; e < d; ++e) g[e] -= (double)bj[e];
+    }
+    return NULL;
+}
+
+static void* orc_grad_cols_worker(void* p)
+{
+    orc_grad_job* j = (orc_grad_job*)p;
+    const int d = j->d;
+    for (int64_t r = j->begin; r < j->end; ++r) {
+        const int64_t k = j->rows[r];
+        const float* bk = j->B + k * d;
+        double* out = j->dB + r * (int64_t)d;
+        double mass = 0.0;
+        for (int e = 0; e < d; ++e) out[e] = 0.0;
+        for (int64_t t = 0; t < j->n_gt; ++t) {
+            const float* a = j->A + (int64_t)j->gt[2 * t] * d;
+            const double pk = exp(orc_similarity(a, bk, d) / j->tau - j->lse[t]);
+            mass += pk;
+            for (int e = 0; e < d; ++e) out[e] += pk * (double)a[e];
+            if (j->gt[2 * t + 1] == k)
+                for (int e = 0; e < d; ++e) out[e] -= (double)a[e];
+        }
+        for (int e = 0; e < d; ++e) out[e] /= j->tau;
+        j->colmass[r] = mass;
+    }
+    return NULL;
+}
+
+static void orc_run_jobs(orc_grad_job* jobs, int n, void* (*fn)(void*))
+{
+    pthread_t th[256];
+    int started[256];
+    for (int i = 1; i < n; ++i) started[i] = pthread_create(&th[i], NULL, fn, &jobs[i]) == 0;
+    if (n > 0) fn(&jobs[0]);
+    for (int i = 1; i < n; ++i) {
+        if (started[i]) pthread_join(th[i], NULL);
+        else fn(&jobs[i]);
+    }
+}
+
+int orc_infonce_grad(const float* A, int64_t n1, const float* B, int64_t n2, int32_t d, const int32_t* gt,
+                     int64_t n_gt, double tau, const int32_t* b_rows, int64_t n_rows, int32_t nthreads,
+                     double* dA, double* dB, double* colmass)
+{
+    if (!A || !B || !gt || !dA || n1 < 0 || n2 < 1 || d < 1 || n_gt < 0 || !(tau > 0) || n_rows < 0 ||
+        (n_rows > 0 && (!b_rows || !dB || !colmass)))
+        return ORC_ERR_ARG;
+    for (int64_t t = 0; t < n_gt; ++t)
+        if (gt[2 * t] < 0 || gt[2 * t] >= n1 || gt[2 * t + 1] < 0 || gt[2 * t + 1] >= n2) return ORC_ERR_ARG;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (b_rows[r] < 0 || b_rows[r] >= n2) return ORC_ERR_ARG;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    double* lse = (double*)malloc(sizeof(double) * (size_t)(n_gt > 0 ? n_gt : 1));
+    double* g = (double*)malloc(sizeof(double) * (size_t)(n_gt > 0 ? n_gt : 1) * (size_t)d);
+    if (!lse || !g) { free(lse); free(g); return ORC_ERR_NOMEM; }
+    orc_grad_job jobs[256];
+    int nt = n_gt > 0 && nthreads > n_gt ? (int)n_gt : nthreads;
+    for (int i = 0; i < nt; ++i)
+        jobs[i] = (orc_grad_job){A, B, n2, d, tau, gt, n_gt, lse, g, b_rows, dB, colmass,
+                                 n_gt * i / nt, n_gt * (i + 1) / nt};
+    orc_run_jobs(jobs, nt, orc_grad_rows_worker);
+    for (int64_t x = 0; x < n1 * (int64_t)d; ++x) dA[x] = 0.0;
+    for (int64_t t = 0; t < n_gt; ++t) {
+        double* row = dA + (int64_t)gt[2 * t] * d;
+        for (int e = 0; e < d; ++e) row[e] += g[t * (int64_t)d + e] / tau;
+    }
+    nt = n_rows > 0 && nthreads > n_rows ? (int)n_rows : nthreads;
+    for (int i = 0; i < nt; ++i)
+        jobs[i] = (orc_grad_job){A, B, n2, d, tau, gt, n_gt, lse, g, b_rows, dB, colmass,
+                                 n_rows * i / nt, n_rows * (i + 1) / nt};
+    if (n_rows > 0) orc_run_jobs(jobs, nt, orc_grad_cols_worker);
+    free(lse);
+    free(g);
+    return ORC_OK;
+}

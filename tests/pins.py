@@ -457,6 +457,54 @@ def pin_infonce_scipy(orc):
         assert abs(tot - ref.sum()) < 1e-9 * max(1.0, np.abs(ref).sum())
 
 
+def pin_infonce_grad_finite_differences(orc):
+    """Every component of both gradients against central differences of the oracle's own
+    (pinned) loss: steps of 2^-14 are exact in fp32 for these inputs and the loss is
+    binary64, so the difference quotient errs by about h^2 |L'''| / 6 (below 1e-6 here)."""
+    rng = np.random.default_rng(43)
+    A = _rand_unit(rng, 5, 4).astype(np.float32)
+    B = _rand_unit(rng, 7, 4).astype(np.float32)
+    gt = np.array([[0, 1], [2, 2], [2, 5], [4, 1], [1, 6]], np.int32)   # a repeated i and a repeated j
+    h = 2.0 ** -14
+    for tau in (0.5, 0.1):
+        dA, dB, mass = orc.infonce_grad(A, B, gt, tau)
+        for X, G in ((A, dA), (B, dB)):
+            for r in range(X.shape[0]):
+                for c in range(X.shape[1]):
+                    v = X[r, c]
+                    up, dn = np.float32(v + h), np.float32(v - h)
+                    assert float(up) - float(v) == h and float(v) - float(dn) == h
+                    X[r, c] = up
+                    lp = orc.infonce(A, B, gt, tau)[1]
+                    X[r, c] = dn
+                    lm = orc.infonce(A, B, gt, tau)[1]
+                    X[r, c] = v
+                    fd = (lp - lm) / (2 * h)
+                    assert abs(G[r, c] - fd) < 1e-6 * max(1.0, abs(fd)), (tau, r, c, G[r, c], fd)
+        assert abs(mass.sum() - len(gt)) < 1e-12
+
+
+def pin_infonce_grad_invariants(orc):
+    """Each term's softmax sums to 1, so the image-2 gradient sums to zero over the rows and
+    the column masses add up to the number of terms; scaling either map scales every score
+    alike, so sum(dA * A) = sum(dB * B).  Listed rows of dB equal the full call's rows."""
+    rng = np.random.default_rng(44)
+    A = _rand_unit(rng, 30, 24).astype(np.float32)
+    B = _rand_unit(rng, 40, 24).astype(np.float32)
+    gt = np.stack([rng.integers(0, 30, 50), rng.integers(0, 40, 50)], 1).astype(np.int32)
+    dA, dB, mass = orc.infonce_grad(A, B, gt, 0.1)
+    assert np.abs(dB.sum(axis=0)).max() < 1e-10
+    assert abs(mass.sum() - 50) < 1e-10
+    lhs = float((dA * A.astype(np.float64)).sum())
+    rhs = float((dB * B.astype(np.float64)).sum())
+    assert abs(lhs - rhs) < 1e-9 * max(1.0, abs(lhs))
+    untouched = np.setdiff1d(np.arange(30), gt[:, 0])
+    assert (dA[untouched] == 0).all()
+    rows = np.array([39, 3, 17], np.int32)
+    _, dBr, mr = orc.infonce_grad(A, B, gt, 0.1, b_rows=rows)
+    assert np.abs(dBr - dB[rows]).max() < 1e-12 and np.abs(mr - mass[rows]).max() < 1e-12
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]
 
 

@@ -45,6 +45,12 @@ MUTANTS = {
     "nce_temperature_ignored": ("const double z = orc_similarity(q, j->B + k * (int64_t)j->d, j->d) / j->tau;",
                                 "const double z = orc_similarity(q, j->B + k * (int64_t)j->d, j->d);"),
     "nce_sign_flipped": ("j->terms[t] = m + log(sum) - pos;", "j->terms[t] = pos - m - log(sum);"),
+    # matching-loss gradient
+    "grad_positive_term_dropped": ("for (int e = 0; e < d; ++e) g[e] -= (double)bj[e];", ""),
+    "grad_rows_without_temperature": ("row[e] += g[t * (int64_t)d + e] / tau;", "row[e] += g[t * (int64_t)d + e];"),
+    "grad_cols_match_on_query_index": ("if (j->gt[2 * t + 1] == k)", "if (j->gt[2 * t] == k)"),
+    "grad_cols_softmax_unnormalised": ("const double pk = exp(orc_similarity(a, bk, d) / j->tau - j->lse[t]);",
+                                       "const double pk = exp(orc_similarity(a, bk, d) / j->tau);"),
 }
 
 
