@@ -385,10 +385,34 @@ def other_infonce(args, torch, dev):
     return out
 
 
+def other_infonce_backward(args, torch, dev):
+    """The matching loss and its gradient with respect to both maps, same pair and ground
+    truth as infonce-512x384-bf16: the forward stage, then a row pass (softmax-weighted
+    rows of image 2 per term) and a column pass (softmax-weighted ground-truth rows of
+    image 1 per pixel of image 2), each recomputing every score."""
+    import dense_grounded_image_amd as mr
+    import workloads
+    p = workloads.config_pair(2)
+    A, B = dev_maps(p, torch, dev)
+    gt = torch.from_numpy(workloads.gt_pairs(p)).to(dev).unsqueeze(0)
+    n_gt = int(gt.shape[1])
+    f = mr.InfoNCE(A, B, n_gt, 0.1, backward=True)
+    steps = max(3, args.steps // 4)
+    ms, kms, kn = time_steps(lambda: f(A, B, gt), steps, 2, torch, 2 * steps)
+    scores = n_gt * p.N
+    rl = roofline_lse(2 * scores, p.d, steps, kms, kn)
+    if rl:
+        rl["kernel"] = "nce_grad_kernel (row and column passes)"
+        rl["mfma"]["note"] = "2*d flops per score for the scores; the p*X products add 4*32 executed flops per score"
+    return {"loss_and_grad_per_s": round(1000.0 / ms, 2), "ms_per_call": round(ms, 3), "n_gt": n_gt,
+            "scores_per_s": round(3 * scores * 1000.0 / ms, 1), "roofline": rl}
+
+
 OTHER = {"batch64-512x384-f32": other_batch64, "pair-1024x768-bf16": other_bf16_1024,
          "graph-50x512x384-f32": other_graph,
          "pointmaps-512x384-f32": other_points_fast, "pointmaps-512x384-f32-bruteforce": other_points_bruteforce,
-         "pair-512x384-bf16-bruteforce": other_bruteforce, "infonce-512x384-bf16": other_infonce}
+         "pair-512x384-bf16-bruteforce": other_bruteforce, "infonce-512x384-bf16": other_infonce,
+         "infonce-backward-512x384-bf16": other_infonce_backward}
 
 
 def main():

@@ -24,12 +24,13 @@ MR_OP_NN_ARGMAX, MR_OP_MUTUAL_NN, MR_OP_FAST_RECIPROCAL = 0, 1, 2
 MR_OP_POINT_NN, MR_OP_POINT_MUTUAL_NN, MR_OP_POINT_FAST_RECIPROCAL = 3, 4, 5
 MR_OP_FAST_RECIPROCAL_GRAPH = 6
 MR_OP_INFONCE = 7
+MR_OP_INFONCE_BACKWARD = 8
 STATUS = {0: "MR_OK", 1: "MR_ERR_NULL", 2: "MR_ERR_SHAPE", 3: "MR_ERR_DTYPE", 4: "MR_ERR_PARAM",
           5: "MR_ERR_WORKSPACE", 6: "MR_ERR_CAPACITY", 7: "MR_ERR_DEVICE"}
 
 EXPORTS = ("mr_workspace_bytes", "mr_status_str", "mr_seed_count", "mr_nn_argmax", "mr_mutual_nn",
            "mr_fast_reciprocal", "mr_fast_reciprocal_graph", "mr_point_nn", "mr_point_mutual_nn",
-           "mr_point_fast_reciprocal", "mr_infonce_forward",
+           "mr_point_fast_reciprocal", "mr_infonce_forward", "mr_infonce_backward",
            "mr_profile_begin", "mr_profile_end")
 
 
@@ -79,6 +80,8 @@ def load_library(path: str = LIB_PATH):
     lib.mr_point_fast_reciprocal.restype = ctypes.c_int
     lib.mr_infonce_forward.argtypes = [MP, MP, P, i64, ctypes.c_float, P, P, P, sz, P]
     lib.mr_infonce_forward.restype = ctypes.c_int
+    lib.mr_infonce_backward.argtypes = [MP, MP, P, i64, ctypes.c_float, P, P, P, P, P, sz, P]
+    lib.mr_infonce_backward.restype = ctypes.c_int
     lib.mr_profile_begin.argtypes = [i32]
     lib.mr_profile_begin.restype = ctypes.c_int
     lib.mr_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
@@ -320,28 +323,41 @@ class InfoNCE:
     once): terms[b, t] = logsumexp_k(<a_i, b_k> / tau) - <a_i, b_j> / tau for the
     ground-truth pair gt[b, t] = (i, j), and loss[b] = sum_t terms[b, t] (float64)."""
 
-    def __init__(self, a, b, n_gt: int, tau: float = 0.1):
+    def __init__(self, a, b, n_gt: int, tau: float = 0.1, backward: bool = False):
         torch = _torch()
         self.lib = load_library()
         self.tau = float(tau)
         self.n_gt = int(n_gt)
+        self.backward = bool(backward)
         ma, mb = _as_map(a), _as_map(b)
         self.B = ma.batch
         dev = a.device
         self.terms = torch.empty((self.B, self.n_gt), dtype=torch.float32, device=dev)
         self.loss = torch.empty((self.B,), dtype=torch.float64, device=dev)
-        need = self.lib.mr_workspace_bytes(MR_OP_INFONCE, ctypes.byref(ma), ctypes.byref(mb), self.n_gt, 0, 0)
+        if self.backward:
+            self.grad_a = torch.empty(_batched(a).shape, dtype=torch.float32, device=dev)
+            self.grad_b = torch.empty(_batched(b).shape, dtype=torch.float32, device=dev)
+        op = MR_OP_INFONCE_BACKWARD if self.backward else MR_OP_INFONCE
+        need = self.lib.mr_workspace_bytes(op, ctypes.byref(ma), ctypes.byref(mb), self.n_gt, 0, 0)
         if need == 0:
             raise MrError("mr_workspace_bytes", 2)
         self.ws = _workspace(need, dev)
         self.shape = (tuple(_batched(a).shape), tuple(_batched(b).shape), a.dtype)
 
     def __call__(self, a, b, gt):
+        """(terms, loss), plus (grad_a, grad_b) of each pair's loss when built with backward=True."""
         torch = _torch()
         if (tuple(_batched(a).shape), tuple(_batched(b).shape), a.dtype) != self.shape:
             raise ValueError("shapes differ from the ones this InfoNCE was built for")
         gt = gt.to(device=a.device, dtype=torch.int32).reshape(self.B, self.n_gt, 2).contiguous()
         ma, mb = _as_map(a), _as_map(b)
+        if self.backward:
+            rc = self.lib.mr_infonce_backward(ctypes.byref(ma), ctypes.byref(mb), gt.data_ptr(), self.n_gt,
+                                              self.tau, self.terms.data_ptr(), self.loss.data_ptr(),
+                                              self.grad_a.data_ptr(), self.grad_b.data_ptr(), self.ws.data_ptr(),
+                                              self.ws.numel(), _stream(a))
+            _check("mr_infonce_backward", rc)
+            return self.terms, self.loss, self.grad_a, self.grad_b
         rc = self.lib.mr_infonce_forward(ctypes.byref(ma), ctypes.byref(mb), gt.data_ptr(), self.n_gt, self.tau,
                                          self.terms.data_ptr(), self.loss.data_ptr(), self.ws.data_ptr(),
                                          self.ws.numel(), _stream(a))
@@ -355,6 +371,14 @@ def infonce(a, b, gt, tau: float = 0.1):
     B = _batched(a).shape[0]
     n_gt = gt.numel() // (2 * B)
     return InfoNCE(a, b, n_gt, tau)(a, b, gt)
+
+
+def infonce_backward(a, b, gt, tau: float = 0.1):
+    """The matching loss and its gradient (bf16 maps, d <= 32): returns (terms float32
+    [B, n_gt], loss float64 [B], grad_a float32 like a, grad_b float32 like b)."""
+    B = _batched(a).shape[0]
+    n_gt = gt.numel() // (2 * B)
+    return InfoNCE(a, b, n_gt, tau, backward=True)(a, b, gt)
 
 
 def matches(pairs, n_pairs, b: int = 0):

@@ -1415,6 +1415,7 @@ struct NceArgs {
     float k2;                // log2(e) / tau
     float2* partial;         // [batch][n_gt][nseg] (m, s) of LseSum (base 2), merged over the lane halves
     float* terms;            // [batch][n_gt]
+    float* lse2;             // NULL or [batch][n_gt]: the base-2 log-sum-exp of each pair
     double* block_sums;      // [batch][nblk]
     double* loss;            // [batch]
 };
@@ -1519,6 +1520,7 @@ __global__ __launch_bounds__(256) void nce_terms_kernel(NceArgs a) {
             c = (tot - S) - y;
             S = tot;
         }
+        if (a.lse2) a.lse2[pt] = m + log2f(S);
         float term = __builtin_nanf("");
         if (i >= 0 && i < a.n1 && j >= 0 && j < a.n2) {
             const T* x = static_cast<const T*>(a.amap) + pair * a.a_pair_elems + (int64_t)i * a.d;
@@ -1552,6 +1554,241 @@ __global__ __launch_bounds__(256) void nce_loss_kernel(NceArgs a) {
         __syncthreads();
     }
     if (threadIdx.x == 0) a.loss[pair] = red[0];
+}
+
+// ---------------------------------------------------------------------------- matching loss, gradient
+
+// With p[t][k] = 2^(<a_i, b_k> k2 - lse2_t) (term t's softmax over the rows k of b,
+// lse2_t its base-2 log-sum-exp), the gradient of the summed loss is
+//     dL/da_i = (1/tau) sum_{t: i_t = i} ( sum_k p[t][k] b_k - b_{j_t} ),
+//     dL/db_k = (1/tau) sum_t p[t][k] a_{i_t} - (1/tau) sum_{t: j_t = k} a_{i_t}.
+// Both softmax-weighted sums are attention-like products that nce_grad_kernel
+// forms without storing p: the row pass takes the ground-truth rows a_{i_t} as
+// queries and streams b (O_t = sum_k p[t][k] b_k); the column pass takes the rows
+// of b as queries and streams the gathered rows a_{i_t} (O_k = sum_t p[t][k]
+// a_{i_t}).  Per 32-row tile the scores come from the similarity MFMA (the same
+// instruction, operand roles and order as the forward, so p is consistent with
+// lse2), p from one fma and one v_exp per score, and O += p X on the matrix cores
+// with p split exactly-to-2^-17 into two bf16 parts (hi + lo) and X the staged
+// tile read transposed.  bf16 maps, d <= 32.
+constexpr int kGradQT = 2;   // query tiles per wave
+
+struct NceGradArgs {
+    const void* qmap;        // query rows: a (row pass, through the ground truth) or b (column pass)
+    const void* xmap;        // streamed rows: b (row pass) or a (column pass, through the ground truth)
+    int64_t q_pair_elems, x_pair_elems;
+    int32_t nq_rows, nx_rows;  // rows of the query / streamed map per pair
+    int32_t d;
+    const int32_t* gt;       // [batch][n_gt][2]
+    int32_t n_gt;
+    int32_t nq, nx;          // queries and streamed rows per pair
+    int32_t nseg;            // streamed segments (partials per query)
+    float k2;                // log2(e) / tau
+    const float* lse2;       // [batch][n_gt]
+    float* partial;          // [batch][nq][nseg][32] fp32 (columns c < d used)
+};
+
+template <int P, bool COLS>
+__global__ __launch_bounds__(kThreads) void nce_grad_kernel(NceGradArgs a) {
+    constexpr int TILE = 32 * 32 * P;                 // bytes of a staged 32-row tile (bf16, row stride d)
+    __shared__ __attribute__((aligned(16))) char lds[2 * TILE];
+    __shared__ float lse_x[2][32];                    // column pass: lse2 of the staged rows
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5;
+    const int jl = lane & 31;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.y;
+    const int d = a.d;
+    const int rb = 2 * d;
+    const int nq = a.nq, nx = a.nx, nsg = a.nseg;
+    const int ntiles = (nx + 31) >> 5;
+    const int nqt = (nq + 31) >> 5;
+    const int qgroups = (nqt + kWaves * kGradQT - 1) / (kWaves * kGradQT);
+    const int items = qgroups * nsg;
+    const uint16_t* qbase = static_cast<const uint16_t*>(a.qmap) + pair * a.q_pair_elems;
+    const char* xbytes = static_cast<const char*>(a.xmap) + pair * a.x_pair_elems * 2;
+    const int32_t* gt = a.gt + (int64_t)pair * a.n_gt * 2;
+    const float* lse2 = a.lse2 + (int64_t)pair * a.n_gt;
+
+    // row of the streamed map behind streamed index x (-1: none)
+    auto x_row = [&](int x) -> int64_t {
+        if (x >= nx) return -1;
+        if (!COLS) return x;
+        const int64_t r = gt[2 * x];
+        return r >= 0 && r < a.nx_rows ? r : -1;
+    };
+
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int qg = item / nsg;
+        const int sg = item - qg * nsg;
+        const int g0 = (int)((int64_t)qg * nqt / qgroups);
+        const int g1 = (int)((int64_t)(qg + 1) * nqt / qgroups);
+        const int nact = g0 + wv < g1 ? (g1 - g0 - wv + kWaves - 1) / kWaves : 0;
+        Operand<AR_BF16, P> q[kGradQT];
+        float lq[kGradQT];                            // row pass: the query's lse2
+#pragma unroll
+        for (int j = 0; j < kGradQT; ++j) {
+            lq[j] = INFINITY;
+            if (j < nact) {
+                const int qp = (g0 + wv + j * kWaves) * 32 + jl;
+                int64_t row = -1;
+                if (qp < nq) {
+                    if (COLS) row = qp;
+                    else {
+                        row = gt[2 * qp];
+                        lq[j] = lse2[qp];
+                    }
+                }
+                const bool valid = row >= 0 && row < a.nq_rows;
+                q[j].load(qbase, valid ? row : 0, valid, h, d, COLS ? 2 : 1);
+            }
+        }
+        const int t0 = (int)((int64_t)sg * ntiles / nsg);
+        const int t1 = (int)((int64_t)(sg + 1) * ntiles / nsg);
+        f32x16 o[kGradQT];
+#pragma unroll
+        for (int j = 0; j < kGradQT; ++j) o[j] = f32x16{};
+
+        // staging: 16-byte chunks of the tile's rows (zeros past the end), one per thread
+        const int nchunk = 32 * rb / 16;
+        auto fetch = [&](int t) {
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if ((int)threadIdx.x < nchunk) {
+                const int r = threadIdx.x / (rb / 16), cc = threadIdx.x - r * (rb / 16);
+                const int64_t row = x_row(t * 32 + r);
+                if (row >= 0) v = *reinterpret_cast<const u32x4*>(xbytes + row * rb + cc * 16);
+            }
+            return v;
+        };
+        auto fetch_lse = [&](int t) {
+            const int x = t * 32 + (int)threadIdx.x;
+            return COLS && threadIdx.x < 32 && x < nx ? lse2[x] : INFINITY;
+        };
+        auto put = [&](int buf, u32x4 v, float l) {
+            if ((int)threadIdx.x < nchunk) *reinterpret_cast<u32x4*>(lds + buf * TILE + threadIdx.x * 16) = v;
+            if (COLS && threadIdx.x < 32) lse_x[buf][threadIdx.x] = l;
+        };
+        auto compute = [&](int buf, int t) {
+            const uint16_t* xs = reinterpret_cast<const uint16_t*>(lds + buf * TILE);
+            Operand<AR_BF16, P> xo;
+            xo.load(xs, jl, true, h, d, COLS ? 1 : 2);
+            // the tile read transposed: lane (h, c) holds X[row R(s, h, e)][c], e = 0..7,
+            // with R the accumulator's row order, so k-slot 8h + e of step s pairs p and X
+            bf16x8 xt[2];
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = tile_row(8 * s2 + e, h);
+                    xt[s2][e] = __builtin_bit_cast(__bf16, jl < d ? xs[r * d + jl] : (uint16_t)0);
+                }
+            float lx[16];
+            if (COLS) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) lx[v] = lse_x[buf][tile_row(v, h)];
+            }
+#pragma unroll
+            for (int j = 0; j < kGradQT; ++j) {
+                if (j < nact) {
+                    const f32x16 acc = xo.mfma(q[j], f32x16{});
+                    bf16x8 ph[2], pl[2];
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const bool live = t * 32 + tile_row(v, h) < nx;
+                        const float lse = COLS ? lx[v] : lq[j];
+                        const float pv = live ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], a.k2, -lse)) : 0.0f;
+                        const __bf16 hi = (__bf16)pv;
+                        ph[v >> 3][v & 7] = hi;
+                        pl[v >> 3][v & 7] = (__bf16)(pv - (float)hi);
+                    }
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2) {
+                        o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[s2], xt[s2], o[j], 0, 0, 0);
+                        o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[s2], xt[s2], o[j], 0, 0, 0);
+                    }
+                }
+            }
+        };
+
+        if (t0 < t1) {
+            u32x4 st = fetch(t0);
+            float sl = fetch_lse(t0);
+            put(0, st, sl);
+            __syncthreads();
+            for (int t = t0; t < t1; ++t) {
+                const int buf = (t - t0) & 1;
+                if (t + 1 < t1) {
+                    st = fetch(t + 1);
+                    sl = fetch_lse(t + 1);
+                }
+                compute(buf, t);
+                if (t + 1 < t1) put(buf ^ 1, st, sl);
+                __syncthreads();
+            }
+        }
+        // lane (h, c) holds O[query tile_row(v, h)][c]
+#pragma unroll
+        for (int j = 0; j < kGradQT; ++j) {
+            if (j < nact) {
+                const int qb = (g0 + wv + j * kWaves) * 32;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int qp = qb + tile_row(v, h);
+                    if (qp < nq) a.partial[(((int64_t)pair * nq + qp) * nsg + sg) * 32 + jl] = o[j][v];
+                }
+            }
+        }
+    }
+}
+
+// Column pass result: db[k][c] = sum over segments (in order) of O_k[c], for every
+// row k of b (binary64 scratch, written once).
+__global__ __launch_bounds__(256) void nce_grad_cols_finish(NceGradArgs a, double* db) {
+    const int pair = blockIdx.y;
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < (int64_t)a.nq * a.d; x += (int64_t)gridDim.x * 256) {
+        const int64_t k = x / a.d;
+        const int c = (int)(x - k * a.d);
+        const float* p = a.partial + ((int64_t)pair * a.nq + k) * a.nseg * 32 + c;
+        float s = 0.0f;
+        for (int g = 0; g < a.nseg; ++g) s += p[g * 32];
+        db[(int64_t)pair * a.nq * a.d + x] = (double)s;
+    }
+}
+
+// Row pass result and the ground-truth terms of the gradient, per (t, c): da[i_t][c]
+// += sum over segments of O_t[c] - b[j_t][c], and db[j_t][c] -= a[i_t][c] (binary64
+// atomics; every addend is an fp32 value).  Pairs with an index out of range are
+// skipped.
+__global__ __launch_bounds__(256) void nce_grad_rows_finish(NceGradArgs a, const uint16_t* amap,
+                                                            const uint16_t* bmap, int64_t a_elems,
+                                                            int64_t b_elems, int32_t n1, int32_t n2, double* da,
+                                                            double* db) {
+    const int pair = blockIdx.y;
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < (int64_t)a.nq * a.d; x += (int64_t)gridDim.x * 256) {
+        const int64_t t = x / a.d;
+        const int c = (int)(x - t * a.d);
+        const int32_t* g = a.gt + ((int64_t)pair * a.n_gt + t) * 2;
+        const int i = g[0], j = g[1];
+        if (i < 0 || i >= n1 || j < 0 || j >= n2) continue;
+        const float* p = a.partial + ((int64_t)pair * a.nq + t) * a.nseg * 32 + c;
+        float s = 0.0f;
+        for (int k = 0; k < a.nseg; ++k) s += p[k * 32];
+        double* dai = da + ((int64_t)pair * n1 + i) * a.d + c;
+        double* dbj = db + ((int64_t)pair * n2 + j) * a.d + c;
+        atomicAdd(dai, (double)s);
+        atomicAdd(dai, -(double)elem_f32(bmap[pair * b_elems + (int64_t)j * a.d + c]));
+        atomicAdd(dbj, -(double)elem_f32(amap[pair * a_elems + (int64_t)i * a.d + c]));
+    }
+}
+
+// grad = acc / tau, rounded once to fp32.
+__global__ __launch_bounds__(256) void nce_grad_scale(const double* acc, float* grad, int64_t n, double inv_tau) {
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256)
+        grad[x] = (float)(acc[x] * inv_tau);
+}
+
+__global__ __launch_bounds__(256) void fill_f32_kernel(float* p, int64_t n, float v) {
+    for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (int64_t)gridDim.x * 256) p[x] = v;
 }
 
 // ---------------------------------------------------------------------------- host helpers
@@ -2037,27 +2274,29 @@ int validate_nce(const mr_map* a, const mr_map* b, int64_t n_gt) {
     if (rc) return rc;
     if (n_gt < 0 || n_gt > (int64_t(1) << 28)) return MR_ERR_PARAM;
     if (npix(b) == 0) return MR_ERR_SHAPE;   // the softmax needs at least one row
+    if (n_gt > 0 && npix(a) == 0) return MR_ERR_SHAPE;   // no ground-truth row can name a row of an empty map
     if (a->dtype == MR_F32 && (a->d % 8 != 0 || a->d > 32)) return MR_ERR_SHAPE;
     return MR_OK;
 }
 
-int infonce_impl(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau, float* out_terms,
-                 double* out_loss, void* ws, size_t ws_bytes, void* stream) {
-    int rc = validate_nce(a, b, n_gt);
-    if (rc) return rc;
-    if (!(tau > 0.0f) || !(tau < INFINITY)) return MR_ERR_PARAM;
-    if (!out_loss) return MR_ERR_NULL;
-    if (n_gt > 0 && (!gt || !out_terms)) return MR_ERR_NULL;
-    hipStream_t st = static_cast<hipStream_t>(stream);
+// hipEvents around one launch for the measurement aid (when it is on and has room).
+int prof_mark(hipStream_t st, bool& rec) {
+    rec = g_prof.on && g_prof.used < g_prof.cap;
+    return rec && hipEventRecord(g_prof.ev[2 * g_prof.used], st) != hipSuccess ? MR_ERR_DEVICE : MR_OK;
+}
+int prof_close(hipStream_t st, bool rec) {
+    if (!rec) return MR_OK;
+    if (hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st) != hipSuccess) return MR_ERR_DEVICE;
+    ++g_prof.used;
+    return MR_OK;
+}
+
+// The forward stages: log-sum-exp partials, terms (and lse2 when asked), loss.
+// Arguments are validated and n_gt > 0.
+int nce_forward_launch(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau,
+                       const NceLayout& L, void* ws, float* out_terms, double* out_loss, float* lse2, bool timed,
+                       hipStream_t st) {
     const int batch = a->batch;
-    if (n_gt == 0) {
-        hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(batch)), dim3(256), 0, st,
-                           reinterpret_cast<uint64_t*>(out_loss), (int64_t)batch, (uint64_t)0);   // +0.0
-        return dev_err();
-    }
-    NceLayout L;
-    if ((rc = nce_layout(a, b, n_gt, L))) return rc;
-    if ((rc = check_ws(ws, ws_bytes, L.total))) return rc;
     NceArgs x;
     memset(&x, 0, sizeof(x));
     x.amap = a->data;
@@ -2074,26 +2313,169 @@ int infonce_impl(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_
     x.k2 = (float)(1.4426950408889634 / (double)tau);
     x.partial = at<float2>(ws, L.partial);
     x.terms = out_terms;
+    x.lse2 = lse2;
     x.block_sums = at<double>(ws, L.sums);
     x.loss = out_loss;
-    const bool prof = g_prof.on && g_prof.used < g_prof.cap;
-    if (prof && hipEventRecord(g_prof.ev[2 * g_prof.used], st) != hipSuccess) return MR_ERR_DEVICE;
+    bool rec = false;
+    int rc;
+    if (timed && (rc = prof_mark(st, rec))) return rc;
     rc = with_lse_arith(a->dtype, a->d, [&](auto ar, auto p) {
         constexpr int AR = decltype(ar)::value, P = decltype(p)::value;
         hipLaunchKernelGGL((lse_partial_kernel<AR, P>), dim3(L.grid, batch), dim3(kThreads), 0, st, x);
         return dev_err();
     });
-    if (rc) return rc;
-    if (prof) {
-        if (hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st) != hipSuccess) return MR_ERR_DEVICE;
-        ++g_prof.used;
-    }
+    if (rc || (rc = prof_close(st, rec))) return rc;
     if (a->dtype == MR_BF16)
         hipLaunchKernelGGL(nce_terms_kernel<uint16_t>, dim3(L.nblk, batch), dim3(256), 0, st, x);
     else
         hipLaunchKernelGGL(nce_terms_kernel<float>, dim3(L.nblk, batch), dim3(256), 0, st, x);
     if (dev_err()) return MR_ERR_DEVICE;
     hipLaunchKernelGGL(nce_loss_kernel, dim3(batch), dim3(256), 0, st, x);
+    return dev_err();
+}
+
+int fill_zero(void* p, int64_t words, hipStream_t st) {   // words of 8 bytes
+    if (words <= 0) return MR_OK;
+    hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(words)), dim3(256), 0, st, static_cast<uint64_t*>(p), words,
+                       (uint64_t)0);
+    return dev_err();
+}
+
+int infonce_impl(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau, float* out_terms,
+                 double* out_loss, void* ws, size_t ws_bytes, void* stream) {
+    int rc = validate_nce(a, b, n_gt);
+    if (rc) return rc;
+    if (!(tau > 0.0f) || !(tau < INFINITY)) return MR_ERR_PARAM;
+    if (!out_loss) return MR_ERR_NULL;
+    if (n_gt > 0 && (!gt || !out_terms)) return MR_ERR_NULL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n_gt == 0) return fill_zero(out_loss, a->batch, st);   // +0.0
+    NceLayout L;
+    if ((rc = nce_layout(a, b, n_gt, L))) return rc;
+    if ((rc = check_ws(ws, ws_bytes, L.total))) return rc;
+    return nce_forward_launch(a, b, gt, n_gt, tau, L, ws, out_terms, out_loss, nullptr, true, st);
+}
+
+// ---- gradient
+
+struct NceGradLayout {
+    NceLayout f;
+    int nseg_r = 0, nseg_c = 0, grid_r = 0, grid_c = 0;
+    size_t lse2 = 0, prow = 0, pcol = 0, da = 0, db = 0, total = 0;
+};
+
+// Segments of a gradient pass as for the forward: resident workgroups spread over the
+// query groups, at most one per streamed tile, a multiple of 8 when large.
+template <int P, bool COLS>
+void grad_pass_shape(int batch, int64_t nq, int64_t nx, int& nseg, int& grid) {
+    const int g = grid_per_pair(resident_blocks<nce_grad_kernel<P, COLS>>(), batch);
+    const int64_t ntiles = (nx + 31) / 32;
+    const int64_t qgroups = ((nq + 31) / 32 + kWaves * kGradQT - 1) / (kWaves * kGradQT);
+    int64_t ns = qgroups > 0 ? g / qgroups : 1;
+    const int64_t cap = ntiles < kMaxSegGroups ? ntiles : kMaxSegGroups;
+    ns = ns < 1 ? 1 : (ns > cap ? cap : ns);
+    if (ns >= 8) ns &= ~int64_t(7);
+    nseg = (int)ns;
+    grid = (int)(qgroups * ns < g ? qgroups * ns : g);
+    if (grid < 1) grid = 1;
+}
+
+int validate_nce_grad(const mr_map* a, const mr_map* b, int64_t n_gt) {
+    const int rc = validate_nce(a, b, n_gt);
+    if (rc) return rc;
+    if (a->dtype != MR_BF16) return MR_ERR_DTYPE;
+    if (a->d > 32) return MR_ERR_SHAPE;
+    return MR_OK;
+}
+
+int nce_grad_layout(const mr_map* a, const mr_map* b, int64_t n_gt, NceGradLayout& L) {
+    const int rc = nce_layout(a, b, n_gt, L.f);
+    if (rc) return rc;
+    const int64_t n1 = npix(a), n2 = npix(b);
+    const int batch = a->batch;
+    if (a->d <= 16) {
+        grad_pass_shape<1, false>(batch, n_gt, n2, L.nseg_r, L.grid_r);
+        grad_pass_shape<1, true>(batch, n2, n_gt, L.nseg_c, L.grid_c);
+    } else {
+        grad_pass_shape<2, false>(batch, n_gt, n2, L.nseg_r, L.grid_r);
+        grad_pass_shape<2, true>(batch, n2, n_gt, L.nseg_c, L.grid_c);
+    }
+    const size_t B = (size_t)batch, d = (size_t)a->d, ngt = (size_t)(n_gt > 0 ? n_gt : 1);
+    size_t off = L.f.total;
+    L.lse2 = off; off = align256(off + B * ngt * sizeof(float));
+    L.prow = off; off = align256(off + B * ngt * (size_t)L.nseg_r * 32 * sizeof(float));
+    L.pcol = off; off = align256(off + B * (size_t)n2 * (size_t)L.nseg_c * 32 * sizeof(float));
+    L.da = off; off = align256(off + B * (size_t)(n1 > 0 ? n1 : 1) * d * sizeof(double));
+    L.db = off; off = align256(off + B * (size_t)n2 * d * sizeof(double));
+    L.total = off;
+    return MR_OK;
+}
+
+int infonce_backward_impl(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau,
+                          float* out_terms, double* out_loss, float* grad_a, float* grad_b, void* ws,
+                          size_t ws_bytes, void* stream) {
+    int rc = validate_nce_grad(a, b, n_gt);
+    if (rc) return rc;
+    if (!(tau > 0.0f) || !(tau < INFINITY)) return MR_ERR_PARAM;
+    const int64_t n1 = npix(a), n2 = npix(b);
+    if (!out_loss || !grad_b || (n1 > 0 && !grad_a)) return MR_ERR_NULL;
+    if (n_gt > 0 && (!gt || !out_terms)) return MR_ERR_NULL;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int batch = a->batch;
+    const int d = a->d;
+    if (n_gt == 0) {   // loss 0, gradients 0
+        if ((rc = fill_zero(out_loss, batch, st))) return rc;
+        if (n1 > 0)
+            hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_1d(batch * n1 * d)), dim3(256), 0, st, grad_a,
+                               (int64_t)batch * n1 * d, 0.0f);
+        hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_1d(batch * n2 * d)), dim3(256), 0, st, grad_b,
+                           (int64_t)batch * n2 * d, 0.0f);
+        return dev_err();
+    }
+    NceGradLayout L;
+    if ((rc = nce_grad_layout(a, b, n_gt, L))) return rc;
+    if ((rc = check_ws(ws, ws_bytes, L.total))) return rc;
+    double* da = at<double>(ws, L.da);
+    double* db = at<double>(ws, L.db);
+    float* lse2 = at<float>(ws, L.lse2);
+    if ((rc = fill_zero(da, (int64_t)batch * n1 * d, st))) return rc;
+    if ((rc = nce_forward_launch(a, b, gt, n_gt, tau, L.f, ws, out_terms, out_loss, lse2, false, st))) return rc;
+
+    NceGradArgs r;
+    memset(&r, 0, sizeof(r));
+    r.d = d;
+    r.gt = gt;
+    r.n_gt = (int32_t)n_gt;
+    r.k2 = (float)(1.4426950408889634 / (double)tau);
+    r.lse2 = lse2;
+    NceGradArgs c = r;
+    r.qmap = a->data; r.xmap = b->data; r.q_pair_elems = n1 * d; r.x_pair_elems = n2 * d;
+    r.nq_rows = (int32_t)n1; r.nx_rows = (int32_t)n2; r.nq = (int32_t)n_gt; r.nx = (int32_t)n2;
+    r.nseg = L.nseg_r; r.partial = at<float>(ws, L.prow);
+    c.qmap = b->data; c.xmap = a->data; c.q_pair_elems = n2 * d; c.x_pair_elems = n1 * d;
+    c.nq_rows = (int32_t)n2; c.nx_rows = (int32_t)n1; c.nq = (int32_t)n2; c.nx = (int32_t)n_gt;
+    c.nseg = L.nseg_c; c.partial = at<float>(ws, L.pcol);
+    bool rec = false;
+    if ((rc = prof_mark(st, rec))) return rc;
+    if (d <= 16) hipLaunchKernelGGL((nce_grad_kernel<1, false>), dim3(L.grid_r, batch), dim3(kThreads), 0, st, r);
+    else hipLaunchKernelGGL((nce_grad_kernel<2, false>), dim3(L.grid_r, batch), dim3(kThreads), 0, st, r);
+    if (dev_err() || (rc = prof_close(st, rec))) return rc ? rc : MR_ERR_DEVICE;
+    if ((rc = prof_mark(st, rec))) return rc;
+    if (d <= 16) hipLaunchKernelGGL((nce_grad_kernel<1, true>), dim3(L.grid_c, batch), dim3(kThreads), 0, st, c);
+    else hipLaunchKernelGGL((nce_grad_kernel<2, true>), dim3(L.grid_c, batch), dim3(kThreads), 0, st, c);
+    if (dev_err() || (rc = prof_close(st, rec))) return rc ? rc : MR_ERR_DEVICE;
+    hipLaunchKernelGGL(nce_grad_cols_finish, dim3(grid_1d(n2 * d), batch), dim3(256), 0, st, c, db);
+    if (dev_err()) return MR_ERR_DEVICE;
+    hipLaunchKernelGGL(nce_grad_rows_finish, dim3(grid_1d(n_gt * d), batch), dim3(256), 0, st, r,
+                       static_cast<const uint16_t*>(a->data), static_cast<const uint16_t*>(b->data), n1 * d, n2 * d,
+                       (int32_t)n1, (int32_t)n2, da, db);
+    if (dev_err()) return MR_ERR_DEVICE;
+    const double inv_tau = 1.0 / (double)tau;
+    if (n1 > 0)
+        hipLaunchKernelGGL(nce_grad_scale, dim3(grid_1d(batch * n1 * d)), dim3(256), 0, st, da, grad_a,
+                           (int64_t)batch * n1 * d, inv_tau);
+    hipLaunchKernelGGL(nce_grad_scale, dim3(grid_1d(batch * n2 * d)), dim3(256), 0, st, db, grad_b,
+                       (int64_t)batch * n2 * d, inv_tau);
     return dev_err();
 }
 
@@ -2147,6 +2529,11 @@ size_t mr_workspace_bytes(int op, const mr_map* a, const mr_map* b, int64_t n_q,
             if (validate_nce(a, b, n_q) != MR_OK || nce_layout(a, b, n_q, L) != MR_OK) return 0;
             return L.total;
         }
+        case MR_OP_INFONCE_BACKWARD: {
+            NceGradLayout L;
+            if (validate_nce_grad(a, b, n_q) != MR_OK || nce_grad_layout(a, b, n_q, L) != MR_OK) return 0;
+            return L.total;
+        }
         default: return 0;
     }
 }
@@ -2154,6 +2541,12 @@ size_t mr_workspace_bytes(int op, const mr_map* a, const mr_map* b, int64_t n_q,
 int mr_infonce_forward(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau,
                        float* out_terms, double* out_loss, void* ws, size_t ws_bytes, void* stream) {
     return infonce_impl(a, b, gt, n_gt, tau, out_terms, out_loss, ws, ws_bytes, stream);
+}
+
+int mr_infonce_backward(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau,
+                        float* out_terms, double* out_loss, float* grad_a, float* grad_b, void* ws, size_t ws_bytes,
+                        void* stream) {
+    return infonce_backward_impl(a, b, gt, n_gt, tau, out_terms, out_loss, grad_a, grad_b, ws, ws_bytes, stream);
 }
 
 int mr_nn_argmax(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q, int32_t* out_idx,

@@ -79,7 +79,8 @@ enum {
     MR_OP_NN_ARGMAX = 0, MR_OP_MUTUAL_NN = 1, MR_OP_FAST_RECIPROCAL = 2,
     MR_OP_POINT_NN = 3, MR_OP_POINT_MUTUAL_NN = 4, MR_OP_POINT_FAST_RECIPROCAL = 5,
     MR_OP_FAST_RECIPROCAL_GRAPH = 6,  /* a = b = the image collection, n_q = number of edges */
-    MR_OP_INFONCE = 7                 /* n_q = ground-truth pairs per image pair */
+    MR_OP_INFONCE = 7,                /* n_q = ground-truth pairs per image pair */
+    MR_OP_INFONCE_BACKWARD = 8        /* n_q = ground-truth pairs per image pair */
 };
 
 /* Workspace bytes that entry point `op` needs for these maps and parameters
@@ -204,8 +205,8 @@ int mr_point_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, i
  * the log-sum-exp is accumulated online in fp32 with the largest score as its
  * shift, so no exponential overflows for any finite input; the positive score
  * is an fp32 dot product in component order.
- *   a, b     : maps of equal batch, d and dtype; b has at least one row (else
- *              MR_ERR_SHAPE).  bf16 maps: any supported d; fp32 maps: d in
+ *   a, b     : maps of equal batch, d and dtype; b has at least one row, and
+ *              a too when n_gt > 0 (else MR_ERR_SHAPE).  bf16 maps: any supported d; fp32 maps: d in
  *              {8, 16, 24, 32} (else MR_ERR_SHAPE).
  *   gt       : DEVICE int32 [batch][n_gt][2] rows (i in a, j in b) of each
  *              pair; an out-of-range pair is not an error: its term is NaN
@@ -219,6 +220,34 @@ int mr_point_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, i
  * --------------------------------------------------------------------------- */
 int mr_infonce_forward(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau,
                        float* out_terms, double* out_loss, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mr_infonce_backward: the matching loss of mr_infonce_forward (same terms and
+ * loss outputs) and its gradient with respect to both maps ("MASt3R
+ * dissection", section 3 "Napkin Formula": the loss the descriptor head is
+ * trained with).  The derivative of each term's log-sum-exp is its softmax
+ * p[t][k] over the rows of b, so for image pair b of the batch
+ *     grad_a[i] = (1/tau) sum_{t: i_t = i} ( sum_k p[t][k] b[k] - b[j_t] ),
+ *     grad_b[k] = (1/tau) sum_t p[t][k] a[i_t] - (1/tau) sum_{t: j_t = k} a[i_t],
+ * the gradient of that pair's loss (a sum over its terms); rows of a that no
+ * ground-truth pair names get 0.
+ *   a, b   : bf16 maps (else MR_ERR_DTYPE) with d <= 32 (else MR_ERR_SHAPE);
+ *            otherwise as mr_infonce_forward.
+ *   grad_a : [batch][h_a][w_a][d] fp32 (may be NULL only when a has no rows);
+ *   grad_b : [batch][h_b][w_b][d] fp32.
+ *   ws     : mr_workspace_bytes(MR_OP_INFONCE_BACKWARD, a, b, n_gt, 0, 0) bytes
+ *            (unused when n_gt = 0).
+ * The softmax-weighted sums are formed on the matrix cores with each softmax
+ * value split into two bf16 parts (relative error below 2^-17) and fp32
+ * accumulation; rows that several ground-truth pairs share are accumulated with
+ * binary64 atomic adds of fp32 values before the final scaling and rounding, so
+ * the result can differ between runs only where such a sum rounds in binary64.
+ * A ground-truth pair with an index out of range makes that image pair's loss
+ * NaN; its gradient is then unspecified (finite or not), never out of bounds.
+ * --------------------------------------------------------------------------- */
+int mr_infonce_backward(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau,
+                        float* out_terms, double* out_loss, float* grad_a, float* grad_b, void* ws,
+                        size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Measurement aid (not thread-safe; one profiling window per process).
