@@ -44,6 +44,8 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;            // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
@@ -1589,7 +1591,7 @@ struct NceGradArgs {
 };
 
 template <int P, bool COLS>
-__global__ __launch_bounds__(kThreads) void nce_grad_kernel(NceGradArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void nce_grad_kernel(NceGradArgs a) {
     constexpr int TILE = 32 * 32 * P;                 // bytes of a staged 32-row tile (bf16, row stride d)
     __shared__ __attribute__((aligned(16))) char lds[2 * TILE];
     __shared__ float lse_x[2][32];                    // column pass: lse2 of the staged rows
@@ -1668,7 +1670,8 @@ __global__ __launch_bounds__(kThreads) void nce_grad_kernel(NceGradArgs a) {
             if ((int)threadIdx.x < nchunk) *reinterpret_cast<u32x4*>(lds + buf * TILE + threadIdx.x * 16) = v;
             if (COLS && threadIdx.x < 32) lse_x[buf][threadIdx.x] = l;
         };
-        auto compute = [&](int buf, int t) {
+        auto compute = [&](int buf, int t, auto ragged) {
+            constexpr bool RAGGED = decltype(ragged)::value;
             const uint16_t* xs = reinterpret_cast<const uint16_t*>(lds + buf * TILE);
             Operand<AR_BF16, P> xo;
             xo.load(xs, jl, true, h, d, COLS ? 1 : 2);
@@ -1691,15 +1694,24 @@ __global__ __launch_bounds__(kThreads) void nce_grad_kernel(NceGradArgs a) {
             for (int j = 0; j < kGradQT; ++j) {
                 if (j < nact) {
                     const f32x16 acc = xo.mfma(q[j], f32x16{});
-                    bf16x8 ph[2], pl[2];
+                    float pv[16];
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const bool live = t * 32 + tile_row(v, h) < nx;
                         const float lse = COLS ? lx[v] : lq[j];
-                        const float pv = live ? __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], a.k2, -lse)) : 0.0f;
-                        const __bf16 hi = (__bf16)pv;
-                        ph[v >> 3][v & 7] = hi;
-                        pl[v >> 3][v & 7] = (__bf16)(pv - (float)hi);
+                        pv[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[v], a.k2, -lse));
+                        if (RAGGED && t * 32 + tile_row(v, h) >= nx) pv[v] = 0.0f;
+                    }
+                    // p = hi + lo, each rounded to bf16 in pairs (v_cvt_pk_bf16_f32)
+                    bf16x8 ph[2], pl[2];
+#pragma unroll
+                    for (int v = 0; v < 16; v += 2) {
+                        const bf16x2 hi = __builtin_convertvector(f32x2{pv[v], pv[v + 1]}, bf16x2);
+                        const f32x2 back = __builtin_convertvector(hi, f32x2);
+                        const bf16x2 lo = __builtin_convertvector(f32x2{pv[v] - back[0], pv[v + 1] - back[1]}, bf16x2);
+                        ph[v >> 3][v & 7] = hi[0];
+                        ph[v >> 3][(v & 7) + 1] = hi[1];
+                        pl[v >> 3][v & 7] = lo[0];
+                        pl[v >> 3][(v & 7) + 1] = lo[1];
                     }
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2) {
@@ -1711,19 +1723,31 @@ __global__ __launch_bounds__(kThreads) void nce_grad_kernel(NceGradArgs a) {
         };
 
         if (t0 < t1) {
-            u32x4 st = fetch(t0);
-            float sl = fetch_lse(t0);
-            put(0, st, sl);
+            // tile t + 1 is loaded into registers two iterations before it is written to
+            // LDS (at the end of iteration t, after the multiply of tile t); loads past
+            // the segment repeat its last tile, so they are issued unconditionally
+            auto clamp = [&](int t) { return t < t1 ? t : t1 - 1; };
+            u32x4 st[2];
+            float sl[2];
+            put(0, fetch(t0), fetch_lse(t0));
+            st[0] = fetch(clamp(t0 + 1));
+            sl[0] = fetch_lse(clamp(t0 + 1));
+            st[1] = fetch(clamp(t0 + 2));
+            sl[1] = fetch_lse(clamp(t0 + 2));
             __syncthreads();
-            for (int t = t0; t < t1; ++t) {
-                const int buf = (t - t0) & 1;
-                if (t + 1 < t1) {
-                    st = fetch(t + 1);
-                    sl = fetch_lse(t + 1);
+            for (int t = t0; t < t1; t += 2) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int tt = t + u;
+                    if (tt < t1) {
+                        if ((tt + 1) * 32 > nx) compute(u, tt, std::true_type{});
+                        else compute(u, tt, std::false_type{});
+                        put(u ^ 1, st[u], sl[u]);
+                        st[u] = fetch(clamp(tt + 3));
+                        sl[u] = fetch_lse(clamp(tt + 3));
+                        __syncthreads();
+                    }
                 }
-                compute(buf, t);
-                if (t + 1 < t1) put(buf ^ 1, st, sl);
-                __syncthreads();
             }
         }
         // lane (h, c) holds O[query tile_row(v, h)][c]
