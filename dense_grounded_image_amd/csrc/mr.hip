@@ -1573,7 +1573,7 @@ __global__ __launch_bounds__(256) void nce_loss_kernel(NceArgs a) {
 // lse2), p from one fma and one v_exp per score, and O += p X on the matrix cores
 // with p split exactly-to-2^-17 into two bf16 parts (hi + lo) and X the staged
 // tile read transposed.  bf16 maps, d <= 32.
-constexpr int kGradQT = 2;   // query tiles per wave
+constexpr int kGradQT = 1;   // query tiles per wave
 
 struct NceGradArgs {
     const void* qmap;        // query rows: a (row pass, through the ground truth) or b (column pass)
@@ -1591,7 +1591,7 @@ struct NceGradArgs {
 };
 
 template <int P, bool COLS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void nce_grad_kernel(NceGradArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void nce_grad_kernel(NceGradArgs a) {
     constexpr int TILE = 32 * 32 * P;                 // bytes of a staged 32-row tile (bf16, row stride d)
     __shared__ __attribute__((aligned(16))) char lds[2 * TILE];
     __shared__ float lse_x[2][32];                    // column pass: lse2 of the staged rows
