@@ -517,11 +517,10 @@ template <int AR, int P> constexpr int lds_row_bytes() {        // a staged row 
 // four waves multiplies the staged tile against its own QT query tiles held in
 // registers and keeps a per-lane running best.
 // The per-lane state ep (one of the epilogue states above) takes each product tile.
-template <int AR, int P, class Ep>
+template <int AR, int P, int QT, class Ep>
 __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb,
-                                             char* lds, const Operand<AR, P> (&q)[qt_of<AR, P>()],
+                                             char* lds, const Operand<AR, P> (&q)[QT],
                                              int nact, int h, int jl, int d, int role, Ep& ep) {
-    constexpr int QT = qt_of<AR, P>();
     constexpr int MAXC = (32 * max_row_bytes<AR, P>() / 16 + kThreads - 1) / kThreads;
     constexpr int BUF = 32 * lds_row_bytes<AR, P>();
     const int tile_bytes = 32 * rb;
@@ -636,12 +635,12 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
 // ragged epilogue masks them.
 constexpr int kStageTiles = 2;
 
-template <int AR, int P, int S, class Ep>
+template <int AR, int P, int S, int QT, class Ep>
 __device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb,
-                                              char* lds, const Operand<AR, P> (&q)[qt_of<AR, P>()], int nact,
+                                              char* lds, const Operand<AR, P> (&q)[QT], int nact,
                                               int h, int jl, int d, int role, Ep& ep) {
     static_assert(AR == AR_BF16, "the staged ring holds bf16 rows");
-    constexpr int QT = qt_of<AR, P>();
+
     constexpr int NB = 3;
     constexpr int STAGE = S * 32 * lds_row_bytes<AR, P>();
     constexpr int MAXC = (S * 32 * max_row_bytes<AR, P>() / 16 + kThreads - 1) / kThreads;
@@ -732,9 +731,9 @@ __device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, i
 // The workgroup-staged stream for an arithmetic: the LDS ring for bf16 rows; the
 // plain double buffer for fp32 rows (measured faster for the long split contraction,
 // whose nine matrix-core steps per tile already cover the staging latency).
-template <int AR, int P, class Ep>
+template <int AR, int P, int QT, class Ep>
 __device__ __forceinline__ void stream_db(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb, char* lds,
-                                          const Operand<AR, P> (&q)[qt_of<AR, P>()], int nact, int h, int jl, int d,
+                                          const Operand<AR, P> (&q)[QT], int nact, int h, int jl, int d,
                                           int role, Ep& ep) {
     if constexpr (AR != AR_BF16)
         stream_tiles<AR, P>(dbytes, rb, t0, t1, ndb, lds, q, nact, h, jl, d, role, ep);
@@ -746,11 +745,10 @@ __device__ __forceinline__ void stream_db(const char* __restrict__ dbytes, int r
 // database operand straight from global memory (the four waves of a workgroup read
 // the same tiles, so L1 serves all but the first) into a ring of D tiles issued D
 // tiles ahead of their use.
-template <int AR, int P, int D, class Ep>
+template <int AR, int P, int D, int QT, class Ep>
 __device__ __forceinline__ void stream_regs(const void* dbase, int t0, int t1,
-                                            const Operand<AR, P> (&q)[qt_of<AR, P>()], int h, int jl, int d,
+                                            const Operand<AR, P> (&q)[QT], int h, int jl, int d,
                                             Ep& ep) {
-    constexpr int QT = qt_of<AR, P>();
     static_assert(AR == AR_BF16, "direct database operands are bf16 only");
     Operand<AR, P> r[D];
     int off[P];
@@ -790,11 +788,10 @@ __device__ __forceinline__ void stream_regs(const void* dbase, int t0, int t1,
 // Small frontiers (all live queries fit in one wave): every wave of the workgroup
 // holds the same queries and streams its own database segment straight from global
 // memory, one tile ahead in registers, with no LDS staging and no barriers.
-template <int AR, int P, class Ep>
+template <int AR, int P, int QT, class Ep>
 __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1, int ndb,
-                                              const Operand<AR, P> (&q)[qt_of<AR, P>()],
+                                              const Operand<AR, P> (&q)[QT],
                                               int nact, int h, int jl, int d, int role, Ep& ep) {
-    constexpr int QT = qt_of<AR, P>();
     if (t0 >= t1) return;
     auto row_of = [&](int t) { return (int64_t)t * 32 + jl; };
     auto get = [&](Operand<AR, P>& o, int t) {
