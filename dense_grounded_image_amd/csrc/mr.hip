@@ -1568,8 +1568,8 @@ __global__ __launch_bounds__(256) void nce_loss_kernel(NceArgs a) {
 // a_{i_t}).  Per 32-row tile the scores come from the similarity MFMA (the same
 // instruction, operand roles and order as the forward, so p is consistent with
 // lse2), p from one fma and one v_exp per score, and O += p X on the matrix cores
-// with p split exactly-to-2^-17 into two bf16 parts (hi + lo) and X the staged
-// tile read transposed.  bf16 maps, d <= 32.
+// with p split into two bf16 parts (hi + lo, relative error below 2^-17) and X the
+// staged tile read transposed (fp32 maps: its three bf16 planes).  d <= 32.
 constexpr int kGradQT = 1;   // query tiles per wave
 
 struct NceGradArgs {
@@ -1587,9 +1587,12 @@ struct NceGradArgs {
     float* partial;          // [batch][nq][nseg][32] fp32 (columns c < d used)
 };
 
-template <int P, bool COLS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void nce_grad_kernel(NceGradArgs a) {
-    constexpr int TILE = 32 * 32 * P;                 // bytes of a staged 32-row tile (bf16, row stride d)
+template <int AR, int P, bool COLS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(AR == AR_BF16 ? 4 : 2)))
+void nce_grad_kernel(NceGradArgs a) {
+    static_assert(AR == AR_BF16 || AR == AR_X3, "bf16 maps or the split fp32 arithmetic");
+    using Elem = typename ArithTraits<AR>::elem;
+    constexpr int TILE = 32 * lds_row_bytes<AR, P>();   // a staged 32-row tile: bf16 rows, or [h|m|l] planes
     __shared__ __attribute__((aligned(16))) char lds[2 * TILE];
     __shared__ float lse_x[2][32];                    // column pass: lse2 of the staged rows
     const int lane = threadIdx.x & 63;
@@ -1598,14 +1601,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int pair = blockIdx.y;
     const int d = a.d;
-    const int rb = 2 * d;
+    const int rb = (int)sizeof(Elem) * d;             // bytes of a map row
     const int nq = a.nq, nx = a.nx, nsg = a.nseg;
     const int ntiles = (nx + 31) >> 5;
     const int nqt = (nq + 31) >> 5;
     const int qgroups = (nqt + kWaves * kGradQT - 1) / (kWaves * kGradQT);
     const int items = qgroups * nsg;
-    const uint16_t* qbase = static_cast<const uint16_t*>(a.qmap) + pair * a.q_pair_elems;
-    const char* xbytes = static_cast<const char*>(a.xmap) + pair * a.x_pair_elems * 2;
+    const Elem* qbase = static_cast<const Elem*>(a.qmap) + pair * a.q_pair_elems;
+    const char* xbytes = reinterpret_cast<const char*>(static_cast<const Elem*>(a.xmap) + pair * a.x_pair_elems);
     const int32_t* gt = a.gt + (int64_t)pair * a.n_gt * 2;
     const float* lse2 = a.lse2 + (int64_t)pair * a.n_gt;
 
@@ -1623,7 +1626,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         const int g0 = (int)((int64_t)qg * nqt / qgroups);
         const int g1 = (int)((int64_t)(qg + 1) * nqt / qgroups);
         const int nact = g0 + wv < g1 ? (g1 - g0 - wv + kWaves - 1) / kWaves : 0;
-        Operand<AR_BF16, P> q[kGradQT];
+        Operand<AR, P> q[kGradQT];
         float lq[kGradQT];                            // row pass: the query's lse2
 #pragma unroll
         for (int j = 0; j < kGradQT; ++j) {
@@ -1639,7 +1642,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                     }
                 }
                 const bool valid = row >= 0 && row < a.nq_rows;
-                q[j].load(qbase, valid ? row : 0, valid, h, d, COLS ? 2 : 1);
+                if constexpr (AR == AR_X3)
+                    q[j].load_f32(reinterpret_cast<const float*>(qbase) + (valid ? row : 0) * d, valid, h, COLS ? 2 : 1);
+                else
+                    q[j].load(qbase, valid ? row : 0, valid, h, d, COLS ? 2 : 1);
             }
         }
         const int t0 = (int)((int64_t)sg * ntiles / nsg);
@@ -1664,24 +1670,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
             return COLS && threadIdx.x < 32 && x < nx ? lse2[x] : INFINITY;
         };
         auto put = [&](int buf, u32x4 v, float l) {
-            if ((int)threadIdx.x < nchunk) *reinterpret_cast<u32x4*>(lds + buf * TILE + threadIdx.x * 16) = v;
+            if ((int)threadIdx.x < nchunk) {
+                if constexpr (AR == AR_X3) {
+                    // four fp32 components -> their h, m, l parts in the row's three planes
+                    const int r = threadIdx.x / (d / 4), c0 = (threadIdx.x - r * (d / 4)) * 4;
+                    uint16_t e3[3][4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) split3(__uint_as_float(v[e]), e3[0][e], e3[1][e], e3[2][e]);
+                    char* dst = lds + buf * TILE + r * 6 * d + c0 * 2;
+#pragma unroll
+                    for (int k = 0; k < 3; ++k)
+                        *reinterpret_cast<uint2*>(dst + k * 2 * d) =
+                            uint2{(uint32_t)e3[k][0] | ((uint32_t)e3[k][1] << 16),
+                                  (uint32_t)e3[k][2] | ((uint32_t)e3[k][3] << 16)};
+                } else {
+                    *reinterpret_cast<u32x4*>(lds + buf * TILE + threadIdx.x * 16) = v;
+                }
+            }
             if (COLS && threadIdx.x < 32) lse_x[buf][threadIdx.x] = l;
         };
         auto compute = [&](int buf, int t, auto ragged) {
             constexpr bool RAGGED = decltype(ragged)::value;
+            constexpr int NPL = AR == AR_X3 ? 3 : 1;  // bf16 planes of a staged row
             const uint16_t* xs = reinterpret_cast<const uint16_t*>(lds + buf * TILE);
-            Operand<AR_BF16, P> xo;
+            Operand<AR, P> xo;
             xo.load(xs, jl, true, h, d, COLS ? 1 : 2);
-            // the tile read transposed: lane (h, c) holds X[row R(s, h, e)][c], e = 0..7,
-            // with R the accumulator's row order, so k-slot 8h + e of step s pairs p and X
-            bf16x8 xt[2];
+            // the tile read transposed: lane (h, c) holds plane k of X[row R(s, h, e)][c],
+            // e = 0..7, with R the accumulator's row order, so k-slot 8h + e of step s
+            // pairs p and X
+            bf16x8 xt[NPL][2];
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
+            for (int k = 0; k < NPL; ++k)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = tile_row(8 * s2 + e, h);
-                    xt[s2][e] = __builtin_bit_cast(__bf16, jl < d ? xs[r * d + jl] : (uint16_t)0);
-                }
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int r = tile_row(8 * s2 + e, h);
+                        xt[k][s2][e] =
+                            __builtin_bit_cast(__bf16, jl < d ? xs[(r * NPL + k) * d + jl] : (uint16_t)0);
+                    }
             float lx[16];
             if (COLS) {
 #pragma unroll
@@ -1712,8 +1739,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
                     }
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2) {
-                        o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[s2], xt[s2], o[j], 0, 0, 0);
-                        o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[s2], xt[s2], o[j], 0, 0, 0);
+                        // bf16 X: p_hi X + p_lo X.  Split X = X_h + X_m + X_l: the five
+                        // products above 2^-24 of |p||X| (p_lo X_l is below it)
+                        o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[s2], xt[0][s2], o[j], 0, 0, 0);
+                        o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[s2], xt[0][s2], o[j], 0, 0, 0);
+                        if constexpr (NPL == 3) {
+                            o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[s2], xt[1][s2], o[j], 0, 0, 0);
+                            o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[s2], xt[1][s2], o[j], 0, 0, 0);
+                            o[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[s2], xt[2][s2], o[j], 0, 0, 0);
+                        }
                     }
                 }
             }
@@ -1780,10 +1814,10 @@ __global__ __launch_bounds__(256) void nce_grad_cols_finish(NceGradArgs a, doubl
 // += sum over segments of O_t[c] - b[j_t][c], and db[j_t][c] -= a[i_t][c] (binary64
 // atomics; every addend is an fp32 value).  Pairs with an index out of range are
 // skipped.
-__global__ __launch_bounds__(256) void nce_grad_rows_finish(NceGradArgs a, const uint16_t* amap,
-                                                            const uint16_t* bmap, int64_t a_elems,
-                                                            int64_t b_elems, int32_t n1, int32_t n2, double* da,
-                                                            double* db) {
+template <typename T>
+__global__ __launch_bounds__(256) void nce_grad_rows_finish(NceGradArgs a, const T* amap, const T* bmap,
+                                                            int64_t a_elems, int64_t b_elems, int32_t n1, int32_t n2,
+                                                            double* da, double* db) {
     const int pair = blockIdx.y;
     for (int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x; x < (int64_t)a.nq * a.d; x += (int64_t)gridDim.x * 256) {
         const int64_t t = x / a.d;
@@ -2387,9 +2421,9 @@ struct NceGradLayout {
 
 // Segments of a gradient pass as for the forward: resident workgroups spread over the
 // query groups, at most one per streamed tile, a multiple of 8 when large.
-template <int P, bool COLS>
+template <int AR, int P, bool COLS>
 void grad_pass_shape(int batch, int64_t nq, int64_t nx, int& nseg, int& grid) {
-    const int g = grid_per_pair(resident_blocks<nce_grad_kernel<P, COLS>>(), batch);
+    const int g = grid_per_pair(resident_blocks<nce_grad_kernel<AR, P, COLS>>(), batch);
     const int64_t ntiles = (nx + 31) / 32;
     const int64_t qgroups = ((nq + 31) / 32 + kWaves * kGradQT - 1) / (kWaves * kGradQT);
     int64_t ns = qgroups > 0 ? g / qgroups : 1;
@@ -2404,9 +2438,27 @@ void grad_pass_shape(int batch, int64_t nq, int64_t nx, int& nseg, int& grid) {
 int validate_nce_grad(const mr_map* a, const mr_map* b, int64_t n_gt) {
     const int rc = validate_nce(a, b, n_gt);
     if (rc) return rc;
-    if (a->dtype != MR_BF16) return MR_ERR_DTYPE;
-    if (a->d > 32) return MR_ERR_SHAPE;
+    if (a->d > 32) return MR_ERR_SHAPE;   // fp32 maps are already held to d in {8, 16, 24, 32}
     return MR_OK;
+}
+
+// The gradient kernel instance for a map dtype and d (bf16: P = ceil(d / 16) steps;
+// fp32: the split arithmetic, P = 3d / 8), as integral constants to f.
+template <class F>
+int with_grad_arith(int dtype, int d, F&& f) {
+    using std::integral_constant;
+    if (dtype == MR_BF16) {
+        if (d <= 16) return f(integral_constant<int, AR_BF16>{}, integral_constant<int, 1>{});
+        if (d <= 32) return f(integral_constant<int, AR_BF16>{}, integral_constant<int, 2>{});
+        return MR_ERR_SHAPE;
+    }
+    switch (d) {
+        case 8: return f(integral_constant<int, AR_X3>{}, integral_constant<int, 3>{});
+        case 16: return f(integral_constant<int, AR_X3>{}, integral_constant<int, 6>{});
+        case 24: return f(integral_constant<int, AR_X3>{}, integral_constant<int, 9>{});
+        case 32: return f(integral_constant<int, AR_X3>{}, integral_constant<int, 12>{});
+        default: return MR_ERR_SHAPE;
+    }
 }
 
 int nce_grad_layout(const mr_map* a, const mr_map* b, int64_t n_gt, NceGradLayout& L) {
@@ -2414,13 +2466,13 @@ int nce_grad_layout(const mr_map* a, const mr_map* b, int64_t n_gt, NceGradLayou
     if (rc) return rc;
     const int64_t n1 = npix(a), n2 = npix(b);
     const int batch = a->batch;
-    if (a->d <= 16) {
-        grad_pass_shape<1, false>(batch, n_gt, n2, L.nseg_r, L.grid_r);
-        grad_pass_shape<1, true>(batch, n2, n_gt, L.nseg_c, L.grid_c);
-    } else {
-        grad_pass_shape<2, false>(batch, n_gt, n2, L.nseg_r, L.grid_r);
-        grad_pass_shape<2, true>(batch, n2, n_gt, L.nseg_c, L.grid_c);
-    }
+    const int rs = with_grad_arith(a->dtype, a->d, [&](auto ar, auto p) {
+        constexpr int AR = decltype(ar)::value, P = decltype(p)::value;
+        grad_pass_shape<AR, P, false>(batch, n_gt, n2, L.nseg_r, L.grid_r);
+        grad_pass_shape<AR, P, true>(batch, n2, n_gt, L.nseg_c, L.grid_c);
+        return (int)MR_OK;
+    });
+    if (rs) return rs;
     const size_t B = (size_t)batch, d = (size_t)a->d, ngt = (size_t)(n_gt > 0 ? n_gt : 1);
     size_t off = L.f.total;
     L.lse2 = off; off = align256(off + B * ngt * sizeof(float));
@@ -2476,20 +2528,29 @@ int infonce_backward_impl(const mr_map* a, const mr_map* b, const int32_t* gt, i
     c.qmap = b->data; c.xmap = a->data; c.q_pair_elems = n2 * d; c.x_pair_elems = n1 * d;
     c.nq_rows = (int32_t)n2; c.nx_rows = (int32_t)n1; c.nq = (int32_t)n2; c.nx = (int32_t)n_gt;
     c.nseg = L.nseg_c; c.partial = at<float>(ws, L.pcol);
-    bool rec = false;
-    if ((rc = prof_mark(st, rec))) return rc;
-    if (d <= 16) hipLaunchKernelGGL((nce_grad_kernel<1, false>), dim3(L.grid_r, batch), dim3(kThreads), 0, st, r);
-    else hipLaunchKernelGGL((nce_grad_kernel<2, false>), dim3(L.grid_r, batch), dim3(kThreads), 0, st, r);
-    if (dev_err() || (rc = prof_close(st, rec))) return rc ? rc : MR_ERR_DEVICE;
-    if ((rc = prof_mark(st, rec))) return rc;
-    if (d <= 16) hipLaunchKernelGGL((nce_grad_kernel<1, true>), dim3(L.grid_c, batch), dim3(kThreads), 0, st, c);
-    else hipLaunchKernelGGL((nce_grad_kernel<2, true>), dim3(L.grid_c, batch), dim3(kThreads), 0, st, c);
-    if (dev_err() || (rc = prof_close(st, rec))) return rc ? rc : MR_ERR_DEVICE;
+    rc = with_grad_arith(a->dtype, d, [&](auto ar, auto p) {
+        constexpr int AR = decltype(ar)::value, P = decltype(p)::value;
+        bool rec = false;
+        int e;
+        if ((e = prof_mark(st, rec))) return e;
+        hipLaunchKernelGGL((nce_grad_kernel<AR, P, false>), dim3(L.grid_r, batch), dim3(kThreads), 0, st, r);
+        if (dev_err()) return (int)MR_ERR_DEVICE;
+        if ((e = prof_close(st, rec)) || (e = prof_mark(st, rec))) return e;
+        hipLaunchKernelGGL((nce_grad_kernel<AR, P, true>), dim3(L.grid_c, batch), dim3(kThreads), 0, st, c);
+        if (dev_err()) return (int)MR_ERR_DEVICE;
+        return prof_close(st, rec);
+    });
+    if (rc) return rc;
     hipLaunchKernelGGL(nce_grad_cols_finish, dim3(grid_1d(n2 * d), batch), dim3(256), 0, st, c, db);
     if (dev_err()) return MR_ERR_DEVICE;
-    hipLaunchKernelGGL(nce_grad_rows_finish, dim3(grid_1d(n_gt * d), batch), dim3(256), 0, st, r,
-                       static_cast<const uint16_t*>(a->data), static_cast<const uint16_t*>(b->data), n1 * d, n2 * d,
-                       (int32_t)n1, (int32_t)n2, da, db);
+    if (a->dtype == MR_BF16)
+        hipLaunchKernelGGL(nce_grad_rows_finish<uint16_t>, dim3(grid_1d(n_gt * d), batch), dim3(256), 0, st, r,
+                           static_cast<const uint16_t*>(a->data), static_cast<const uint16_t*>(b->data), n1 * d,
+                           n2 * d, (int32_t)n1, (int32_t)n2, da, db);
+    else
+        hipLaunchKernelGGL(nce_grad_rows_finish<float>, dim3(grid_1d(n_gt * d), batch), dim3(256), 0, st, r,
+                           static_cast<const float*>(a->data), static_cast<const float*>(b->data), n1 * d, n2 * d,
+                           (int32_t)n1, (int32_t)n2, da, db);
     if (dev_err()) return MR_ERR_DEVICE;
     const double inv_tau = 1.0 / (double)tau;
     if (n1 > 0)

@@ -231,15 +231,15 @@ int mr_infonce_forward(const mr_map* a, const mr_map* b, const int32_t* gt, int6
  *     grad_b[k] = (1/tau) sum_t p[t][k] a[i_t] - (1/tau) sum_{t: j_t = k} a[i_t],
  * the gradient of that pair's loss (a sum over its terms); rows of a that no
  * ground-truth pair names get 0.
- *   a, b   : bf16 maps (else MR_ERR_DTYPE) with d <= 32 (else MR_ERR_SHAPE);
- *            otherwise as mr_infonce_forward.
+ *   a, b   : as mr_infonce_forward, with d <= 32 (else MR_ERR_SHAPE): bf16
+ *            maps, or fp32 maps with d in {8, 16, 24, 32}.
  *   grad_a : [batch][h_a][w_a][d] fp32 (may be NULL only when a has no rows);
  *   grad_b : [batch][h_b][w_b][d] fp32.
  *   ws     : mr_workspace_bytes(MR_OP_INFONCE_BACKWARD, a, b, n_gt, 0, 0) bytes
  *            (unused when n_gt = 0).
  * The softmax-weighted sums are formed on the matrix cores with each softmax
- * value split into two bf16 parts (relative error below 2^-17) and fp32
- * accumulation; rows that several ground-truth pairs share are accumulated with
+ * value split into two bf16 parts (relative error below 2^-17), fp32 map rows
+ * split exactly into three, and fp32 accumulation; rows that several ground-truth pairs share are accumulated with
  * binary64 atomic adds of fp32 values before the final scaling and rounding, so
  * the result can differ between runs only where such a sum rounds in binary64.
  * A ground-truth pair with an index out of range makes that image pair's loss

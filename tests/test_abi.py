@@ -221,17 +221,20 @@ def test_infonce_validation(lib):
 
 
 def test_infonce_backward_validation(lib):
-    """The gradient call takes bf16 maps with d <= 32 and rejects what the forward rejects."""
+    """The gradient call takes d <= 32 (fp32: d in {8, 16, 24, 32}) and rejects what the
+    forward rejects."""
     out = ctypes.c_void_p(FAKE)
     a, b = M(10, 10, d=24, dtype=1), M(7, 9, d=24, dtype=1)
     need = lib.mr_workspace_bytes(8, R(a), R(b), 50, 0, 0)
     assert need > lib.mr_workspace_bytes(7, R(a), R(b), 50, 0, 0) > 0
-    assert lib.mr_workspace_bytes(8, R(M(10, 10, d=24)), R(M(7, 9, d=24)), 50, 0, 0) == 0
+    assert lib.mr_workspace_bytes(8, R(M(10, 10, d=24)), R(M(7, 9, d=24)), 50, 0, 0) > 0
+    assert lib.mr_workspace_bytes(8, R(M(10, 10, d=20)), R(M(7, 9, d=20)), 50, 0, 0) == 0
     assert lib.mr_workspace_bytes(8, R(M(10, 10, d=40, dtype=1)), R(M(7, 9, d=40, dtype=1)), 50, 0, 0) == 0
     ws = ctypes.c_void_p(FAKE)
     call = lambda a_=a, b_=b, gt=out, n=50, tau=0.1, terms=out, loss=out, ga=out, gb=out, wsb=need: \
         lib.mr_infonce_backward(R(a_), R(b_), gt, n, tau, terms, loss, ga, gb, ws, wsb, None)
-    assert call(a_=M(10, 10, d=24), b_=M(7, 9, d=24)) == DTYPE
+    assert call(a_=M(10, 10, d=24), b_=M(7, 9, d=24, dtype=1)) == DTYPE
+    assert call(a_=M(10, 10, d=20), b_=M(7, 9, d=20)) == SHAPE
     assert call(a_=M(10, 10, d=40, dtype=1), b_=M(7, 9, d=40, dtype=1)) == SHAPE
     assert call(a_=M(0, 10, d=24, dtype=1, data=None)) == SHAPE
     for tau in (0.0, float("nan"), float("inf")):

@@ -36,15 +36,20 @@ def log(*a):
     print(*a, flush=True)
 
 
-def bf16_pair(rng, n1, n2, d):
+def bf16_pair(rng, n1, n2, d, dtype="bf16"):
+    """Unit rows; for bf16 the oracle reads the exactly widened values.  Returns the fp32
+    arrays and the arrays the device gets (bf16 bit patterns, or the fp32 arrays)."""
     A = workloads.unit_rows(rng, n1, d).astype(np.float32)
     B = workloads.unit_rows(rng, n2, d).astype(np.float32)
+    if dtype == "f32":
+        return A, B, A, B
     ba, bb = workloads.f32_to_bf16_bits(A), workloads.f32_to_bf16_bits(B)
     return workloads.bf16_bits_to_f32(ba), workloads.bf16_bits_to_f32(bb), ba, bb
 
 
-def dev_bits(bits, H, W):
-    return torch.from_numpy(np.ascontiguousarray(bits).reshape(H, W, -1)).view(torch.bfloat16).to(DEV)
+def dev_bits(arr, H, W):
+    t = torch.from_numpy(np.ascontiguousarray(arr).reshape(H, W, -1))
+    return (t.view(torch.bfloat16) if arr.dtype == np.int16 else t).to(DEV)
 
 
 def run(bits_a, bits_b, gt, tau, H1, W1, H2, W2):
@@ -74,27 +79,30 @@ def check_grads(ga, gb, A, B, gt, tau, b_rows=None, a_rows=None):
     return float((ea / np.maximum(tol_a, 1e-30)).max()), float((eb / tol_b).max())
 
 
-def test_grad_tiny_planted():
-    """64x48 planted bf16 pair, every non-occluded pixel of image 2 as ground truth."""
-    p = workloads.make_pair(64, 48, 24, 0, warp="shift", sigma=0.1, rho=0.2, dtype="bf16")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_grad_tiny_planted(dtype):
+    """64x48 planted pair, every non-occluded pixel of image 2 as ground truth."""
+    p = workloads.make_pair(64, 48, 24, 0, warp="shift", sigma=0.1, rho=0.2, dtype=dtype)
     gt = workloads.gt_pairs(p)
-    terms, loss, ga, gb = run(p.D1_bits, p.D2_bits, gt, 0.1, p.H, p.W, p.H, p.W)
+    da, db = (p.D1_bits, p.D2_bits) if dtype == "bf16" else (p.D1, p.D2)
+    terms, loss, ga, gb = run(da, db, gt, 0.1, p.H, p.W, p.H, p.W)
     ra, rb = check_grads(ga, gb, p.D1, p.D2, gt, 0.1)
-    log("grad tiny", len(gt), "err/tol", ra, rb)
+    log("grad tiny", dtype, len(gt), "err/tol", ra, rb)
 
 
-@pytest.mark.parametrize("d", [8, 16, 24, 32])
-def test_grad_ragged(d):
+@pytest.mark.parametrize("dtype,d", [("bf16", 8), ("bf16", 16), ("bf16", 24), ("bf16", 32), ("f32", 8), ("f32", 16),
+                                     ("f32", 24), ("f32", 32)])
+def test_grad_ragged(dtype, d):
     """37x29 against 23x41 pixels (ragged tiles), 517 pairs with repeated rows on both sides."""
     rng = np.random.default_rng(200 + d)
-    A, B, ba, bb = bf16_pair(rng, 37 * 29, 23 * 41, d)
+    A, B, ba, bb = bf16_pair(rng, 37 * 29, 23 * 41, d, dtype)
     n_gt = 517
     gt = np.stack([rng.integers(0, len(A), n_gt), rng.integers(0, len(B), n_gt)], axis=1).astype(np.int32)
     gt[5:9, 0] = gt[4, 0]
     gt[20:25, 1] = gt[19, 1]
     terms, loss, ga, gb = run(ba, bb, gt, 0.1, 37, 29, 23, 41)
     ra, rb = check_grads(ga, gb, A, B, gt, 0.1)
-    log("grad ragged", d, "err/tol", ra, rb)
+    log("grad ragged", dtype, d, "err/tol", ra, rb)
 
 
 @pytest.mark.parametrize("n_gt", [1, 5, 33, 3000])
@@ -132,18 +140,20 @@ def test_grad_empty_ground_truth():
     assert float(loss[0].cpu()) == 0.0 and not ga.any() and not gb.any()
 
 
-def test_grad_full_size_sampled():
-    """512x384 bf16 maps with 2048 ground-truth pairs of the planted field: every named row
-    of dA and 512 sampled rows of dB against the oracle."""
-    p = workloads.config_pair(2)
+@pytest.mark.parametrize("cfg", [2, 1])
+def test_grad_full_size_sampled(cfg):
+    """512x384 maps (bf16, then fp32) with 2048 ground-truth pairs of the planted field:
+    every named row of dA and 512 sampled rows of dB against the oracle."""
+    p = workloads.config_pair(cfg)
     gt_all = workloads.gt_pairs(p)
     rng = np.random.default_rng(6)
     gt = gt_all[np.sort(rng.choice(len(gt_all), 2048, replace=False))]
-    terms, loss, ga, gb = run(p.D1_bits, p.D2_bits, gt, 0.1, p.H, p.W, p.H, p.W)
+    da, db = (p.D1_bits, p.D2_bits) if p.dtype == "bf16" else (p.D1, p.D2)
+    terms, loss, ga, gb = run(da, db, gt, 0.1, p.H, p.W, p.H, p.W)
     b_rows = np.sort(np.concatenate([rng.choice(p.N, 448, replace=False), gt[:64, 1]])).astype(np.int32)
     a_rows = np.unique(gt[:, 0])
     ra, rb = check_grads(ga, gb, p.D1, p.D2, gt, 0.1, b_rows=b_rows, a_rows=a_rows)
-    log("grad 512x384", "err/tol", ra, rb)
+    log("grad 512x384", p.dtype, "err/tol", ra, rb)
 
 
 def test_grad_bench_size_invariants():
