@@ -252,8 +252,9 @@ int mr_infonce_backward(const mr_map* a, const mr_map* b, const int32_t* gt, int
 /* ---------------------------------------------------------------------------
  * Measurement aid (not thread-safe; one profiling window per process).
  * mr_profile_begin(n): from now on, record a pair of hipEvents on the call's
- * stream around every launch of the similarity/argmax kernel, for up to n
- * launches.  mr_profile_end: wait for those events, return the summed kernel
+ * stream around every launch of the similarity/argmax kernel (both metrics),
+ * of the matching loss's log-sum-exp kernel (mr_infonce_forward) and of the two
+ * gradient passes (mr_infonce_backward), for up to n launches.  mr_profile_end: wait for those events, return the summed kernel
  * time in milliseconds and the number of launches timed, release the events.
  * --------------------------------------------------------------------------- */
 int mr_profile_begin(int32_t max_launches);
