@@ -22,6 +22,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "image pairs/sec fast reciprocal NN @512×384 d=24; NN-queries/sec; %MFMA peak"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense matrix-core peaks
+PEAK_HBM_GBPS = 8000.0
 # fp32 VALU lane-operations per second: the published fp32 vector peak, 157.3 TFLOP/s,
 # is 78.6 T fused multiply-adds per second (32 fp32 lanes per SIMD per clock, 256 CUs x
 # 4 SIMDs x 2.4 GHz, twice the fp64 rate); a plain fp32 VALU operation (subtract,
@@ -72,7 +73,7 @@ def dev_maps(p, torch, dev):
     return A.to(dev).unsqueeze(0), B.to(dev).unsqueeze(0)
 
 
-def time_steps(fn, steps, warmup, torch, prof_launches=0):
+def time_steps(fn, steps, warmup, torch, prof_launches=0, each=None):
     """Warm up, then time exactly `steps` calls between two synchronisations with nothing
     else on the stream.  With prof_launches, the same steps run once more with the
     library's per-launch hipEvents on (they cost a few microseconds per launch, so they
@@ -96,7 +97,11 @@ def time_steps(fn, steps, warmup, torch, prof_launches=0):
         for _ in range(steps):
             fn()
         torch.cuda.synchronize()
-        kms, kn = mr.profile_end()
+        if each is None:
+            kms, kn = mr.profile_end()
+        else:
+            kms, kn, per = mr.profile_end_each(prof_launches)
+            each.extend(per)
     return ms, kms, kn
 
 
@@ -143,13 +148,38 @@ def run_fast(p, batch_pairs, args, torch, dev, prof=True, point=False):
         A, B = batch_pairs
     f = mr.FastReciprocal(A, B, p.stride, p.offset, p.max_iters, point=point)
     launches = 2 * p.max_iters * args.steps
-    ms, kms, kn = time_steps(lambda: f(A, B), args.steps, args.warmup, torch, launches if prof else 0)
+    each = []
+    ms, kms, kn = time_steps(lambda: f(A, B), args.steps, args.warmup, torch, launches if prof else 0, each)
     pairs, n_pairs, active = f(A, B)
     torch.cuda.synchronize()
     act = active.cpu().numpy()
     q, flops = fast_work(act, p.N, p.d)
-    return dict(ms=ms, kernel_ms=kms, launches=kn, nn_queries=q, flops=flops,
+    return dict(ms=ms, kernel_ms=kms, launches=kn, nn_queries=q, flops=flops, each=each,
                 active=act[0].tolist(), matches=[int(x) for x in n_pairs.cpu()], batch=A.shape[0])
+
+
+def rounds_roofline(r, N, d, elem_bytes, peak_tflops):
+    """Per round of the fast scheme: its two similarity launches' measured time (averaged
+    over the timed calls) against the round's lower bound max(flops / matrix peak,
+    bytes / HBM), flops 4*|U_t|*N*d and bytes two map reads of N*d elements; overall,
+    the summed bounds over the summed kernel time."""
+    each, act = r["each"], r["active"]
+    per_call = 2 * len(act)
+    if not each or len(each) % per_call:
+        return None
+    calls = len(each) // per_call
+    out, lb_sum, t_sum = [], 0.0, 0.0
+    for t, u in enumerate(act):
+        ms = sum(each[c * per_call + 2 * t] + each[c * per_call + 2 * t + 1] for c in range(calls)) / calls
+        fl = 4.0 * u * N * d
+        by = 2.0 * N * d * elem_bytes if u else 0.0
+        lb = max(fl / (peak_tflops * 1e12), by / (PEAK_HBM_GBPS * 1e9)) * 1e3
+        lb_sum += lb
+        t_sum += ms
+        out.append({"t": t, "active": int(u), "ms": round(ms, 4), "lb_ms": round(lb, 4),
+                    "frac": round(lb / ms, 4) if ms > 0 else None})
+    return {"rounds": out, "lb_ms": round(lb_sum, 4), "kernel_ms": round(t_sum, 4),
+            "frac": round(lb_sum / t_sum, 4) if t_sum else None}
 
 
 def measured_traffic(name):
@@ -450,6 +480,7 @@ def main():
         "roofline": roofline(r["flops"], args.steps, r["kernel_ms"], r["launches"], "f32",
                              measured_traffic("nn_argmax_pair512x384_f32_traffic.json")),
         "step_mfma_frac": round(r["flops"] / (r["ms"] * 1e-3) / 1e12 / PEAK_TFLOPS["f32"], 4),
+        "binding_roof_by_round": rounds_roofline(r, p.N, p.d, 4, PEAK_TFLOPS["f32"]),
     }
     f1 = mr.FastReciprocal(*dev_maps(p, torch, dev), p.stride, p.offset, p.max_iters)
     A1, B1 = dev_maps(p, torch, dev)

@@ -31,7 +31,7 @@ STATUS = {0: "MR_OK", 1: "MR_ERR_NULL", 2: "MR_ERR_SHAPE", 3: "MR_ERR_DTYPE", 4:
 EXPORTS = ("mr_workspace_bytes", "mr_status_str", "mr_seed_count", "mr_nn_argmax", "mr_mutual_nn",
            "mr_fast_reciprocal", "mr_fast_reciprocal_graph", "mr_point_nn", "mr_point_mutual_nn",
            "mr_point_fast_reciprocal", "mr_infonce_forward", "mr_infonce_backward",
-           "mr_profile_begin", "mr_profile_end")
+           "mr_profile_begin", "mr_profile_end", "mr_profile_end_each")
 
 
 class MrMap(ctypes.Structure):
@@ -86,6 +86,8 @@ def load_library(path: str = LIB_PATH):
     lib.mr_profile_begin.restype = ctypes.c_int
     lib.mr_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64)]
     lib.mr_profile_end.restype = ctypes.c_int
+    lib.mr_profile_end_each.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), P, i32]
+    lib.mr_profile_end_each.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -399,3 +401,13 @@ def profile_end():
     n = ctypes.c_int64(0)
     _check("mr_profile_end", load_library().mr_profile_end(ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def profile_end_each(cap: int):
+    """Returns (summed milliseconds, launches timed, list of each launch's milliseconds
+    in launch order, at most cap of them)."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    each = (ctypes.c_float * max(1, cap))()
+    _check("mr_profile_end_each", load_library().mr_profile_end_each(ctypes.byref(ms), ctypes.byref(n), each, cap))
+    return ms.value, n.value, [float(x) for x in each[:min(cap, n.value)]]

@@ -2705,8 +2705,8 @@ int mr_profile_begin(int32_t max_launches) {
     return MR_OK;
 }
 
-int mr_profile_end(double* total_ms, int64_t* launches) {
-    if (!g_prof.on) return MR_ERR_PARAM;
+int mr_profile_end_each(double* total_ms, int64_t* launches, float* each_ms, int32_t cap) {
+    if (!g_prof.on || cap < 0 || (cap > 0 && !each_ms)) return MR_ERR_PARAM;
     double tot = 0.0;
     int rc = MR_OK;
     for (int i = 0; i < g_prof.used; ++i) {
@@ -2715,6 +2715,7 @@ int mr_profile_end(double* total_ms, int64_t* launches) {
             hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess)
             rc = MR_ERR_DEVICE;
         tot += ms;
+        if (i < cap) each_ms[i] = ms;
     }
     for (int i = 0; i < 2 * g_prof.cap; ++i) (void)hipEventDestroy(g_prof.ev[i]);
     free(g_prof.ev);
@@ -2722,6 +2723,10 @@ int mr_profile_end(double* total_ms, int64_t* launches) {
     if (launches) *launches = g_prof.used;
     g_prof = Profiler();
     return rc;
+}
+
+int mr_profile_end(double* total_ms, int64_t* launches) {
+    return mr_profile_end_each(total_ms, launches, nullptr, 0);
 }
 
 }  // extern "C"

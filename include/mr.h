@@ -254,11 +254,16 @@ int mr_infonce_backward(const mr_map* a, const mr_map* b, const int32_t* gt, int
  * mr_profile_begin(n): from now on, record a pair of hipEvents on the call's
  * stream around every launch of the similarity/argmax kernel (both metrics),
  * of the matching loss's log-sum-exp kernel (mr_infonce_forward) and of the two
- * gradient passes (mr_infonce_backward), for up to n launches.  mr_profile_end: wait for those events, return the summed kernel
- * time in milliseconds and the number of launches timed, release the events.
+ * gradient passes (mr_infonce_backward), for up to n launches.
+ * mr_profile_end: wait for those events, return the summed kernel time in
+ * milliseconds and the number of launches timed, release the events.
+ * mr_profile_end_each: the same, and also each launch's time in milliseconds,
+ * in launch order, into each_ms[0 .. min(cap, launches)) (cap >= 0; each_ms may
+ * be NULL only when cap = 0).  Both return MR_ERR_PARAM without an open window.
  * --------------------------------------------------------------------------- */
 int mr_profile_begin(int32_t max_launches);
 int mr_profile_end(double* total_ms, int64_t* launches);
+int mr_profile_end_each(double* total_ms, int64_t* launches, float* each_ms, int32_t cap);
 
 #ifdef __cplusplus
 }

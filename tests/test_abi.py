@@ -145,6 +145,8 @@ def test_profile_end_without_begin(lib):
     ms = ctypes.c_double()
     n = ctypes.c_int64()
     assert lib.mr_profile_end(ctypes.byref(ms), ctypes.byref(n)) == PARAM
+    each = (ctypes.c_float * 4)()
+    assert lib.mr_profile_end_each(ctypes.byref(ms), ctypes.byref(n), each, 4) == PARAM
 
 
 def test_point_validation(lib):
