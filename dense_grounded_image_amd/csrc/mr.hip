@@ -17,6 +17,10 @@
 //    keep cycle-consistent pairs, restart the rest where they landed ("DUSt3R
 //    and MASt3R explained", the paragraph on MASt3R's fast reciprocal
 //    matching).
+//  - The matching loss the descriptors are trained with, InfoNCE over
+//    ground-truth pairs ("MASt3R dissection", section 3), and its gradient: the
+//    same similarity tiles with a log-sum-exp epilogue (lse_partial_kernel), and
+//    softmax-weighted sums formed on the matrix cores (nce_grad_kernel).
 //
 // Layout of the MFMA operands (wave64, 32x32 output tile):
 //  - lane l holds output column j = l & 31 (a query) and the 16 rows
@@ -515,8 +519,8 @@ template <int AR, int P> constexpr int lds_row_bytes() {        // a staged row 
 // One workgroup streams 32-row database tiles through a double-buffered LDS stage
 // (one cooperative 16-byte-chunk copy per tile, one barrier per tile); each of its
 // four waves multiplies the staged tile against its own QT query tiles held in
-// registers and keeps a per-lane running best.
-// The per-lane state ep (one of the epilogue states above) takes each product tile.
+// registers; the per-lane state ep (one of the epilogue states above) takes each
+// product tile.
 template <int AR, int P, int QT, class Ep>
 __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb,
                                              char* lds, const Operand<AR, P> (&q)[QT],
@@ -627,8 +631,8 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
 // One workgroup streams its database segment (bf16 rows) through a ring of three LDS
 // stages of S tiles: global loads are issued two stages ahead of their LDS write,
 // one barrier per stage.  Each wave multiplies the staged tiles against its own
-// nact query tiles held in registers and keeps a per-lane running best (epilogue
-// EP).  Loads and LDS writes are issued unconditionally -- stage indices past the
+// nact query tiles held in registers and hands each product tile to the per-lane
+// state ep.  Loads and LDS writes are issued unconditionally -- stage indices past the
 // end clamp to the last stage, chunks past the map's last row to that row's last
 // chunk -- so that the compiler counts outstanding loads exactly and waits only for
 // the oldest stage.  LDS rows past the map's end hold stale (finite) data; the
