@@ -390,6 +390,7 @@ enum Epilogue { EP_KEY = 0, EP_EXACT = 1, EP_TILE = 2, EP_LSE = 3 };
 // Keyed row maximum: (score, row) of the NN while the lane's best score is >= 0.
 template <int QT> struct KeyBest {
     static constexpr int kind = EP_KEY;
+    static constexpr int valu = 27;   // vector instructions per tile, for scheduling
     int bk[QT], bt[QT];
     __device__ __forceinline__ KeyBest() {
 #pragma unroll
@@ -431,6 +432,7 @@ template <int QT> struct ExactBest {
 // Tile-level maximum: best compared score and the first tile reaching it.
 template <int QT> struct TileBest {
     static constexpr int kind = EP_TILE;
+    static constexpr int valu = 12;   // vector instructions per tile, for scheduling
     float bv[QT];
     int bt[QT];
     __device__ __forceinline__ TileBest() {
@@ -459,6 +461,7 @@ template <int QT> struct TileBest {
 // so its error stays at a few units of fp32 rounding however long the segment.
 template <int QT> struct LseSum {
     static constexpr int kind = EP_LSE;
+    static constexpr int valu = 64;   // vector instructions per tile, for scheduling
     float m[QT], s[QT], c[QT];
     float k2;
     __device__ __forceinline__ explicit LseSum(float k2_) : k2(k2_) {
@@ -514,6 +517,19 @@ template <int AR, int P> constexpr int max_row_bytes() {        // a map row in 
 }
 template <int AR, int P> constexpr int lds_row_bytes() {        // a staged row (X3: three planes)
     return AR == AR_X3 ? 16 * P : max_row_bytes<AR, P>();
+}
+
+// Scheduling hint for a loop body of N matrix instructions: issue each one followed by
+// V vector instructions.  A wave issues in order, and one that reaches a matrix
+// instruction while the matrix core is busy stalls there; vector work placed between
+// the matrix instructions of the same wave runs while they execute.
+template <int N, int V>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, V, 0);   // then V VALU
+    }
 }
 
 // One workgroup streams 32-row database tiles through a double-buffered LDS stage
@@ -577,6 +593,24 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
         }
     };
 
+    // Full tiles of the split contraction with keyed epilogues run one (tile, query
+    // tile) unit behind: the products of unit n are issued with the epilogue of unit
+    // n - 1 between them, so the vector work runs while the matrix core is busy.  The
+    // pending unit is (lag, lag_t, query tile QT - 1) across tiles.  Applying a unit to
+    // a keyed state twice changes nothing (the comparison is strict, against the key
+    // with its low bits set), so the first full tile's stand-in (all scores -inf,
+    // whose keys are negative and never beat a lane's best once it is >= 0; a lane
+    // whose best stays negative is recomputed exactly) needs no special case either.
+    f32x16 lag;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) lag[v] = -INFINITY;
+    int lag_t = t0;
+    bool pending = false;
+    auto flush = [&]() {
+        if (pending) ep.template tile<false>(lag, lag_t, h, ndb, QT - 1);
+        pending = false;
+    };
+
     auto compute = [&](int i) {
         const int t = t0 + i;
         const bool ragged = (t + 1) * 32 > ndb;
@@ -584,19 +618,22 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
         r.load(lds + (i & 1) * BUF, jl, true, h, d, role);
         if constexpr (AR == AR_X3 && Ep::kind == EP_KEY) {
             if (nact == QT && !ragged) {
-                // the query tiles' step chains interleaved: consecutive products are
-                // independent, so none waits for the one before it
-                f32x16 acc[QT];
 #pragma unroll
-                for (int j = 0; j < QT; ++j) acc[j] = f32x16{};
+                for (int j = 0; j < QT; ++j) {
+                    f32x16 acc = {};
 #pragma unroll
-                for (int st = 0; st < P; ++st)
-#pragma unroll
-                    for (int j = 0; j < QT; ++j) acc[j] = r.step(st, q[j], acc[j]);
-#pragma unroll
-                for (int j = 0; j < QT; ++j) ep.template tile<false>(acc[j], t, h, ndb, j);
+                    for (int st = 0; st < P; ++st) acc = r.step(st, q[j], acc);
+                    if (j > 0) ep.template tile<false>(lag, t, h, ndb, j - 1);
+                    else ep.template tile<false>(lag, lag_t, h, ndb, QT - 1);
+                    lag = acc;
+                    interleave_mfma_valu<P, (Ep::valu + P - 1) / P>();
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                lag_t = t;
+                pending = true;
                 return;
             }
+            flush();
         }
 #pragma unroll
         for (int j = 0; j < QT; ++j) {
@@ -626,6 +663,7 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
         if (i + 2 < nt) put(0, stage0);
         __syncthreads();
     }
+    if constexpr (AR == AR_X3 && Ep::kind == EP_KEY) flush();
 }
 
 // One workgroup streams its database segment (bf16 rows) through a ring of three LDS
@@ -774,14 +812,27 @@ __device__ __forceinline__ void stream_regs(const void* dbase, int t0, int t1,
     };
     // whole groups of D tiles: no branch inside, refills clamped, so the compiler
     // counts outstanding loads exactly
+    // Inside a group the epilogue runs one (tile, query tile) unit behind the matrix
+    // products: the products of unit n are issued, then the epilogue of unit n - 1,
+    // whose results are complete by then, fills the matrix core's busy cycles.
     int t = t0;
     for (; t + D <= t1; t += D) {
+        f32x16 prev;
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            compute(r[u], t + u);
+#pragma unroll
+            for (int j = 0; j < QT; ++j) {
+                const f32x16 acc = r[u].mfma(q[j], f32x16{});
+                if (j > 0) ep.template tile<false>(prev, t + u, h, 0, j - 1);
+                else if (u > 0) ep.template tile<false>(prev, t + u - 1, h, 0, QT - 1);
+                prev = acc;
+                interleave_mfma_valu<P, (Ep::valu + P - 1) / P>();
+                __builtin_amdgcn_sched_barrier(0);
+            }
             const int tn = t + u + D < tlast ? t + u + D : tlast;
             r[u].load_db(dbytes + tn * tile_bytes, off);
         }
+        ep.template tile<false>(prev, t + D - 1, h, 0, QT - 1);
     }
     // the last t1 - t < D tiles are already in the ring
 #pragma unroll
