@@ -186,17 +186,20 @@ __host__ __device__ __forceinline__ constexpr int x3_plane(int role, int p) {
                      : (p == 1 || p == 5 ? 1 : (p == 3 ? 2 : 0));
 }
 
-// Exact split of an fp32 value into three bf16 parts v = h + m + l (round to nearest
-// even at each step; each difference is exact in fp32).
-__device__ __forceinline__ void split3(float v, uint16_t& hb, uint16_t& mb, uint16_t& lb) {
-    const __bf16 h = (__bf16)v;
-    const float r1 = v - (float)h;
-    const __bf16 m = (__bf16)r1;
-    const float r2 = r1 - (float)m;
-    const __bf16 l = (__bf16)r2;
-    hb = __builtin_bit_cast(uint16_t, h);
-    mb = __builtin_bit_cast(uint16_t, m);
-    lb = __builtin_bit_cast(uint16_t, l);
+// Exact split of fp32 values into three bf16 parts v = h + m + l (round to nearest
+// even at each step; each difference is exact in fp32), for four values at once: each
+// plane comes out as two words of two bf16 (value 2i in the low half).  A conversion
+// rounds a pair of values, each exactly as a scalar conversion would.
+__device__ __forceinline__ void split3x4(float v0, float v1, float v2, float v3, uint2 (&pl)[3]) {
+    f32x2 a = {v0, v1}, b = {v2, v3};
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const bf16x2 ha = __builtin_convertvector(a, bf16x2);
+        const bf16x2 hb = __builtin_convertvector(b, bf16x2);
+        pl[k] = uint2{__builtin_bit_cast(uint32_t, ha), __builtin_bit_cast(uint32_t, hb)};
+        a = a - __builtin_convertvector(ha, f32x2);
+        b = b - __builtin_convertvector(hb, f32x2);
+    }
 }
 
 // P = 6d/16 steps (d = 8P/3); slot q = 16*s + 8*h + e holds product type q / d and
@@ -228,15 +231,12 @@ template <int P> struct Operand<AR_X3, P> {
 #pragma unroll
         for (int i = 0; i < D / 4; ++i) {
             const float4 v = valid ? reinterpret_cast<const float4*>(rowp)[i] : float4{0.f, 0.f, 0.f, 0.f};
-            uint16_t a[3][4];
-            split3(v.x, a[0][0], a[1][0], a[2][0]);
-            split3(v.y, a[0][1], a[1][1], a[2][1]);
-            split3(v.z, a[0][2], a[1][2], a[2][2]);
-            split3(v.w, a[0][3], a[1][3], a[2][3]);
+            uint2 a[3];
+            split3x4(v.x, v.y, v.z, v.w, a);
 #pragma unroll
             for (int k = 0; k < 3; ++k) {
-                pl[k][2 * i] = (uint32_t)a[k][0] | ((uint32_t)a[k][1] << 16);
-                pl[k][2 * i + 1] = (uint32_t)a[k][2] | ((uint32_t)a[k][3] << 16);
+                pl[k][2 * i] = a[k].x;
+                pl[k][2 * i + 1] = a[k].y;
             }
         }
 #pragma unroll
@@ -578,14 +578,12 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
                     // four fp32 components -> their h, m, l bf16 in the row's three planes
                     constexpr int D = 8 * P / 3;
                     const int r = ch / (D / 4), c0 = (ch - r * (D / 4)) * 4;
-                    uint16_t a[3][4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) split3(__uint_as_float(stage[c][e]), a[0][e], a[1][e], a[2][e]);
+                    uint2 a[3];
+                    split3x4(__uint_as_float(stage[c][0]), __uint_as_float(stage[c][1]),
+                             __uint_as_float(stage[c][2]), __uint_as_float(stage[c][3]), a);
                     char* dst = lds + buf * BUF + r * 6 * D + c0 * 2;
 #pragma unroll
-                    for (int k = 0; k < 3; ++k)
-                        *reinterpret_cast<uint2*>(dst + k * 2 * D) =
-                            uint2{(uint32_t)a[k][0] | ((uint32_t)a[k][1] << 16), (uint32_t)a[k][2] | ((uint32_t)a[k][3] << 16)};
+                    for (int k = 0; k < 3; ++k) *reinterpret_cast<uint2*>(dst + k * 2 * D) = a[k];
                 } else {
                     *reinterpret_cast<u32x4*>(lds + buf * BUF + ch * 16) = stage[c];
                 }
@@ -1729,15 +1727,12 @@ void nce_grad_kernel(NceGradArgs a) {
                 if constexpr (AR == AR_X3) {
                     // four fp32 components -> their h, m, l parts in the row's three planes
                     const int r = threadIdx.x / (d / 4), c0 = (threadIdx.x - r * (d / 4)) * 4;
-                    uint16_t e3[3][4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) split3(__uint_as_float(v[e]), e3[0][e], e3[1][e], e3[2][e]);
+                    uint2 e3[3];
+                    split3x4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]),
+                             __uint_as_float(v[3]), e3);
                     char* dst = lds + buf * TILE + r * 6 * d + c0 * 2;
 #pragma unroll
-                    for (int k = 0; k < 3; ++k)
-                        *reinterpret_cast<uint2*>(dst + k * 2 * d) =
-                            uint2{(uint32_t)e3[k][0] | ((uint32_t)e3[k][1] << 16),
-                                  (uint32_t)e3[k][2] | ((uint32_t)e3[k][3] << 16)};
+                    for (int k = 0; k < 3; ++k) *reinterpret_cast<uint2*>(dst + k * 2 * d) = e3[k];
                 } else {
                     *reinterpret_cast<u32x4*>(lds + buf * TILE + threadIdx.x * 16) = v;
                 }
