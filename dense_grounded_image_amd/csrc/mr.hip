@@ -451,17 +451,22 @@ template <int QT> struct TileBest {
 
 // Online log-sum-exp of a query's scores over the database rows (the softmax
 // normaliser of the matching loss), in base 2: with k2 = log2(e) / tau and
-// z = score * k2, the state is m = the largest z seen (each z rounded once to fp32)
-// and s = the sum over the rows seen of 2^(z - m), each exponent formed as
-// fma(score, k2, -m) (one rounding, at most 0 up to that rounding, so no term
-// overflows; a term below the fp32 range is below 2^-126 of the largest).  When a
-// tile raises m, s is rescaled by 2^(m_old - m_new), which is exactly 1 while m
-// stays (a rescale by the rounding error of score * k2 at every tile would bias s
-// over thousands of tiles).  s is a compensated (Kahan) sum with compensation c,
-// so its error stays at a few units of fp32 rounding however long the segment.
+// z = score * k2, the state is an integer offset m and s = the sum over the rows seen
+// of 2^(z - m), each exponent formed as fma(score, k2, -m) (one rounding).  m starts
+// at -inf and is raised only when a tile's terms would sum past 2^64 (the first tile,
+// or a rise of the scores by more than 64 / k2): it becomes the integer just above
+// the tile's largest z, and s is rescaled by 2^(m_old - m_new), an exact power of
+// two.  Between raises the terms may exceed 1 (by at most 2^64 per tile), so s needs
+// no per-tile maximum, rescale or second exponential; a raise recomputes that tile's
+// terms.  s is a compensated (Kahan) sum with compensation c, so its error stays at a
+// few units of fp32 rounding however long the segment.
+__device__ __forceinline__ float scale_pow2(float x, float e) {   // x * 2^e, e an integer
+    return __builtin_ldexpf(x, (int)e);
+}
+
 template <int QT> struct LseSum {
     static constexpr int kind = EP_LSE;
-    static constexpr int valu = 64;   // vector instructions per tile, for scheduling
+    static constexpr int valu = 52;   // vector instructions per tile, for scheduling
     float m[QT], s[QT], c[QT];
     float k2;
     __device__ __forceinline__ explicit LseSum(float k2_) : k2(k2_) {
@@ -473,30 +478,43 @@ template <int QT> struct LseSum {
         float k[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) k[v] = (RAGGED && t * 32 + tile_row(v, h) >= ndb) ? -INFINITY : acc[v];
-        auto mx3 = [](float a, float b, float c) {
-            return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+        auto terms = [&](float off) {
+            float e[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) e[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(k[v], k2, off));
+#pragma unroll
+            for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+                for (int v = 0; v < w; ++v) e[v] += e[v + w];
+            return e[0];
         };
-        const float m0 = mx3(k[0], k[1], k[2]), m1 = mx3(k[3], k[4], k[5]), m2 = mx3(k[6], k[7], k[8]);
-        const float m3 = mx3(k[9], k[10], k[11]), m4 = mx3(k[12], k[13], k[14]);
-        const float mt = mx3(mx3(m1, m2, m3), m4, __builtin_elementwise_maximum(k[15], m0));
-        const float mn = __builtin_elementwise_maximum(m[j], mt * k2);   // rounding is monotone
-        // a lane with no row yet (possible in ragged tiles only) keeps m = -inf and
-        // s = c = 0: with offset 0 its exponents are all -inf (v_exp gives 0)
-        const float off = (RAGGED && mn == -INFINITY) ? 0.0f : -mn;
-        float e[16];
-#pragma unroll
-        for (int v = 0; v < 16; ++v) e[v] = __builtin_amdgcn_exp2f(__builtin_fmaf(k[v], k2, off));
-#pragma unroll
-        for (int w = 8; w >= 1; w >>= 1)
-#pragma unroll
-            for (int v = 0; v < w; ++v) e[v] += e[v + w];
-        const float f = __builtin_amdgcn_exp2f(m[j] + off);   // 1 unless m rises
-        const float sf = s[j] * f;
-        const float y = e[0] - c[j] * f;
-        const float tot = sf + y;
-        c[j] = (tot - sf) - y;
+        float S = terms(-m[j]);
+        const bool raise = !(S <= 0x1p64f);   // m = -inf (inf or NaN terms), or the scores rose
+        // rare: a wave-uniform branch, so the common tile runs none of it
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+            auto mx3 = [](float a, float b, float c) {
+                return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+            };
+            const float m0 = mx3(k[0], k[1], k[2]), m1 = mx3(k[3], k[4], k[5]), m2 = mx3(k[6], k[7], k[8]);
+            const float m3 = mx3(k[9], k[10], k[11]), m4 = mx3(k[12], k[13], k[14]);
+            const float mt = mx3(mx3(m1, m2, m3), m4, __builtin_elementwise_maximum(k[15], m0));
+            // the other lanes keep their offset; a lane with no row yet (ragged tiles
+            // only) keeps m = -inf and adds nothing
+            const float mn = raise ? __builtin_elementwise_maximum(m[j], __builtin_ceilf(mt * k2)) : m[j];
+            if (mn != m[j]) {
+                if (m[j] != -INFINITY) {
+                    s[j] = scale_pow2(s[j], m[j] - mn);
+                    c[j] = scale_pow2(c[j], m[j] - mn);
+                }
+                m[j] = mn;
+            }
+            const float S2 = terms(mn == -INFINITY ? 0.0f : -mn);
+            S = raise ? S2 : S;
+        }
+        const float y = S - c[j];
+        const float tot = s[j] + y;
+        c[j] = (tot - s[j]) - y;
         s[j] = tot;
-        m[j] = mn;
     }
     __device__ __forceinline__ void step(const f32x16& acc, int t, int h, int ndb, int j, bool ragged) {
         if (ragged) tile<true>(acc, t, h, ndb, j);
@@ -1536,8 +1554,9 @@ void lse_partial_kernel(NceArgs a) {
                 const float sj = ep.s[j] - ep.c[j];
                 const float mo = __shfl_xor(ep.m[j], 32), so = __shfl_xor(sj, 32);
                 const float m = __builtin_elementwise_maximum(ep.m[j], mo);
-                const float off = m == -INFINITY ? 0.0f : -m;
-                const float s = sj * __builtin_amdgcn_exp2f(ep.m[j] + off) + so * __builtin_amdgcn_exp2f(mo + off);
+                // integer offsets: exact power-of-two scales (a half with m = -inf holds 0)
+                const float s = (ep.m[j] == -INFINITY ? 0.0f : scale_pow2(sj, ep.m[j] - m)) +
+                                (mo == -INFINITY ? 0.0f : scale_pow2(so, mo - m));
                 const int qp = (g0 + wv + j * kWaves) * 32 + jl;
                 if (h == 0 && qp < n) a.partial[((int64_t)pair * n + qp) * nsg + sg] = make_float2(m, s);
             }
@@ -1548,9 +1567,10 @@ void lse_partial_kernel(NceArgs a) {
 __device__ __forceinline__ float elem_f32(float x) { return x; }
 __device__ __forceinline__ float elem_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
-// Per ground-truth pair t = (i, j), from the base-2 partials (m_seg, s_seg):
-// m = max m_seg, S = sum over segments (in order, compensated) of s_seg 2^(m_seg - m),
-//     term = ln 2 * (m - <a_i, b_j> * k2) + ln S,
+// Per ground-truth pair t = (i, j), from the base-2 partials (m_seg, s_seg) (integer
+// offsets m_seg): m = max m_seg, S = sum over segments (in order, compensated) of
+// s_seg 2^(m_seg - m); S = S' 2^E with S' in [0.5, 1) and m' = m + E (exact), then
+//     term = ln 2 * (m' - <a_i, b_j> * k2) + ln S',
 // the positive score an fp32 dot product (components in order).  NaN when i or j is
 // out of range.  Each block also leaves the binary64 sum of its terms.
 template <typename T>
@@ -1567,10 +1587,16 @@ __global__ __launch_bounds__(256) void nce_terms_kernel(NceArgs a) {
         for (int k = 0; k < a.nseg; ++k) m = __builtin_elementwise_maximum(m, p[k].x);
         float S = 0.0f, c = 0.0f;
         for (int k = 0; k < a.nseg; ++k) {
-            const float y = p[k].y * __builtin_amdgcn_exp2f(p[k].x - m) - c;
+            if (p[k].x == -INFINITY) continue;   // a segment with no row
+            const float y = scale_pow2(p[k].y, p[k].x - m) - c;
             const float tot = S + y;
             c = (tot - S) - y;
             S = tot;
+        }
+        if (S > 0.0f && m != -INFINITY) {
+            int e = 0;
+            S = __builtin_frexpf(S, &e);
+            m += (float)e;
         }
         if (a.lse2) a.lse2[pt] = m + log2f(S);
         float term = __builtin_nanf("");
