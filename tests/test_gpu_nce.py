@@ -128,6 +128,29 @@ def test_nce_large_scores_do_not_overflow():
     log("large", "max err", e)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nce_scores_rising_along_the_database(dtype):
+    """Database row k is alpha_t * a[k mod 300], alpha stepping up by 0.97 from one
+    32-row tile to the next in runs of four tiles (0.1 .. 3.0): at tau = 0.02 a query's
+    best score then rises by about 70 in base-2 exponent units per tile, so the
+    log-sum-exp offset is raised inside segments, again and again, where it would
+    otherwise stay.  Scores reach 3, so score errors grow by 3x and the exponent errors
+    by 5x against tau = 0.1."""
+    rng = np.random.default_rng(21)
+    A = workloads.unit_rows(rng, 40 * 40, 24).astype(np.float32)
+    k = np.arange(64 * 64)
+    alpha = (0.1 + 0.97 * ((k // 32) % 4)).astype(np.float32)
+    B = (alpha[:, None] * A[k % 300]).astype(np.float32)
+    bits = (None, None)
+    if dtype == "bf16":
+        bits = (workloads.f32_to_bf16_bits(A), workloads.f32_to_bf16_bits(B))
+        A, B = workloads.bf16_bits_to_f32(bits[0]), workloads.bf16_bits_to_f32(bits[1])
+    gt = np.stack([np.arange(300), np.arange(300) + 3 * 32], axis=1).astype(np.int32)
+    terms, loss = run(A, B, gt, 0.02, 40, 40, 64, 64, bits)
+    e = check(terms, loss, A, B, gt, 0.02, atol=10 * ATOL)
+    log("rising", dtype, "max err", e)
+
+
 def test_nce_batch_and_invalid_pairs():
     """Three image pairs in one call; pair 1 holds an out-of-range ground-truth row, whose
     term (and that pair's loss) is NaN while the others are unaffected."""
