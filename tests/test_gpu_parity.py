@@ -167,6 +167,37 @@ def test_nn_all_scores_negative(dtype):
     log("negative", dtype, rep)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nn_mixed_sign_best_scores(dtype):
+    """Full query groups (64x48 queries against a 64x48 map) where every other row of
+    image 1 points away from all of image 2 (best score negative) and the rest toward
+    it: one workgroup holds lanes of both kinds, so the keyed search, its exact
+    fallback and the tile epilogue run one unit behind the products all meet."""
+    rng = np.random.default_rng(15)
+    d, (h, w) = 24, (64, 48)
+    e = np.zeros(d)
+    e[0] = 1.0
+
+    def unit(x):
+        return (x / np.linalg.norm(x, axis=1, keepdims=True)).astype(np.float32)
+
+    sign = np.where(np.arange(h * w) % 2 == 0, 1.0, -1.0)[:, None]
+    A = unit(sign * 0.9 * e + 0.25 * rng.standard_normal((h * w, d)) / np.sqrt(d))
+    B = unit(0.9 * e + 0.25 * rng.standard_normal((h * w, d)) / np.sqrt(d))
+    Ab = Bb = None
+    if dtype == "bf16":
+        Ab, Bb = workloads.f32_to_bf16_bits(A), workloads.f32_to_bf16_bits(B)
+        A, B = workloads.bf16_bits_to_f32(Ab), workloads.bf16_bits_to_f32(Bb)
+    gi, gs = mr.nn_argmax(dev_map(A, h, w, Ab), dev_map(B, h, w, Bb), with_score=True)
+    torch.cuda.synchronize()
+    oi, o1, o2 = oracle.nn(A, B)
+    assert o1[1::2].max() < 0 < o1[0::2].min()
+    rep = checks.check_nn(gi.cpu().numpy(), oi, o1, o2, A, np.arange(len(A)), B, dtype)
+    s = oracle.similarity_pairs(A, B, np.arange(len(A)), gi.cpu().numpy())
+    assert np.abs(gs.cpu().numpy().astype(np.float64) - s).max() < 3e-6
+    log("mixed sign", dtype, rep)
+
+
 def test_mutual_c2_bf16_full_size_sampled():
     """512x384 bf16 pair, full 196608^2 brute force; the oracle checks 4096 random rows and
     4096 random columns (and the reciprocity of the sampled rows)."""
