@@ -950,6 +950,8 @@ void nn_argmax_kernel(NNArgs a) {
                     q[j].load_f32(static_cast<const float*>(qbase) + (valid ? row : 0) * a.d, valid, h, a.q_role);
                 else
                     q[j].load(qbase, valid ? row : 0, valid, h, a.d, a.q_role);
+            } else if constexpr (AR == AR_BF16) {
+                q[j].load(qbase, 0, false, h, a.d, a.q_role);   // zero: the register stream runs every slot
             }
         }
     };
@@ -1047,12 +1049,15 @@ void nn_argmax_kernel(NNArgs a) {
         int rw[QT];
         if constexpr (TB) {
             TileBest<QT> best;
-            // the choice must be the same for all four waves: both paths stage tiles
-            // cooperatively, with workgroup barriers
-            if (g1 - g0 == kWaves * QT && (int64_t)t1 * 32 <= a.ndb)
-                stream_regs<AR, P, 4>(dbytes, t0, t1, q, h, jl, a.d, best);
-            else
+            // segments without a ragged tile stream through registers, each wave on its
+            // own (a wave short of query tiles multiplies zero operands in the empty
+            // slots, whose keys are never written; a wave with none skips the stream);
+            // the choice is the same for all four waves, as the staged path has barriers
+            if ((int64_t)t1 * 32 <= a.ndb) {
+                if (nact > 0) stream_regs<AR, P, 4>(dbytes, t0, t1, q, h, jl, a.d, best);
+            } else {
                 stream_db<AR, P>(dbytes, rb, t0, t1, a.ndb, lds, q, nact, h, jl, a.d, a.db_role, best);
+            }
 #pragma unroll
             for (int j = 0; j < QT; ++j) { sv[j] = best.bv[j]; rw[j] = best.bt[j]; }
         } else {
@@ -1533,17 +1538,22 @@ void lse_partial_kernel(NceArgs a) {
                     q[j].load_f32(static_cast<const float*>(qbase) + (valid ? row : 0) * a.d, valid, h, 1);
                 else
                     q[j].load(qbase, valid ? row : 0, valid, h, a.d, 1);
+            } else if constexpr (AR == AR_BF16) {
+                q[j].load(qbase, 0, false, h, a.d, 1);   // zero: the register stream runs every slot
             }
         }
         const int t0 = (int)((int64_t)sg * ntiles / nsg);
         const int t1 = (int)((int64_t)(sg + 1) * ntiles / nsg);
         LseSum<QT> ep(a.k2);
         bool direct = false;
-        if constexpr (AR == AR_BF16) direct = g1 - g0 == kWaves * QT && (int64_t)t1 * 32 <= a.n2;
-        // full bf16 items stream without LDS (the choice is uniform over the workgroup,
-        // whose staged path has barriers)
+        if constexpr (AR == AR_BF16) direct = (int64_t)t1 * 32 <= a.n2;
+        // bf16 segments without a ragged tile stream without LDS, each wave on its own
+        // (empty query slots hold zero operands and are never written; a wave with no
+        // query tile skips the stream); the choice is uniform over the workgroup, whose
+        // staged path has barriers
         if (direct) {
-            if constexpr (AR == AR_BF16) stream_regs<AR, P, 4>(dbytes, t0, t1, q, h, jl, a.d, ep);
+            if constexpr (AR == AR_BF16)
+                if (nact > 0) stream_regs<AR, P, 4>(dbytes, t0, t1, q, h, jl, a.d, ep);
         } else {
             stream_db<AR, P>(dbytes, rb, t0, t1, a.n2, lds, q, nact, h, jl, a.d, 2, ep);
         }
