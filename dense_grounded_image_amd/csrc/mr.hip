@@ -970,9 +970,10 @@ void nn_argmax_kernel(NNArgs a) {
         }
     };
 
-    if (qgroups == 1) {
-        // small frontier (one query group): the four waves share each query block and
-        // split the database four ways; query blocks are taken one after another
+    if (qgroups == 1 && nqt < kWaves) {
+        // small frontier (fewer query tiles than waves, so some wave of the one query
+        // group would sit idle): the four waves share each query block and split the
+        // database four ways; query blocks are taken one after another
         const int cap = (ntiles + kWaves - 1) / kWaves < kMaxSegGroups ? (ntiles + kWaves - 1) / kWaves
                                                                        : kMaxSegGroups;
         const int ngroups = (int)gridDim.x < cap ? (int)gridDim.x : cap;
