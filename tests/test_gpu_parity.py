@@ -84,6 +84,28 @@ def test_nn_argmax_query_list_batch():
         checks.check_nn(gi[b], oi, o1, o2, p.D1, rows[b], p.D2, "f32")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("db_hw", [(64, 48), (50, 60)])
+def test_nn_argmax_query_counts_across_modes(dtype, db_hw):
+    """Query lists of 1 .. 545 rows against a database of whole 32-row tiles (64x48)
+    or with a ragged last tile (50x60): fewer query tiles than waves (the per-wave
+    mode), one partial or full query group (the general mode; for bf16 the register
+    stream with zero operands in empty slots), and two groups."""
+    d = 24
+    p = workloads.make_pair(64, 48, d, seed=41, warp="shift", sigma=0.1, rho=0.2, dtype=dtype)
+    q = workloads.make_pair(db_hw[0], db_hw[1], d, seed=42, warp="shift", sigma=0.1, rho=0.2, dtype=dtype)
+    A = dev_map(p.D1, p.H, p.W, p.D1_bits)
+    B = dev_map(q.D2, q.H, q.W, q.D2_bits)
+    rng = np.random.default_rng(43)
+    for n in (1, 33, 96, 97, 127, 200, 385, 480, 512, 545):
+        rows = rng.integers(0, p.N, size=n).astype(np.int32)
+        gi = mr.nn_argmax(A, B, q_idx=torch.from_numpy(rows).to(DEV))
+        torch.cuda.synchronize()
+        oi, o1, o2 = oracle.nn_rows(p.D1, rows, q.D2)
+        rep = checks.check_nn(gi.cpu().numpy(), oi, o1, o2, p.D1, rows, q.D2, dtype)
+        log("query count", dtype, db_hw, n, rep)
+
+
 def test_scores_bitwise_symmetric():
     """For every mutual pair the forward and backward searches report the same fp32 score
     bit for bit: the similarity does not depend on which map is the query side."""
