@@ -94,16 +94,22 @@ def test_nce_ragged_sizes(dtype, d):
 
 
 @pytest.mark.parametrize("n_gt", [1, 5, 31, 33, 4000])
-def test_nce_counts(n_gt):
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nce_counts(n_gt, dtype):
     """Few ground-truth pairs spread each query over many database segments; many fill
-    several query groups."""
+    several query groups (partial ones too: for bf16 the register stream then runs zero
+    operands in the empty query slots)."""
     rng = np.random.default_rng(n_gt)
     A = workloads.unit_rows(rng, 96 * 64, 24).astype(np.float32)
     B = workloads.unit_rows(rng, 80 * 72, 24).astype(np.float32)
+    bits = (None, None)
+    if dtype == "bf16":
+        bits = (workloads.f32_to_bf16_bits(A), workloads.f32_to_bf16_bits(B))
+        A, B = workloads.bf16_bits_to_f32(bits[0]), workloads.bf16_bits_to_f32(bits[1])
     gt = np.stack([rng.integers(0, len(A), n_gt), rng.integers(0, len(B), n_gt)], axis=1).astype(np.int32)
-    terms, loss = run(A, B, gt, 0.1, 96, 64, 80, 72)
+    terms, loss = run(A, B, gt, 0.1, 96, 64, 80, 72, bits)
     e = check(terms, loss, A, B, gt, 0.1)
-    log("count", n_gt, "max err", e)
+    log("count", dtype, n_gt, "max err", e)
 
 
 @pytest.mark.parametrize("tau", [0.05, 0.1, 1.0])
