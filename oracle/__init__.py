@@ -60,6 +60,8 @@ def _bind(lib):
     lib.orc_fast_metric.argtypes = [P, i32, i32, P, i64, i32, i32, i32, i32, i32, i32, i32, f64, P, i64,
                                     P, P, P, P]
     lib.orc_fast_metric.restype = ctypes.c_int
+    lib.orc_fast_ex.argtypes = lib.orc_fast_metric.argtypes + [P, P, P]
+    lib.orc_fast_ex.restype = ctypes.c_int
     lib.orc_infonce.argtypes = [P, i64, P, i64, i32, P, i64, f64, i32, P, P]
     lib.orc_infonce.restype = ctypes.c_int
     lib.orc_infonce_grad.argtypes = [P, i64, P, i64, i32, P, i64, f64, P, i64, i32, P, P, P]
@@ -170,7 +172,9 @@ class Oracle:
         """Fast reciprocal matching seeded on image 1's grid.
 
         Returns dict(pairs int32 [m,2] ascending in u, clean uint8 [m], active int64 [T],
-        nn_queries int)."""
+        nn_queries int, fresh int64 [T] (pixels live at iteration t and in no earlier one),
+        seed_u int32 [ns] (where seed c's chain converged, -1 if it did not within T),
+        seed_clean uint8 [ns] (every decision on seed c's chain cleared eps))."""
         lib = self.lib
         A, B = _f32(A), _f32(B)
         assert A.shape[0] == H1 * W1 and A.shape[1] == B.shape[1]
@@ -181,15 +185,20 @@ class Oracle:
         pairs = np.empty((cap, 2), np.int32)
         clean = np.zeros(cap, np.uint8)
         active = np.zeros(max(1, max_iters), np.int64)
+        fresh = np.zeros(max(1, max_iters), np.int64)
+        seed_u = np.full(cap, -1, np.int32)
+        seed_clean = np.ones(cap, np.uint8)
         npairs = ctypes.c_int64(0)
         nq = ctypes.c_int64(0)
-        rc = lib.orc_fast_metric(_ptr(A), H1, W1, _ptr(B), B.shape[0], A.shape[1], metric, stride, offset,
-                                 max_iters, seed_limit, nthreads or default_threads(), eps, _ptr(pairs), cap,
-                                 ctypes.byref(npairs), _ptr(clean), _ptr(active), ctypes.byref(nq))
+        rc = lib.orc_fast_ex(_ptr(A), H1, W1, _ptr(B), B.shape[0], A.shape[1], metric, stride, offset,
+                             max_iters, seed_limit, nthreads or default_threads(), eps, _ptr(pairs), cap,
+                             ctypes.byref(npairs), _ptr(clean), _ptr(active), ctypes.byref(nq), _ptr(fresh),
+                             _ptr(seed_u), _ptr(seed_clean))
         assert rc == 0, rc
         m = npairs.value
         return dict(pairs=pairs[:m].copy(), clean=clean[:m].copy(), active=active[:max_iters].copy(),
-                    nn_queries=nq.value)
+                    nn_queries=nq.value, fresh=fresh[:max_iters].copy(), seed_u=seed_u[:ns].copy(),
+                    seed_clean=seed_clean[:ns].copy())
 
 
     def infonce(self, A, B, gt, tau, nthreads=None):

@@ -286,12 +286,26 @@ static double orc_margin(double top1, double top2, int metric)
  *                  only NN decisions whose margin exceeds eps: top1 - top2 for
  *                  the inner product; for pointmaps the relative margin
  *                  (d2 - d1) / d2 of the two smallest squared distances;
- *  - nn_queries  : number of NN searches performed (after memoisation).
+ *  - nn_queries  : number of NN searches performed (after memoisation);
+ *  - fresh[t]    : number of those pixels live at iteration t that were live
+ *                  in no earlier iteration (NULL to skip).  A policy that
+ *                  never restarts a chain on a pixel that has ever been live
+ *                  (the set of pairs is the same, see the characterisation
+ *                  above) carries exactly these pixels at iteration t;
+ *  - seed_u[c]   : the image-1 pixel at which seed c's chain converged, -1 if
+ *                  it had not converged after T iterations (NULL to skip);
+ *  - seed_clean[c]: 1 if every NN decision made along seed c's chain (up to
+ *                  its convergence, or through iteration T-1) had a margin
+ *                  above eps (NULL to skip).
+ * A chain whose decisions all clear the margin is followed identically by any
+ * search whose chosen NN equals the exact one wherever the margin exceeds
+ * eps; only the other chains can end elsewhere.
  * ------------------------------------------------------------------------ */
-int orc_fast_metric(const float* A, int32_t H1, int32_t W1, const float* B, int64_t n2, int32_t d,
-                    int32_t metric, int32_t stride, int32_t offset, int32_t T, int32_t seed_limit,
-                    int32_t nthreads, double eps, int32_t* pairs, int64_t cap, int64_t* n_pairs,
-                    uint8_t* pair_clean, int64_t* active, int64_t* nn_queries)
+int orc_fast_ex(const float* A, int32_t H1, int32_t W1, const float* B, int64_t n2, int32_t d,
+                int32_t metric, int32_t stride, int32_t offset, int32_t T, int32_t seed_limit,
+                int32_t nthreads, double eps, int32_t* pairs, int64_t cap, int64_t* n_pairs,
+                uint8_t* pair_clean, int64_t* active, int64_t* nn_queries, int64_t* fresh,
+                int32_t* seed_u, uint8_t* seed_clean)
 {
     if (!A || !B || !pairs || !n_pairs || H1 < 0 || W1 < 0 || n2 < 0 || d < 1 || stride < 1 ||
         offset < 0 || T < 0 || metric < 0 || metric > 1)
@@ -301,12 +315,18 @@ int orc_fast_metric(const float* A, int32_t H1, int32_t W1, const float* B, int6
     if (nn_queries) *nn_queries = 0;
     if (active)
         for (int t = 0; t < T; ++t) active[t] = 0;
+    if (fresh)
+        for (int t = 0; t < T; ++t) fresh[t] = 0;
 
     /* seeds */
     int64_t ns = 0;
     for (int64_t y = offset; y < H1; y += stride)
         for (int64_t x = offset; x < W1; x += stride) ++ns;
     if (seed_limit >= 0 && ns > seed_limit) ns = seed_limit;
+    for (int64_t c = 0; c < ns; ++c) {
+        if (seed_u) seed_u[c] = -1;
+        if (seed_clean) seed_clean[c] = 1;
+    }
     if (ns == 0 || n1 == 0 || n2 == 0 || T == 0) return ORC_OK;
 
     int rc = ORC_ERR_NOMEM;
@@ -321,15 +341,16 @@ int orc_fast_metric(const float* A, int32_t H1, int32_t W1, const float* B, int6
     uint8_t* mclean = malloc(n1);
     uint8_t* seen1 = malloc(n1);
     uint8_t* seen2 = malloc(n2);
+    uint8_t* ever1 = malloc(n1);                         /* live in some earlier iteration */
     int32_t* todo = malloc(sizeof(int32_t) * ns);
     int32_t* res = malloc(sizeof(int32_t) * ns);
     double* t1 = malloc(sizeof(double) * ns);
     double* t2 = malloc(sizeof(double) * ns);
     if (!cur || !alive || !clean || !nn12 || !mg12 || !nn21 || !mg21 || !match || !mclean ||
-        !seen1 || !seen2 || !todo || !res || !t1 || !t2)
+        !seen1 || !seen2 || !ever1 || !todo || !res || !t1 || !t2)
         goto done;
 
-    for (int64_t i = 0; i < n1; ++i) { nn12[i] = -1; match[i] = -1; mclean[i] = 0; seen1[i] = 0; }
+    for (int64_t i = 0; i < n1; ++i) { nn12[i] = -1; match[i] = -1; mclean[i] = 0; seen1[i] = 0; ever1[i] = 0; }
     for (int64_t i = 0; i < n2; ++i) { nn21[i] = -1; seen2[i] = 0; }
     {
         int64_t c = 0;
@@ -344,14 +365,21 @@ int orc_fast_metric(const float* A, int32_t H1, int32_t W1, const float* B, int6
 
     for (int32_t t = 0; t < T; ++t) {
         /* forward: NN12 of every distinct live pixel not yet known */
-        int64_t nt = 0, distinct = 0;
+        int64_t nt = 0, distinct = 0, first_visits = 0;
         for (int64_t c = 0; c < ns; ++c) {
             if (!alive[c]) continue;
             int32_t u = cur[c];
-            if (!seen1[u]) { seen1[u] = 1; ++distinct; if (nn12[u] < 0) todo[nt++] = u; }
+            if (!seen1[u]) {
+                seen1[u] = 1;
+                ++distinct;
+                if (!ever1[u]) ++first_visits;
+                if (nn12[u] < 0) todo[nt++] = u;
+            }
         }
-        for (int64_t c = 0; c < ns; ++c) if (alive[c]) seen1[cur[c]] = 0;
+        for (int64_t c = 0; c < ns; ++c)
+            if (alive[c]) { seen1[cur[c]] = 0; ever1[cur[c]] = 1; }
         if (active) active[t] = distinct;
+        if (fresh) fresh[t] = first_visits;
         if (distinct == 0) break;
         orc_nn_parallel(A, todo, nt, B, n2, d, metric, nthreads, res, t1, t2);
         for (int64_t k = 0; k < nt; ++k) { nn12[todo[k]] = res[k]; mg12[todo[k]] = orc_margin(t1[k], t2[k], metric); }
@@ -379,6 +407,7 @@ int orc_fast_metric(const float* A, int32_t H1, int32_t W1, const float* B, int6
             if (u2 == u) {
                 match[u] = v;
                 if (clean[c]) mclean[u] = 1;
+                if (seed_u) seed_u[c] = u;
                 alive[c] = 0;
             } else {
                 cur[c] = u2;
@@ -398,11 +427,24 @@ int orc_fast_metric(const float* A, int32_t H1, int32_t W1, const float* B, int6
         }
         *n_pairs = m;
     }
+    if (seed_clean)
+        for (int64_t c = 0; c < ns; ++c) seed_clean[c] = clean[c];
     rc = ORC_OK;
 done:
     free(cur); free(alive); free(clean); free(nn12); free(mg12); free(nn21); free(mg21);
-    free(match); free(mclean); free(seen1); free(seen2); free(todo); free(res); free(t1); free(t2);
+    free(match); free(mclean); free(seen1); free(seen2); free(ever1); free(todo); free(res); free(t1);
+    free(t2);
     return rc;
+}
+
+/* orc_fast_ex without the per-seed and first-visit records. */
+int orc_fast_metric(const float* A, int32_t H1, int32_t W1, const float* B, int64_t n2, int32_t d,
+                    int32_t metric, int32_t stride, int32_t offset, int32_t T, int32_t seed_limit,
+                    int32_t nthreads, double eps, int32_t* pairs, int64_t cap, int64_t* n_pairs,
+                    uint8_t* pair_clean, int64_t* active, int64_t* nn_queries)
+{
+    return orc_fast_ex(A, H1, W1, B, n2, d, metric, stride, offset, T, seed_limit, nthreads, eps, pairs, cap,
+                       n_pairs, pair_clean, active, nn_queries, NULL, NULL, NULL);
 }
 
 /* The inner-product form of orc_fast_metric. */

@@ -324,6 +324,83 @@ def pin_fast_clean_flag(orc):
     assert r["clean"].tolist() == [0, 1]
 
 
+def _numpy_nn(Q, D):
+    """NN by the float64 similarity matrix (numpy takes the first maximum, i.e. the lowest
+    index) with the top-1 minus top-2 margin."""
+    S = Q.astype(np.float64) @ D.astype(np.float64).T
+    idx = S.argmax(1)
+    srt = np.sort(S, axis=1)
+    top2 = srt[:, -2] if S.shape[1] > 1 else np.full(S.shape[0], -np.inf)
+    return idx, srt[:, -1] - top2
+
+
+def _walk_seed_records(n12, m12, n21, m21, seeds, T, eps):
+    """Each seed's chain walked by hand: where it converged (-1 if not within T iterations),
+    whether every decision on it cleared eps, and per iteration the number of live pixels
+    that were live in no earlier iteration."""
+    ends, cleans, fresh = [], [], [0] * T
+    live_at = [set() for _ in range(T)]
+    for s in seeds:
+        u, ok, end = int(s), True, -1
+        for t in range(T):
+            live_at[t].add(u)
+            v = int(n12[u])
+            u2 = int(n21[v])
+            ok = ok and m12[u] > eps and m21[v] > eps
+            if u2 == u:
+                end = u
+                break
+            u = u2
+        ends.append(end)
+        cleans.append(int(ok))
+    ever = set()
+    for t in range(T):
+        fresh[t] = len(live_at[t] - ever)
+        ever |= live_at[t]
+    return ends, cleans, fresh
+
+
+def pin_fast_seed_records(orc):
+    """Per-seed end points and clean flags, and the first-visit count per iteration, against
+    a hand walk of every chain over numpy brute-force NN maps and margins."""
+    cases = ((20, 18, 0.1, 0.2, 4, 2, 10, 1e-5), (16, 13, 0.3, 0.5, 3, 1, 4, 1e-5),
+             (24, 20, 0.2, 0.3, 5, 0, 2, 1e-5), (14, 12, 0.25, 0.4, 2, 1, 6, 0.02))
+    for k, (H, W, sig, rho, stride, off, T, eps) in enumerate(cases):
+        p = workloads.make_pair(H, W, 24, seed=40 + k, warp="affine", sigma=sig, rho=rho)
+        n12, m12 = _numpy_nn(p.D1, p.D2)
+        n21, m21 = _numpy_nn(p.D2, p.D1)
+        seeds = _grid(H, W, stride, off)
+        ends, cleans, fresh = _walk_seed_records(n12, m12, n21, m21, seeds, T, eps)
+        r = orc.fast(p.D1, H, W, p.D2, stride, off, T, eps=eps)
+        assert r["seed_u"].tolist() == ends, k
+        assert r["seed_clean"].tolist() == cleans, k
+        assert r["fresh"].tolist() == fresh, (k, r["fresh"], fresh)
+        # the collected pairs are the end points, with the forward NN
+        assert _pairs_set(r["pairs"]) == {(u, int(n12[u])) for u in ends if u >= 0}
+        # a pair is clean when some clean chain collected it
+        want_clean = {u for u, c in zip(ends, cleans) if u >= 0 and c}
+        assert {int(u) for (u, _), c in zip(r["pairs"], r["clean"]) if c} == want_clean
+    assert k == len(cases) - 1
+
+
+def pin_fast_seed_records_closed_forms(orc):
+    """Stride 1 and T = 1: every pixel is a seed and converges where it starts iff it is a
+    mutual pixel; all N pixels are first visits.  The noise-free planted field: every seed
+    that is a source pixel converges in place in the first iteration, no seed is live
+    twice, and every decision is exact (large margins)."""
+    p = workloads.make_pair(12, 10, 24, seed=45, warp="shift", sigma=0.1, rho=0.2)
+    mutual = {int(u) for u, _ in orc.mutual_nn(p.D1, p.D2)[0]}
+    r = orc.fast(p.D1, p.H, p.W, p.D2, 1, 0, 1)
+    assert r["seed_u"].tolist() == [u if u in mutual else -1 for u in range(p.N)]
+    assert r["fresh"].tolist() == [p.N]
+    q = workloads.make_pair(24, 16, 24, seed=27, warp="shift", sigma=0.0, rho=0.0)
+    srcs = set(q.src.tolist())
+    seeds = _grid(q.H, q.W, 4, 2)
+    r = orc.fast(q.D1, q.H, q.W, q.D2, 4, 2, 3)
+    assert r["seed_u"].tolist() == [s if s in srcs else r["seed_u"][i] for i, s in enumerate(seeds)]
+    assert r["fresh"][0] == len(seeds) and sum(r["fresh"]) <= q.N
+
+
 # ============================================================================ pointmaps
 # Metric 1: nearest = smallest Euclidean distance between 3D points ("DUSt3R and MASt3R
 # explained", the paragraph on recovering the cameras); scores are -|a - b|^2.

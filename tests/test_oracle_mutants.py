@@ -30,6 +30,12 @@ MUTANTS = {
     "seed_grid_column_major": ("cur[c] = (int32_t)(y * W1 + x);", "cur[c] = (int32_t)(x * H1 + y);"),
     "clean_flag_ignores_backward": ("if (!(mg12[u] > eps) || !(mg21[v] > eps)) clean[c] = 0;",
                                     "if (!(mg12[u] > eps)) clean[c] = 0;"),
+    "fresh_counts_every_live_pixel": ("if (!ever1[u]) ++first_visits;", "++first_visits;"),
+    "fresh_forgets_earlier_iterations": ("if (alive[c]) { seen1[cur[c]] = 0; ever1[cur[c]] = 1; }",
+                                         "if (alive[c]) { seen1[cur[c]] = 0; }"),
+    "seed_end_records_partner": ("if (seed_u) seed_u[c] = u;", "if (seed_u) seed_u[c] = v;"),
+    "seed_clean_always_set": ("for (int64_t c = 0; c < ns; ++c) seed_clean[c] = clean[c];",
+                              "for (int64_t c = 0; c < ns; ++c) seed_clean[c] = 1;"),
     # pointmap metric
     "point_metric_ignored": ("if (metric == ORC_NEG_SQ_L2) {", "if (0) {"),
     "point_farthest_instead_of_nearest": ("return -acc;", "return acc;"),
