@@ -13,7 +13,14 @@ form, the rules are:
         margin above 1e-5 ("clean") is in the GPU output;
   (ii)  every GPU pair (u, v) is eps-reciprocal in binary64:
         s(u, v) >= top1(u -> image 2) - eps and s(u, v) >= top1(v -> image 1) - eps;
-  (iii) the GPU output is one-to-one and ascending in u.
+  (iii) the GPU output is one-to-one and ascending in u;
+  (iv)  if every seed's chain is clean, the GPU set equals the oracle's set, and the
+        GPU's live count per iteration equals the oracle's count of first visits
+        (the GPU never restarts a chain on a pixel that was live before);
+  (v)   otherwise only unclean chains may end elsewhere: a chain whose decisions all
+        clear the margin is followed identically on the GPU, and a chain yields at
+        most one pair, so the GPU-only pairs and the oracle-only pairs each number
+        at most the unclean seeds.
 """
 from __future__ import annotations
 
@@ -93,8 +100,9 @@ def check_reciprocal(pairs, A, B, dtype, nthreads=None, metric=0):
     assert _near_enough(s, b1, dtype, metric).all(), "a GPU pair is not a backward NN within tolerance"
 
 
-def check_fast(gpu_pairs, orc, A, B, dtype, nthreads=None, metric=0):
-    """Rules (i)-(iii) against a full oracle run `orc` (dict from oracle.fast)."""
+def check_fast(gpu_pairs, orc, A, B, dtype, nthreads=None, metric=0, gpu_active=None):
+    """Rules (i)-(v) against a full oracle run `orc` (dict from oracle.fast);
+    gpu_active: the GPU's live count per iteration, or None."""
     gpu_pairs = np.asarray(gpu_pairs).reshape(-1, 2)
     check_one_to_one_sorted(gpu_pairs)
     gset = {(int(a), int(b)) for a, b in gpu_pairs}
@@ -103,8 +111,19 @@ def check_fast(gpu_pairs, orc, A, B, dtype, nthreads=None, metric=0):
     missing = clean - gset
     assert not missing, f"{len(missing)} clean oracle pairs missing, e.g. {sorted(missing)[:3]}"
     check_reciprocal(gpu_pairs, A, B, dtype, nthreads, metric)
+    unclean = int((np.asarray(orc["seed_clean"]) == 0).sum())
+    gpu_only, oracle_only = gset - oset, oset - gset
+    if unclean == 0:
+        assert not gpu_only and not oracle_only, \
+            f"every chain is clean, yet {len(gpu_only)} GPU-only and {len(oracle_only)} oracle-only pairs, " \
+            f"e.g. {sorted(gpu_only)[:3]} {sorted(oracle_only)[:3]}"
+        if gpu_active is not None:
+            ga = np.asarray(gpu_active).reshape(-1)[:len(orc["fresh"])].tolist()
+            assert ga == orc["fresh"].tolist(), f"live counts {ga} != oracle first visits {orc['fresh'].tolist()}"
+    assert len(gpu_only) <= unclean, f"{len(gpu_only)} GPU-only pairs but only {unclean} unclean chains"
+    assert len(oracle_only) <= unclean, f"{len(oracle_only)} oracle-only pairs but only {unclean} unclean chains"
     return dict(gpu=len(gset), oracle=len(oset), clean=len(clean), common=len(gset & oset),
-                gpu_only=len(gset - oset), oracle_only=len(oset - gset))
+                gpu_only=len(gpu_only), oracle_only=len(oracle_only), unclean_seeds=unclean)
 
 
 def oracle_chains(A, B, seeds, T, nthreads=None, eps=None, metric=0):

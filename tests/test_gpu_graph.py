@@ -37,20 +37,27 @@ def test_graph_equals_per_pair_and_oracle(dtype):
         assert act[e].cpu().tolist() == ra[0].cpu().tolist()
         if e % 5 == 0:
             orc = oracle.fast(maps[i], H, W, maps[j], 4, 2, 6)
-            rep = checks.check_fast(got, orc, maps[i], maps[j], dtype)
+            rep = checks.check_fast(got, orc, maps[i], maps[j], dtype, gpu_active=act[e].cpu().numpy())
             log("graph edge", e, i, j, rep)
 
 
 def test_graph_full_size_sampled():
-    """8 images of 512x384 fp32, all 28 edges: three edges against the per-pair call."""
+    """8 images of 512x384 fp32, all 28 edges: three edges against the per-pair call, and
+    one of them against a full oracle run."""
     n, H, W = 8, 512, 384
     maps, _, _ = workloads.make_collection(n, H, W, 24, seed=801)
     imgs = torch.from_numpy(maps.reshape(n, H, W, 24)).to(DEV)
     edges = workloads.all_edges(n)
-    pairs, npairs, _ = mr.fast_reciprocal_graph(imgs, edges, 8, 4, 10)
+    pairs, npairs, act = mr.fast_reciprocal_graph(imgs, edges, 8, 4, 10)
     torch.cuda.synchronize()
     for e in (0, 13, len(edges) - 1):
         i, j = edges[e]
         rp, rn, _ = mr.fast_reciprocal(imgs[i], imgs[j], 8, 4, 10)
         assert mr.matches(pairs, npairs, e).tolist() == mr.matches(rp, rn).tolist()
-    log("graph 8x512x384", [int(x) for x in npairs.cpu()[:5]])
+    # one full-size edge against a full oracle run
+    e = 13
+    i, j = edges[e]
+    orc = oracle.fast(maps[i], H, W, maps[j], 8, 4, 10)
+    rep = checks.check_fast(mr.matches(pairs, npairs, e), orc, maps[i], maps[j], "f32",
+                            gpu_active=act[e].cpu().numpy())
+    log("graph 8x512x384", [int(x) for x in npairs.cpu()[:5]], "edge", e, rep)

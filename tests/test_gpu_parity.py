@@ -281,8 +281,8 @@ def test_fast_full(cfg, dtype):
     fp, fn, act = mr.fast_reciprocal(A, B, cfg["stride"], cfg["offset"], cfg["T"])
     torch.cuda.synchronize()
     orc = oracle.fast(p.D1, p.H, p.W, p.D2, cfg["stride"], cfg["offset"], cfg["T"])
-    rep = checks.check_fast(mr.matches(fp, fn), orc, p.D1, p.D2, dtype)
     act = act[0].cpu().numpy()
+    rep = checks.check_fast(mr.matches(fp, fn), orc, p.D1, p.D2, dtype, gpu_active=act)
     assert act[0] == len(seeds_of(p.H, p.W, cfg["stride"], cfg["offset"]))
     assert (np.diff(act) <= 0).all()
     log("fast", cfg, dtype, rep, act.tolist())
@@ -346,8 +346,30 @@ def test_fast_c1_full_size():
     fp, fn, act = mr.fast_reciprocal(A, B, p.stride, p.offset, p.max_iters)
     torch.cuda.synchronize()
     orc = oracle.fast(p.D1, p.H, p.W, p.D2, p.stride, p.offset, p.max_iters)
-    rep = checks.check_fast(mr.matches(fp, fn), orc, p.D1, p.D2, "f32")
-    log("c1", rep, act[0].cpu().tolist(), orc["active"].tolist())
+    rep = checks.check_fast(mr.matches(fp, fn), orc, p.D1, p.D2, "f32", gpu_active=act[0].cpu().numpy())
+    log("c1", rep, act[0].cpu().tolist(), orc["fresh"].tolist())
+
+
+def test_c0_workload_mutual_and_fast():
+    """The tiny pair exactly as the bench configuration defines it (64x48 fp32, seed 0):
+    brute-force mutual NN in full against the oracle, and the fast scheme (stride 8,
+    offset 4, 10 iterations) against a full oracle run, live counts included."""
+    p = workloads.config_pair(0)
+    A, B = pair_maps(p)
+    pairs, n, nn_ab, nn_ba = mr.mutual_nn(A, B)
+    fp, fn, act = mr.fast_reciprocal(A, B, p.stride, p.offset, p.max_iters)
+    torch.cuda.synchronize()
+    o_pairs, o12, a1, a2, o21, b1, b2 = oracle.mutual_nn(p.D1, p.D2)
+    checks.check_nn(nn_ab[0].cpu().numpy(), o12, a1, a2, p.D1, np.arange(p.N), p.D2, p.dtype)
+    checks.check_nn(nn_ba[0].cpu().numpy(), o21, b1, b2, p.D2, np.arange(p.N), p.D1, p.dtype)
+    gp = mr.matches(pairs, n)
+    clean = (a1 - a2 > checks.MARGIN) & (b1[o12] - b2[o12] > checks.MARGIN)
+    assert clean.all()
+    assert gp.tolist() == o_pairs.tolist()
+    orc = oracle.fast(p.D1, p.H, p.W, p.D2, p.stride, p.offset, p.max_iters)
+    rep = checks.check_fast(mr.matches(fp, fn), orc, p.D1, p.D2, p.dtype, gpu_active=act[0].cpu().numpy())
+    assert rep["unclean_seeds"] == 0 and rep["gpu"] == rep["oracle"] == rep["common"]
+    log("c0", len(gp), rep, act[0].cpu().tolist())
 
 
 def test_fast_c4_full_size_sampled():
@@ -386,7 +408,7 @@ def test_fast_c3_batch64():
     torch.cuda.synchronize()
     for b in (0, 63):
         orc = oracle.fast(ps[b].D1, p0.H, p0.W, ps[b].D2, p0.stride, p0.offset, p0.max_iters)
-        checks.check_fast(mr.matches(fp, fn, b), orc, ps[b].D1, ps[b].D2, "f32")
+        checks.check_fast(mr.matches(fp, fn, b), orc, ps[b].D1, ps[b].D2, "f32", gpu_active=act[b].cpu().numpy())
     rng = np.random.default_rng(3)
     for b in range(64):
         gp = mr.matches(fp, fn, b)

@@ -124,7 +124,8 @@ def test_point_fast_full(H, W, stride, offset, T):
     gp, gn, act = mr.point_fast_reciprocal(dev(p.D1, H, W), dev(p.D2, H, W), stride, offset, T)
     torch.cuda.synchronize()
     orc = oracle.fast(p.D1, H, W, p.D2, stride, offset, T, eps=checks.MARGIN_PT, metric=PT)
-    rep = checks.check_fast(mr.matches(gp, gn), orc, p.D1, p.D2, "f32", metric=PT)
+    rep = checks.check_fast(mr.matches(gp, gn), orc, p.D1, p.D2, "f32", metric=PT,
+                            gpu_active=act[0].cpu().numpy())
     # the library drops chains that land on a pixel visited in an earlier iteration (its
     # future is already followed); the oracle keeps walking them, so it counts at least as many
     assert (act[0].cpu().numpy()[:T] <= orc["active"][:T]).all()
@@ -146,7 +147,8 @@ def test_point_fast_full_size():
     gp, gn, act = mr.point_fast_reciprocal(dev(p.D1, p.H, p.W), dev(p.D2, p.H, p.W), 8, 4, 10)
     torch.cuda.synchronize()
     orc = oracle.fast(p.D1, p.H, p.W, p.D2, 8, 4, 10, eps=checks.MARGIN_PT, metric=PT)
-    rep = checks.check_fast(mr.matches(gp, gn), orc, p.D1, p.D2, "f32", metric=PT)
+    rep = checks.check_fast(mr.matches(gp, gn), orc, p.D1, p.D2, "f32", metric=PT,
+                            gpu_active=act[0].cpu().numpy())
     log("point fast 512x384", rep, act[0].cpu().tolist())
 
 
