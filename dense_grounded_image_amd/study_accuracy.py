@@ -24,7 +24,6 @@ from __future__ import annotations
 import argparse
 import json
 import sys
-import time
 
 import numpy as np
 
@@ -57,17 +56,6 @@ def gpu_matcher():
         t1.record()
         torch.cuda.synchronize()
         return mr.matches(pairs, n), t0.elapsed_time(t1) * 1e-3
-    return fast
-
-
-def oracle_matcher():
-    """The same interface on the CPU oracle (test infrastructure; used to check the study)."""
-    import oracle
-
-    def fast(A, B, H, W, stride, offset, T):
-        t = time.perf_counter()
-        r = oracle.fast(A, H, W, B, stride, offset, T)
-        return r["pairs"].astype(np.int64), time.perf_counter() - t
     return fast
 
 
