@@ -1935,11 +1935,15 @@ __global__ __launch_bounds__(256) void fill_f32_kernel(float* p, int64_t n, floa
 
 // ---------------------------------------------------------------------------- host helpers
 
+// The measurement aid's window belongs to the thread that opened it: an entry point
+// reads it only on that thread, so calls on other threads never touch it.  It holds
+// no HIP object outside an open window (trivially destructible, no teardown work).
 struct Profiler {
     bool on = false;
     int cap = 0, used = 0;
     hipEvent_t* ev = nullptr;
-} g_prof;
+};
+thread_local Profiler g_prof;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -1982,11 +1986,12 @@ int grid_1d(int64_t n, int threads = 256, int cap = 1 << 24) {
 
 int dev_err() { return hipGetLastError() == hipSuccess ? MR_OK : MR_ERR_DEVICE; }
 
-// Workgroups of kernel K (kThreads each) that the GPU holds at once.
+// Workgroups of kernel K (kThreads each) that the GPU holds at once: a launch-shape
+// constant, computed once per process (a thread-safe static initialisation; a plain
+// int, so process teardown has nothing to release).
 template <auto K>
 int resident_blocks() {
-    static int resident = 0;
-    if (resident == 0) {
+    static const int resident = [] {
         int dev = 0, cus = 256, per_cu = 0;
         if (hipGetDevice(&dev) == hipSuccess) {
             hipDeviceProp_t prop;
@@ -1994,8 +1999,8 @@ int resident_blocks() {
         }
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, kThreads, 0) != hipSuccess || per_cu < 1)
             per_cu = 1;
-        resident = cus * per_cu;
-    }
+        return cus * per_cu;
+    }();
     return resident;
 }
 

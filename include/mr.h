@@ -38,6 +38,9 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls are asynchronous on that stream; outputs are valid once the stream
  *    has completed the call.  Calls that share a workspace must not overlap.
+ *  - The entry points keep no state between calls (the measurement aid at the
+ *    end of this file is the one opt-in exception, confined to the thread that
+ *    opens it) and are thread-safe given distinct workspaces.
  *  - Arguments are validated on the host before anything is launched; a
  *    nonzero return means nothing was enqueued.  MR_ERR_DEVICE reports a
  *    launch failure after some work may have been enqueued.
@@ -250,7 +253,12 @@ int mr_infonce_backward(const mr_map* a, const mr_map* b, const int32_t* gt, int
                         size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Measurement aid (not thread-safe; one profiling window per process).
+ * Measurement aid.  The one piece of state the library keeps between calls, and
+ * only on request: a profiling window belongs to the calling thread (one open
+ * window per thread).  Entry points called on that thread while its window is
+ * open record events into it; calls on any other thread, and calls outside a
+ * window, never read or write it, so the entry points stay thread-safe given
+ * distinct workspaces.
  * mr_profile_begin(n): from now on, record a pair of hipEvents on the call's
  * stream around every launch of the similarity/argmax kernel (both metrics),
  * of the matching loss's log-sum-exp kernel (mr_infonce_forward) and of the two
