@@ -5,10 +5,11 @@ One step = one mr_fast_reciprocal call on inputs already resident in HBM:
 seed grid (stride 8, 3072 seeds), up to 10 forward/backward NN iterations with
 cycle check and frontier compaction, and the ordered match list.  The JSON line
 reports image pairs/s, NN queries/s, the similarity kernel's fraction of the
-fp32 matrix-core peak (timed live with HIP events around each launch), and the
-CPU oracle timed on the host for the same pair.  Other workloads (brute-force
-bf16 mutual NN, the 64-pair batch, the 1024x768 bf16 pair) are reported under
-"other" unless --main-only.
+ceiling of fp32-accurate products on the matrix cores (timed live with HIP events
+around each launch), and the CPU oracle timed on the host for the same pair.
+Other workloads (brute-force bf16 mutual NN, the 64-pair batch, the 1024x768 bf16
+pair, pointmaps, the pair graph, the matching loss) are reported under "other"
+unless --main-only.
 """
 import argparse
 import json
@@ -22,6 +23,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "image pairs/sec fast reciprocal NN @512×384 d=24; NN-queries/sec; %MFMA peak"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}   # MI355X dense matrix-core peaks
+# fp32 maps never use the fp32 matrix instruction: each fp32 product is formed as six
+# exact bf16 products (an exact three-way split of both operands) on the bf16 matrix
+# cores, so the ceiling of fp32-accurate products is the bf16 peak over six.
+SPLIT_PRODUCTS = 6
+PEAK_SPLIT_TFLOPS = PEAK_TFLOPS["bf16"] / SPLIT_PRODUCTS
 PEAK_HBM_GBPS = 8000.0
 # fp32 VALU lane-operations per second: the published fp32 vector peak, 157.3 TFLOP/s,
 # is 78.6 T fused multiply-adds per second (32 fp32 lanes per SIMD per clock, 256 CUs x
@@ -162,7 +168,8 @@ def rounds_roofline(r, N, d, elem_bytes, peak_tflops):
     """Per round of the fast scheme: its two similarity launches' measured time (averaged
     over the timed calls) against the round's lower bound max(flops / matrix peak,
     bytes / HBM), flops 4*|U_t|*N*d and bytes two map reads of N*d elements; overall,
-    the summed bounds over the summed kernel time."""
+    the summed bounds over the summed kernel time.  peak_tflops is the ceiling of the
+    arithmetic the kernel executes (for fp32 maps the split ceiling, bf16 peak / 6)."""
     each, act = r["each"], r["active"]
     per_call = 2 * len(act)
     if not each or len(each) % per_call:
@@ -196,24 +203,31 @@ def measured_traffic(name):
     return rec["hbm_bytes_per_launch"] if rec.get("source_sha256") == sha else None
 
 
-def roofline(flops_per_step, steps, kernel_ms, launches, dtype, traffic=None):
-    """Algorithmic flops (2*N*d per NN query) per launch of the similarity kernel over its
-    average launch time, against the matrix-core peak of the maps' dtype.  fp32 maps are
-    computed as an exact three-way bf16 split (six bf16 products per fp32 product), so
-    their executed bf16 work and its fraction of the bf16 peak are reported as well."""
+def roofline(flops_per_step, steps, kernel_ms, launches, dtype, traffic=None, kernel="nn_argmax_kernel"):
+    """Algorithmic flops (2*N*d per NN query; a brute-force call counts the similarity
+    matrix once) per launch of the similarity kernel over its average launch time,
+    against the ceiling of the arithmetic the kernel executes.  bf16 maps: the bf16
+    matrix-core peak.  fp32 maps: every fp32 product is six exact bf16 products on the
+    bf16 matrix cores (the fp32 matrix instruction is never issued), so the ceiling is
+    the bf16 peak / 6; the fraction of the fp32 matrix peak is kept as a secondary
+    field.  traffic: measured HBM bytes per launch, or None."""
     if not launches:
         return None
     per_launch = flops_per_step * steps / launches
     avg_ms = kernel_ms / launches
     achieved = per_launch / (avg_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[dtype]
-    out = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+    peak = PEAK_SPLIT_TFLOPS if dtype == "f32" else PEAK_TFLOPS[dtype]
+    out = {"bound": "mfma", "achieved": round(achieved, 3), "peak": round(peak, 2), "unit": "TFLOP/s",
            "frac": round(achieved / peak, 4), "traffic": traffic,
-           "kernel": "nn_argmax_kernel", "avg_launch_us": round(avg_ms * 1e3, 2),
+           "kernel": kernel, "avg_launch_us": round(avg_ms * 1e3, 2),
            "flops_per_launch": per_launch}
     if traffic is not None:
         out["hbm_GBps"] = round(traffic / (avg_ms * 1e-3) / 1e9, 1)
+        out["hbm_frac"] = round(traffic / (avg_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
     if dtype == "f32":
+        out["peak_note"] = "fp32-accurate products: bf16 peak 2500 TFLOP/s / 6 bf16 products each"
+        out["fp32_mfma"] = {"peak": PEAK_TFLOPS["f32"], "frac": round(achieved / PEAK_TFLOPS["f32"], 4),
+                            "note": "secondary: the fp32 matrix instruction is not issued"}
         out["executed"] = {"arith": "bf16 x3 split, 6 bf16 products per fp32 product",
                            "achieved_bf16_TFLOPs": round(6 * achieved, 2), "peak": PEAK_TFLOPS["bf16"],
                            "frac": round(6 * achieved / PEAK_TFLOPS["bf16"], 4)}
@@ -258,15 +272,26 @@ def roofline_lse(scores_per_step, d, steps, kernel_ms, launches):
 
 def cpu_baseline(p):
     import oracle
+    import workloads
     threads = oracle.default_threads()
     t = time.perf_counter()
     r = oracle.fast(p.D1, p.H, p.W, p.D2, p.stride, p.offset, p.max_iters, nthreads=threads)
     dt = time.perf_counter() - t
     cpu, ncpu = oracle_host()
-    return {"value": round(1.0 / dt, 4), "unit": "pairs/s", "cores": threads, "kind": "oracle",
-            "sample": "the whole 512x384 pair (3072 seeds, 10 iterations), binary64 C oracle, %d threads, "
-                      "%.2f s, %d NN queries, CPU %s, nproc %d" % (threads, dt, r["nn_queries"], cpu, ncpu),
-            "nn_queries_per_s": round(r["nn_queries"] / dt, 1), "matches": int(len(r["pairs"]))}
+    out = {"value": round(1.0 / dt, 4), "unit": "pairs/s", "cores": threads, "kind": "oracle",
+           "sample": "the whole 512x384 pair (3072 seeds, 10 iterations), binary64 C oracle, %d threads, "
+                     "%.2f s, %d NN queries, CPU %s, nproc %d" % (threads, dt, r["nn_queries"], cpu, ncpu),
+           "nn_queries_per_s": round(r["nn_queries"] / dt, 1), "matches": int(len(r["pairs"]))}
+    # one core: the fast scheme on the 64x48 pair and on this 512x384 pair
+    per_core = {}
+    for name, q in (("pair-64x48-f32", workloads.config_pair(0)), ("pair-512x384-f32", p)):
+        t = time.perf_counter()
+        r1 = oracle.fast(q.D1, q.H, q.W, q.D2, q.stride, q.offset, q.max_iters, nthreads=1)
+        dt1 = time.perf_counter() - t
+        per_core[name] = {"pairs_per_s": round(1.0 / dt1, 4), "seconds": round(dt1, 3), "threads": 1,
+                          "nn_queries_per_s": round(r1["nn_queries"] / dt1, 1)}
+    out["per_core"] = per_core
+    return out
 
 
 def cpu_samples():
@@ -332,10 +357,11 @@ def other_bruteforce(args, torch, dev):
     ws = torch.empty(mr.workspace_bytes(mr.MR_OP_MUTUAL_NN, A2, B2), dtype=torch.uint8, device=dev)
     steps = max(3, args.steps // 4)
     ms, kms, kn = time_steps(lambda: mr.mutual_nn(A2, B2, ws=ws), steps, 2, torch, 2 * steps)
-    fl = 2.0 * 2 * p2.N * p2.N * p2.d   # both directions are computed
+    fl = 2.0 * p2.N * p2.N * p2.d   # the method's work: the similarity matrix once
     out = {"pairs_per_s": round(1000.0 / ms, 2), "ms_per_call": round(ms, 3),
            "nn_queries_per_s": round(2 * p2.N * 1000.0 / ms, 1),
-           "mfma_frac_algorithmic": round(2.0 * p2.N * p2.N * p2.d / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+           "mfma_frac_algorithmic": round(fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+           "similarity_launches_per_call": kn / steps if steps else None,
            "roofline": roofline(fl, steps, kms, kn, "bf16")}
     return out
 
@@ -461,6 +487,7 @@ def main():
     dev = torch.device("cuda:0")
     if args.only:
         print(json.dumps({args.only: OTHER[args.only](args, torch, dev)}), flush=True)
+        release_device(torch)
         return
 
     p = workloads.config_pair(1)
@@ -479,8 +506,8 @@ def main():
         "nn_queries_per_step": r["nn_queries"], "iter_active": r["active"], "matches": r["matches"][0],
         "roofline": roofline(r["flops"], args.steps, r["kernel_ms"], r["launches"], "f32",
                              measured_traffic("nn_argmax_pair512x384_f32_traffic.json")),
-        "step_mfma_frac": round(r["flops"] / (r["ms"] * 1e-3) / 1e12 / PEAK_TFLOPS["f32"], 4),
-        "binding_roof_by_round": rounds_roofline(r, p.N, p.d, 4, PEAK_TFLOPS["f32"]),
+        "step_mfma_frac": round(r["flops"] / (r["ms"] * 1e-3) / 1e12 / PEAK_SPLIT_TFLOPS, 4),
+        "binding_roof_by_round": rounds_roofline(r, p.N, p.d, 4, PEAK_SPLIT_TFLOPS),
     }
     f1 = mr.FastReciprocal(*dev_maps(p, torch, dev), p.stride, p.offset, p.max_iters)
     A1, B1 = dev_maps(p, torch, dev)
@@ -496,6 +523,17 @@ def main():
         if not args.main_only:
             out["cpu_baseline"]["other_samples"] = cpu_samples()
     print(json.dumps(out), flush=True)
+    # release the device objects while the runtime is fully up, so that nothing of this
+    # process touches the GPU during interpreter teardown
+    del f1, A1, B1
+    release_device(torch)
+
+
+def release_device(torch):
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":
