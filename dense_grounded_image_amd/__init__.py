@@ -26,10 +26,10 @@ MR_OP_FAST_RECIPROCAL_GRAPH = 6
 MR_OP_INFONCE = 7
 MR_OP_INFONCE_BACKWARD = 8
 STATUS = {0: "MR_OK", 1: "MR_ERR_NULL", 2: "MR_ERR_SHAPE", 3: "MR_ERR_DTYPE", 4: "MR_ERR_PARAM",
-          5: "MR_ERR_WORKSPACE", 6: "MR_ERR_CAPACITY", 7: "MR_ERR_DEVICE"}
+          5: "MR_ERR_WORKSPACE", 6: "MR_ERR_CAPACITY", 7: "MR_ERR_DEVICE", 8: "MR_ERR_SCRATCH"}
 
 EXPORTS = ("mr_workspace_bytes", "mr_status_str", "mr_seed_count", "mr_nn_argmax", "mr_mutual_nn",
-           "mr_fast_reciprocal", "mr_fast_reciprocal_graph", "mr_point_nn", "mr_point_mutual_nn",
+           "mr_fast_reciprocal", "mr_fast_reciprocal_static", "mr_fast_reciprocal_graph", "mr_point_nn", "mr_point_mutual_nn",
            "mr_point_fast_reciprocal", "mr_infonce_forward", "mr_infonce_backward",
            "mr_profile_begin", "mr_profile_end", "mr_profile_end_each")
 
@@ -70,6 +70,8 @@ def load_library(path: str = LIB_PATH):
     lib.mr_mutual_nn.restype = ctypes.c_int
     lib.mr_fast_reciprocal.argtypes = [MP, MP, i32, i32, i32, P, i64, P, P, P, sz, P]
     lib.mr_fast_reciprocal.restype = ctypes.c_int
+    lib.mr_fast_reciprocal_static.argtypes = [MP, MP, i32, i32, i32, P, i64, P, P, P]
+    lib.mr_fast_reciprocal_static.restype = ctypes.c_int
     lib.mr_fast_reciprocal_graph.argtypes = [MP, P, i32, i32, i32, i32, P, i64, P, P, P, sz, P]
     lib.mr_fast_reciprocal_graph.restype = ctypes.c_int
     lib.mr_point_nn.argtypes = lib.mr_nn_argmax.argtypes
@@ -229,12 +231,17 @@ def point_mutual_nn(a, b, ws=None):
 
 class FastReciprocal:
     """Reusable call of the fast reciprocal scheme for fixed shapes: output and
-    workspace buffers are allocated once, so repeated calls allocate nothing."""
+    workspace buffers are allocated once, so repeated calls allocate nothing.
+    static_scratch=True calls mr_fast_reciprocal_static, which takes no workspace (the
+    library's fixed per-GPU scratch; descriptor maps only)."""
 
     def __init__(self, a, b, stride: int = 8, offset: Optional[int] = None, max_iters: int = 10,
-                 record_active: bool = True, point: bool = False):
+                 record_active: bool = True, point: bool = False, static_scratch: bool = False):
         torch = _torch()
         self.lib = load_library()
+        if static_scratch and point:
+            raise ValueError("the static-scratch call covers descriptor maps only")
+        self.static = bool(static_scratch)
         self.fn = self.lib.mr_point_fast_reciprocal if point else self.lib.mr_fast_reciprocal
         op = MR_OP_POINT_FAST_RECIPROCAL if point else MR_OP_FAST_RECIPROCAL
         self.stride = int(stride)
@@ -249,13 +256,20 @@ class FastReciprocal:
         self.active = (torch.empty((self.B, max(1, self.max_iters)), dtype=torch.int32, device=dev)
                        if record_active else None)
         need = self.lib.mr_workspace_bytes(op, ctypes.byref(ma), ctypes.byref(mb), 0, self.stride, self.offset)
-        self.ws = _workspace(need, dev)
+        self.ws = None if self.static else _workspace(need, dev)
         self.shape = (tuple(a.shape), tuple(b.shape), a.dtype)
 
     def __call__(self, a, b):
         if (tuple(a.shape), tuple(b.shape), a.dtype) != self.shape:
             raise ValueError("shapes differ from the ones this FastReciprocal was built for")
         ma, mb = _as_map(a), _as_map(b)
+        if self.static:
+            rc = self.lib.mr_fast_reciprocal_static(
+                ctypes.byref(ma), ctypes.byref(mb), self.stride, self.offset, self.max_iters,
+                self.pairs.data_ptr(), self.cap, self.n_pairs.data_ptr(),
+                self.active.data_ptr() if self.active is not None else None, _stream(a))
+            _check("mr_fast_reciprocal_static", rc)
+            return self.pairs, self.n_pairs, self.active
         rc = self.fn(ctypes.byref(ma), ctypes.byref(mb), self.stride, self.offset, self.max_iters,
                      self.pairs.data_ptr(), self.cap, self.n_pairs.data_ptr(),
                      self.active.data_ptr() if self.active is not None else None,

@@ -39,9 +39,17 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "mr.h"
+
+// Scratch memory of mr_fast_reciprocal_static: a fixed array in device memory, one
+// copy per GPU, held until the process ends.  Host code never passes this name to a
+// kernel or a copy (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress, per device.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -2653,6 +2661,25 @@ int infonce_backward_impl(const mr_map* a, const mr_map* b, const int32_t* gt, i
     return dev_err();
 }
 
+// Device address of `scratch` on the current device, looked up once per device (with
+// that device current) and kept; every GPU holds its own copy at its own address.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MR_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MR_ERR_DEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MR_OK;
+}
+
 }  // namespace
 
 // ============================================================================ C ABI
@@ -2669,6 +2696,7 @@ const char* mr_status_str(int status) {
         case MR_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case MR_ERR_CAPACITY: return "output capacity below the bound";
         case MR_ERR_DEVICE: return "HIP call failed";
+        case MR_ERR_SCRATCH: return "the problem needs more scratch than the static buffer holds";
         default: return "unknown status";
     }
 }
@@ -2737,6 +2765,24 @@ int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t
                        int32_t* pairs, int64_t cap, int64_t* n_pairs, int32_t* iter_active, void* ws,
                        size_t ws_bytes, void* stream) {
     return fast_impl(a, b, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, ws_bytes, stream, M_INNER);
+}
+
+int mr_fast_reciprocal_static(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset,
+                              int32_t max_iters, int32_t* pairs, int64_t cap, int64_t* n_pairs,
+                              int32_t* iter_active, void* stream) {
+    // the same validation order as mr_fast_reciprocal, then the size check against the
+    // static buffer before anything is launched
+    int rc = validate_for(a, b, M_INNER);
+    if (rc) return rc;
+    if (stride < 1 || offset < 0 || max_iters < 0) return MR_ERR_PARAM;
+    if (!pairs || !n_pairs) return MR_ERR_NULL;
+    const int64_t ns = seed_count(a->h, a->w, stride, offset);
+    if (cap < ns) return MR_ERR_CAPACITY;
+    if (fast_layout(a, b, ns).total > kStaticScratchBytes) return MR_ERR_SCRATCH;
+    void* ws = nullptr;
+    if ((rc = static_scratch(&ws))) return rc;
+    return fast_impl(a, b, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, kStaticScratchBytes,
+                     stream, M_INNER);
 }
 
 int mr_point_nn(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q, int32_t* out_idx,

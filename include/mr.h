@@ -69,7 +69,8 @@ typedef enum {
     MR_ERR_PARAM = 4,     /* stride < 1, offset < 0, max_iters < 0, bad op, n_q < 0 */
     MR_ERR_WORKSPACE = 5, /* ws NULL/misaligned while needed, or ws_bytes too small */
     MR_ERR_CAPACITY = 6,  /* cap below the static bound on the number of pairs */
-    MR_ERR_DEVICE = 7     /* a HIP call failed */
+    MR_ERR_DEVICE = 7,    /* a HIP call failed */
+    MR_ERR_SCRATCH = 8    /* mr_fast_reciprocal_static: more scratch than its static buffer */
 } mr_status;
 
 typedef struct {
@@ -148,6 +149,26 @@ int mr_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_b
 int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset,
                        int32_t max_iters, int32_t* pairs, int64_t cap, int64_t* n_pairs,
                        int32_t* iter_active, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mr_fast_reciprocal_static: mr_fast_reciprocal without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments (minus ws and
+ * ws_bytes), results, validation and error codes as mr_fast_reciprocal.
+ *   Scratch: a static device array of 8 MiB per GPU, held by the library until the
+ *   process ends; the calling thread's current device must be the one `stream` and
+ *   the maps belong to.  Problems needing more (mr_workspace_bytes with
+ *   MR_OP_FAST_RECIPROCAL above 8 MiB: e.g. more than nine 512x384 pairs per call
+ *   at stride 8; one 1024x768 pair needs 3.5 MiB) return MR_ERR_SCRATCH before
+ *   anything is launched.  The call allocates
+ *   nothing: no hipMalloc, hipFree or allocating library routine.
+ *   Every call on a GPU shares that GPU's buffer, and each call re-initialises the
+ *   part it uses on its stream: calls that overlap in time on one GPU (other threads,
+ *   other streams) race and must be serialised by the caller.
+ * --------------------------------------------------------------------------- */
+int mr_fast_reciprocal_static(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset,
+                              int32_t max_iters, int32_t* pairs, int64_t cap, int64_t* n_pairs,
+                              int32_t* iter_active, void* stream);
 
 /* ---------------------------------------------------------------------------
  * mr_fast_reciprocal_graph: the fast scheme on many pairs of one collection of

@@ -12,7 +12,7 @@ import dense_grounded_image_amd as mr
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mr.h")
 
-OK, NULL, SHAPE, DTYPE, PARAM, WS, CAP = 0, 1, 2, 3, 4, 5, 6
+OK, NULL, SHAPE, DTYPE, PARAM, WS, CAP, DEVICE, SCRATCH = 0, 1, 2, 3, 4, 5, 6, 7, 8
 FAKE = 1 << 20  # an aligned non-NULL address; validation failures never dereference it
 
 
@@ -59,8 +59,9 @@ def R(x):
 
 
 def test_status_strings_and_seed_count(lib):
-    for code in range(0, 8):
+    for code in range(0, 9):
         assert lib.mr_status_str(code)
+    assert lib.mr_status_str(SCRATCH) != lib.mr_status_str(99)
     assert lib.mr_seed_count(512, 384, 8, 4) == 3072
     assert lib.mr_seed_count(1024, 768, 8, 4) == 12288
     assert lib.mr_seed_count(64, 48, 8, 4) == 48
@@ -119,6 +120,30 @@ def test_fast_reciprocal_validation(lib):
     big = M(128, 96)
     assert lib.mr_workspace_bytes(2, R(big), R(big), 0, 8, 4) >= need
     assert lib.mr_workspace_bytes(2, R(a), R(b), 0, 4, 2) >= need
+
+
+def test_fast_reciprocal_static_validation(lib):
+    """The workspace-free call validates like mr_fast_reciprocal and rejects problems
+    larger than its static scratch (8 MiB) before anything is launched."""
+    a, b = M(64, 48), M(64, 48)
+    out = ctypes.c_void_p(FAKE)
+    call = lambda a=a, b=b, stride=8, offset=4, T=10, pairs=out, cap=48, n=out: \
+        lib.mr_fast_reciprocal_static(R(a), R(b), stride, offset, T, pairs, cap, n, None, None)
+    assert call(stride=0) == PARAM
+    assert call(offset=-1) == PARAM
+    assert call(T=-1) == PARAM
+    assert call(pairs=None) == NULL
+    assert call(n=None) == NULL
+    assert call(cap=47) == CAP
+    assert call(a=M(dtype=7), b=M(dtype=7)) == DTYPE
+    assert call(a=M(), b=M(batch=2)) == SHAPE
+    # 2048 x 2048 pixels: the per-pixel state alone is 16 MiB
+    big = M(2048, 2048)
+    assert lib.mr_workspace_bytes(2, R(big), R(big), 0, 8, 4) > (8 << 20)
+    assert call(a=big, b=big, cap=1 << 20) == SCRATCH
+    # ten 512x384 pairs at stride 8 need more than 8 MiB, nine fit
+    assert call(a=M(512, 384, batch=10), b=M(512, 384, batch=10), cap=3072) == SCRATCH
+    assert lib.mr_workspace_bytes(2, R(M(512, 384, batch=9)), R(M(512, 384, batch=9)), 0, 8, 4) <= (8 << 20)
 
 
 def test_mutual_and_nn_validation(lib):
