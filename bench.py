@@ -358,11 +358,18 @@ def other_bruteforce(args, torch, dev):
     steps = max(3, args.steps // 4)
     ms, kms, kn = time_steps(lambda: mr.mutual_nn(A2, B2, ws=ws), steps, 2, torch, 2 * steps)
     fl = 2.0 * p2.N * p2.N * p2.d   # the method's work: the similarity matrix once
+    # the two-pass alternative: a row search in each direction (the maps' roles swapped),
+    # i.e. the matrix computed twice; the mutual call above computes it once
+    wn = torch.empty(mr.workspace_bytes(mr.MR_OP_NN_ARGMAX, A2, B2, p2.N), dtype=torch.uint8, device=dev)
+    ms2, _, _ = time_steps(lambda: (mr.nn_argmax(A2, B2, ws=wn), mr.nn_argmax(B2, A2, ws=wn)), steps, 2, torch)
     out = {"pairs_per_s": round(1000.0 / ms, 2), "ms_per_call": round(ms, 3),
+           "variant": "fused row + column pass (rowcol_argmax_kernel), then both recoveries",
+           "two_pass_ms": round(ms2, 3),
+           "two_pass_variant": "two row searches (nn_argmax_kernel, maps swapped), without the pair compaction",
            "nn_queries_per_s": round(2 * p2.N * 1000.0 / ms, 1),
            "mfma_frac_algorithmic": round(fl / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
            "similarity_launches_per_call": kn / steps if steps else None,
-           "roofline": roofline(fl, steps, kms, kn, "bf16")}
+           "roofline": roofline(fl, steps, kms, kn, "bf16", kernel="rowcol_argmax_kernel")}
     return out
 
 

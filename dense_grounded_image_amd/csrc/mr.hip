@@ -57,6 +57,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;            // waves per workgroup
@@ -1164,6 +1165,364 @@ __global__ __launch_bounds__(kThreads) void recover_rows_kernel(NNArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------- fused row + column argmax
+
+// Brute-force reciprocal NN needs both nearest-neighbour maps of one similarity
+// matrix: NN(a_i, b) over its rows and NN(b_k, a) over its columns ("MASt3R
+// dissection", section 1 diagram: the match set needs both directions; section 3
+// "Napkin Formula").  rowcol_argmax_kernel computes every 32x32 similarity tile once
+// and reduces it both ways:
+//  - rows (queries = pixels of a, held as MFMA B operands): the tile-level running
+//    maximum of TileBest (best compared score, first b tile reaching it), merged
+//    across database segments by atomicMax on (score, ~tile) keys and resolved to a
+//    row by recover_rows_kernel;
+//  - columns (pixels of b, streamed as MFMA A operands): per b tile, each lane's
+//    maximum over the wave's query tiles (in-lane, a max3 fold), then a transpose
+//    through LDS and a 16-value maximum per row (one lane pair per row of the tile),
+//    then a maximum over the workgroup's waves and one atomicMax per b row and
+//    workgroup on (score, ~query block) keys, a query block being the 256
+//    consecutive query pixels of one wave.  recover_cols_kernel resolves each
+//    winning block to the lowest query row of the winning score.
+// Both directions compare scores after clearing their 4 low bits, lowest index on
+// ties, exactly like nn_argmax_kernel, so the results equal two separate searches.
+// The b tiles of a workgroup's segment pass through a two-group LDS ring, copied
+// straight from global memory into LDS (global_load_lds, no registers) one group of
+// kRcFlush tiles ahead; the barrier that publishes a group's wave maxima also
+// publishes the next group's copy.  The matrix work is half that of two searches; the
+// vector work (a tile-level row maximum and a column fold for every score) is about
+// the same, and it bounds the kernel on this chip.
+constexpr int kRcWaves = 8;                 // waves per workgroup (two per SIMD)
+constexpr int kRcThreads = 64 * kRcWaves;
+constexpr int kRcQT = 8;                    // query tiles per wave (one query block)
+constexpr int kRcGroupTiles = kRcWaves * kRcQT;
+constexpr int kRcFlush = 8;                 // b tiles per column merge (one barrier each)
+constexpr int kRcPad = 36;                  // floats per row of the transpose area (16-byte rows, no write conflicts)
+constexpr int kRcMaxTileBytes = 32 * 64;    // a 32-row b tile of bf16 rows, d <= 32
+constexpr uint32_t kWaitVm0 = 0x0F70;       // s_waitcnt vmcnt(0) (expcnt, lgkmcnt at their maximum)
+
+typedef const void __attribute__((address_space(1)))* gptr_t;
+typedef void __attribute__((address_space(3)))* lptr_t;
+
+struct RowColArgs {
+    const void* amap;        // [batch][na][d] bf16: queries (rows of the similarity)
+    const void* bmap;        // [batch][nb][d] bf16: streamed (columns)
+    int64_t a_pair_elems, b_pair_elems;
+    int32_t na, nb, d;
+    int32_t nsg;             // b segments per query group
+    uint64_t* keys_ab;       // [batch][na]: (score, ~b tile)
+    uint64_t* keys_ba;       // [batch][nb]: (score, ~query block)
+};
+
+template <int P>
+__global__ __launch_bounds__(kRcThreads) void rowcol_argmax_kernel(RowColArgs a) {
+    using Op = Operand<AR_BF16, P>;
+    __shared__ __attribute__((aligned(16))) float tr[kRcWaves][32 * kRcPad];   // per-wave transpose
+    __shared__ float mg[2 * kRcFlush + 1][kRcWaves][32];   // wave maxima, two sets (+ a discard slot)
+    __shared__ __attribute__((aligned(16))) char ring[2][kRcFlush * kRcMaxTileBytes];   // b tiles, two groups
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5;
+    const int jl = lane & 31;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.y;
+    const int na = a.na, nb = a.nb, d = a.d;
+    const int nqt = (na + 31) >> 5;
+    const int ntiles = (nb + 31) >> 5;
+    const int qgroups = (nqt + kRcGroupTiles - 1) / kRcGroupTiles;
+    const int nsg = a.nsg;
+    const int items = qgroups * nsg;
+    const void* abase = static_cast<const uint16_t*>(a.amap) + pair * a.a_pair_elems;
+    const char* bbytes = reinterpret_cast<const char*>(static_cast<const uint16_t*>(a.bmap) + pair * a.b_pair_elems);
+    uint64_t* keys_ab = a.keys_ab + (int64_t)pair * na;
+    uint64_t* keys_ba = a.keys_ba + (int64_t)pair * nb;
+    int off[P];
+    Op::db_offsets(jl, h, d, off);
+    const int64_t tile_bytes = (int64_t)64 * d;   // 32 rows of 2d bytes
+    float* trw = tr[wv];
+    int gc = 0;   // merge sets used so far (alternating halves of mg)
+
+    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+        const int qg = item / nsg;
+        const int sg = item - qg * nsg;
+        const int tq0 = qg * kRcGroupTiles + wv * kRcQT;               // this wave's first query tile
+        const int nact = nqt - tq0 >= kRcQT ? kRcQT : (nqt - tq0 > 0 ? nqt - tq0 : 0);
+        const int qvalid_last = na - (tq0 + kRcQT - 1) * 32;            // valid lanes of the last tile
+        const bool full = nact == kRcQT && qvalid_last >= 32;           // no partial query tile
+        Op q[kRcQT];
+#pragma unroll
+        for (int j = 0; j < kRcQT; ++j) {
+            const int qp = (tq0 + j) * 32 + jl;
+            const bool valid = j < nact && qp < na;
+            q[j].load(abase, valid ? qp : 0, valid, h, d, 1);
+        }
+        const int t0 = (int)((int64_t)sg * ntiles / nsg);
+        const int t1 = (int)((int64_t)(sg + 1) * ntiles / nsg);
+        TileBest<kRcQT> best;
+
+        // b tiles [tg, tend) are copied into ring set `set` by the workgroup, straight
+        // from global memory into LDS (no registers), 16 bytes per lane: the group's
+        // real rows are contiguous in memory and in the set; lanes past them repeat the
+        // last chunk into the unused rest of the set
+        auto load_group = [&](int tg, int tend, int set) {
+            const int rows = (tend * 32 < nb ? tend * 32 : nb) - tg * 32;
+            const int nch = rows * (2 * d) / 16;
+            const char* src = bbytes + (int64_t)tg * tile_bytes;
+            for (int i = wv; i * 64 < nch; i += kRcWaves) {
+                const int ch = i * 64 + lane < nch ? i * 64 + lane : nch - 1;
+                __builtin_amdgcn_global_load_lds((gptr_t)(src + (int64_t)ch * 16), (lptr_t)(&ring[set][i * 1024]), 16,
+                                                 0, 0);
+            }
+        };
+        // column values of tile t (the lane's maximum over its valid queries, rows
+        // (h, v)) -> the wave's maximum per row, through the transpose area, into merge
+        // slot k of the current set
+        auto column_out = [&](const float (&c)[16], int set, int k) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) trw[(h * 16 + v) * kRcPad + jl] = c[v];
+            const int rr = lane >> 1;
+            const float4* src = reinterpret_cast<const float4*>(trw + rr * kRcPad + (lane & 1) * 16);
+            const float4 y0 = src[0], y1 = src[1], y2 = src[2], y3 = src[3];
+            auto mx3 = [](float p, float q_, float s_) {
+                return __builtin_elementwise_maximum(__builtin_elementwise_maximum(p, q_), s_);
+            };
+            float m = mx3(mx3(y0.x, y0.y, y0.z), mx3(y0.w, y1.x, y1.y), mx3(y1.z, y1.w, y2.x));
+            m = mx3(m, mx3(y2.y, y2.z, y2.w), mx3(y3.x, y3.y, y3.z));
+            m = __builtin_elementwise_maximum(m, y3.w);
+            m = __builtin_elementwise_maximum(m, __shfl_xor(m, 1));
+            if ((lane & 1) == 0) mg[set + k][wv][tile_row(rr & 15, rr >> 4)] = m;
+        };
+        // after a group of tiles: merge the waves (lowest block on equal compared
+        // scores) and leave one atomic per b row and workgroup
+        auto merge = [&](int set, int tg, int tend) {
+            __syncthreads();
+            if ((int)threadIdx.x < kRcFlush * 32) {
+                const int k = threadIdx.x >> 5, rw = threadIdx.x & 31;
+                const int t = tg + k;
+                if (t < tend) {
+                    float bs = -INFINITY;
+                    int bw = -1;
+#pragma unroll
+                    for (int w = 0; w < kRcWaves; ++w) {
+                        const float x = trunc4(mg[set + k][w][rw]);
+                        if (x > bs) { bs = x; bw = w; }
+                    }
+                    const int row = t * 32 + rw;
+                    if (bw >= 0 && row < nb)
+                        atomicMax(reinterpret_cast<unsigned long long*>(&keys_ba[row]),
+                                  (unsigned long long)(((uint64_t)ordered_bits(bs) << 32) |
+                                                       (uint64_t)(~(uint32_t)(qg * kRcWaves + bw))));
+                }
+            }
+        };
+        // the segment in groups of kRcFlush tiles: group g + 1 is copied into LDS while
+        // group g is multiplied; one barrier per group publishes the copy and the wave
+        // maxima.  FAST: every query tile of the wave full and no ragged b tile
+        // (straight-line code, query tiles in pairs with one max3 per column value).
+        auto stream = [&](auto fast) {
+            constexpr bool FAST = decltype(fast)::value;
+            if (t0 < t1) {
+                load_group(t0, t0 + kRcFlush < t1 ? t0 + kRcFlush : t1, gc & 1);
+                __builtin_amdgcn_s_waitcnt(kWaitVm0);
+                __syncthreads();
+            }
+            for (int tg = t0; tg < t1; tg += kRcFlush, ++gc) {
+                const int tend = tg + kRcFlush < t1 ? tg + kRcFlush : t1;
+                const int set = gc & 1;
+                if (tend < t1) load_group(tend, tend + kRcFlush < t1 ? tend + kRcFlush : t1, set ^ 1);
+                if constexpr (FAST) {
+                    // units of two query tiles; the epilogue of each unit (rows of both,
+                    // and the column fold) runs one unit behind its products, between the
+                    // products of the next unit, which also keeps one unit's products live
+                    // at a time; the column values of a tile leave through the transpose
+                    // after its last unit's epilogue.  The group starts with a stand-in
+                    // unit of -inf scores (it changes no row state) whose column output
+                    // goes to the discard slot.  The b operand is read from LDS one tile
+                    // ahead (the whole group is in the ring; the read past its last tile
+                    // stays inside the set).
+                    f32x16 p0, p1;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) { p0[v] = -INFINITY; p1[v] = -INFINITY; }
+                    float c[16];
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) c[v] = -INFINITY;
+                    auto fold = [&](const f32x16& y0, const f32x16& y1, int tt, int j) {
+                        best.template tile<false>(y0, tt, h, nb, j);
+                        best.template tile<false>(y1, tt, h, nb, j + 1);
+                        if (j == 0) {
+#pragma unroll
+                            for (int v = 0; v < 16; ++v) c[v] = __builtin_elementwise_maximum(y0[v], y1[v]);
+                        } else {
+#pragma unroll
+                            for (int v = 0; v < 16; ++v)
+                                c[v] = __builtin_elementwise_maximum(__builtin_elementwise_maximum(c[v], y0[v]), y1[v]);
+                        }
+                    };
+                    Op nxt;
+                    nxt.load_db(&ring[set][0], off);
+                    for (int t = tg; t < tend; ++t) {
+                        const Op cur = nxt;
+                        nxt.load_db(&ring[set][(t + 1 - tg < kRcFlush ? t + 1 - tg : 0) * tile_bytes], off);
+#pragma unroll
+                        for (int j = 0; j < kRcQT; j += 2) {
+                            const f32x16 x0 = cur.mfma(q[j], f32x16{});
+                            const f32x16 x1 = cur.mfma(q[j + 1], f32x16{});
+                            if (j == 0) {
+                                // the previous tile's last unit, then its column output
+                                fold(p0, p1, t - 1, kRcQT - 2);
+                                column_out(c, t == tg ? 2 * kRcFlush : set * kRcFlush + (t - 1 - tg), 0);
+                                interleave_mfma_valu<2 * P, 14>();
+                            } else {
+                                fold(p0, p1, t, j - 2);
+                                interleave_mfma_valu<2 * P, 10>();
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
+                            p0 = x0;
+                            p1 = x1;
+                        }
+                    }
+                    fold(p0, p1, tend - 1, kRcQT - 2);
+                    column_out(c, set * kRcFlush + (tend - 1 - tg), 0);
+                } else {
+                for (int t = tg; t < tend; ++t) {
+                    Op cur;
+                    cur.load_db(&ring[set][(t - tg) * tile_bytes], off);
+                    float c[16];
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) c[v] = -INFINITY;
+                    const bool ragged = (t + 1) * 32 > nb;
+#pragma unroll
+                    for (int j = 0; j < kRcQT; ++j) {
+                        if (j < nact) {
+                            const f32x16 x = cur.mfma(q[j], f32x16{});
+                            best.step(x, t, h, nb, j, ragged);
+                            // queries past na hold zero operands: they take no part in the columns
+                            const bool qok = (tq0 + j) * 32 + jl < na;
+#pragma unroll
+                            for (int v = 0; v < 16; ++v)
+                                c[v] = qok ? __builtin_elementwise_maximum(c[v], x[v]) : c[v];
+                        }
+                    }
+                    column_out(c, set * kRcFlush, t - tg);
+                }
+                }
+                __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's copies of the next group
+                merge(set * kRcFlush, tg, tend);        // barrier, then the wave maxima
+            }
+        };
+        if (full && t1 * 32 <= nb) stream(std::true_type{});
+        else stream(std::false_type{});
+
+        // rows: merge the lane halves, one atomic per query and item
+#pragma unroll
+        for (int j = 0; j < kRcQT; ++j) {
+            uint64_t key = best.bt[j] >= 0 ? pack_key(best.bv[j], (uint32_t)best.bt[j]) : 0;
+            const uint64_t o = shfl_xor_u64(key, 32);
+            key = o > key ? o : key;
+            const int qp = (tq0 + j) * 32 + jl;
+            if (h == 0 && j < nact && qp < na && key != 0)
+                atomicMax(reinterpret_cast<unsigned long long*>(&keys_ab[qp]), (unsigned long long)key);
+        }
+    }
+}
+
+// (score, ~query block) -> (score, ~row) for the columns: one b tile per wave.  For
+// each distinct winning block among the tile's 32 rows (a wave-uniform loop), the
+// wave multiplies the b tile (A operand, loaded as the fused pass loaded it) with the
+// block's query tiles (B operands) -- the same instruction, operand layout and step
+// order, so the scores are bitwise those that were compared -- and every row won by
+// that block takes the lowest query whose compared score equals its key's score.
+template <int P>
+__global__ __launch_bounds__(kThreads) void recover_cols_kernel(RowColArgs a) {
+    using Op = Operand<AR_BF16, P>;
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5;
+    const int jl = lane & 31;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.y;
+    const int na = a.na, nb = a.nb, d = a.d;
+    const int nqt = (na + 31) >> 5;
+    const int nblocks = (nqt + kRcQT - 1) / kRcQT;
+    const int ntiles = (nb + 31) >> 5;
+    const void* abase = static_cast<const uint16_t*>(a.amap) + pair * a.a_pair_elems;
+    const void* bbase = static_cast<const uint16_t*>(a.bmap) + pair * a.b_pair_elems;
+    uint64_t* keys_ba = a.keys_ba + (int64_t)pair * nb;
+    for (int t = blockIdx.x * kWaves + wv; t < ntiles; t += gridDim.x * kWaves) {
+        const int brow = t * 32 + jl;
+        Op r;
+        r.load(bbase, brow < nb ? brow : 0, brow < nb, h, d, 2);
+        // the keys of the 16 rows (h, v) this lane sees (vectors: the compare loop
+        // below indexes them with a wave-uniform v)
+        f32x16 sc;
+        i32x16 blk, found;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row = t * 32 + tile_row(v, h);
+            const uint64_t k = row < nb ? keys_ba[row] : 0;
+            sc[v] = from_ordered((uint32_t)(k >> 32));
+            const uint32_t b = ~(uint32_t)k;
+            blk[v] = k && b < (uint32_t)nblocks ? (int)b : -1;
+            found[v] = INT_MAX;
+        }
+        while (true) {
+            // the lowest unresolved block of the tile (wave-uniform)
+            int lo = INT_MAX;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) lo = blk[v] >= 0 && blk[v] < lo ? blk[v] : lo;
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1) {
+                const int o = __shfl_xor(lo, m);
+                lo = o < lo ? o : lo;
+            }
+            lo = __builtin_amdgcn_readfirstlane(lo);
+            if (lo == INT_MAX) break;
+            // which v (in either half) this block won: only those are compared
+            uint32_t vm = 0;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) vm |= blk[v] == lo ? (1u << v) : 0u;
+            vm |= (uint32_t)__shfl_xor((int)vm, 32);
+            vm = __builtin_amdgcn_readfirstlane(vm);
+            const int tq0 = lo * kRcQT;
+            // the block's query tiles, all loads issued before the products
+            Op qb[kRcQT];
+#pragma unroll
+            for (int j = 0; j < kRcQT; ++j) {
+                const int qp = (tq0 + j) * 32 + jl;
+                qb[j].load(abase, qp < na ? qp : 0, qp < na, h, d, 1);
+            }
+#pragma unroll
+            for (int j = 0; j < kRcQT; ++j) {
+                if (tq0 + j >= nqt) break;
+                const int qp = (tq0 + j) * 32 + jl;
+                const f32x16 x = r.mfma(qb[j], f32x16{});
+                for (uint32_t m = vm; m; m &= m - 1) {
+                    const int v = __builtin_ctz(m);
+                    if (blk[v] == lo && qp < na && trunc4(x[v]) == sc[v] && qp < found[v]) found[v] = qp;
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) blk[v] = blk[v] == lo ? -2 : blk[v];
+        }
+        // lowest query over the 32 lanes of each half, then lane (h, jl < 16) writes row (h, v = jl)
+        int mine = INT_MAX;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            int f = found[v];
+#pragma unroll
+            for (int m = 16; m >= 1; m >>= 1) {
+                const int o = __shfl_xor(f, m);
+                f = o < f ? o : f;
+            }
+            if (jl == v) mine = f;
+        }
+        if (jl < 16) {
+            const int row = t * 32 + tile_row(jl, h);
+            if (row < nb) {
+                const uint64_t k = keys_ba[row];
+                keys_ba[row] = (k != 0 && mine != INT_MAX) ? pack_key(from_ordered((uint32_t)(k >> 32)), (uint32_t)mine) : 0;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------- pointmaps
 
 // Nearest neighbours of 3D points ("DUSt3R and MASt3R explained", the paragraph on
@@ -1994,10 +2353,23 @@ int grid_1d(int64_t n, int threads = 256, int cap = 1 << 24) {
 
 int dev_err() { return hipGetLastError() == hipSuccess ? MR_OK : MR_ERR_DEVICE; }
 
+// hipEvents around one launch for the measurement aid (when it is on and has room).
+int prof_mark(hipStream_t st, bool& rec) {
+    rec = g_prof.on && g_prof.used < g_prof.cap;
+    return rec && hipEventRecord(g_prof.ev[2 * g_prof.used], st) != hipSuccess ? MR_ERR_DEVICE : MR_OK;
+}
+int prof_close(hipStream_t st, bool rec) {
+    if (!rec) return MR_OK;
+    if (hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st) != hipSuccess) return MR_ERR_DEVICE;
+    ++g_prof.used;
+    return MR_OK;
+}
+
+
 // Workgroups of kernel K (kThreads each) that the GPU holds at once: a launch-shape
 // constant, computed once per process (a thread-safe static initialisation; a plain
 // int, so process teardown has nothing to release).
-template <auto K>
+template <auto K, int THREADS = kThreads>
 int resident_blocks() {
     static const int resident = [] {
         int dev = 0, cus = 256, per_cu = 0;
@@ -2005,7 +2377,7 @@ int resident_blocks() {
             hipDeviceProp_t prop;
             if (hipGetDeviceProperties(&prop, dev) == hipSuccess) cus = prop.multiProcessorCount;
         }
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, kThreads, 0) != hipSuccess || per_cu < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, THREADS, 0) != hipSuccess || per_cu < 1)
             per_cu = 1;
         return cus * per_cu;
     }();
@@ -2244,6 +2616,64 @@ int nn_impl(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q
     return dev_err();
 }
 
+// The fused row + column pass for bf16 maps (d <= 32): rowcol_argmax_kernel, then the
+// two recoveries (tile -> row for the rows, query block -> row for the columns).  The
+// keys are zero on entry.
+template <int P>
+int launch_rowcol_t(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* kba, hipStream_t st) {
+    const int batch = a->batch;
+    const int64_t na = npix(a), nb = npix(b);
+    if (na == 0 || nb == 0) return MR_OK;
+    RowColArgs x;
+    memset(&x, 0, sizeof(x));
+    x.amap = a->data;
+    x.bmap = b->data;
+    x.a_pair_elems = na * a->d;
+    x.b_pair_elems = nb * b->d;
+    x.na = (int32_t)na;
+    x.nb = (int32_t)nb;
+    x.d = a->d;
+    x.keys_ab = kab;
+    x.keys_ba = kba;
+    // segments per query group: about three rounds of the resident workgroups, a
+    // multiple of 8 when large (each XCD then streams the same eighth of b), at most
+    // one per b tile
+    const int resident = grid_per_pair(resident_blocks<rowcol_argmax_kernel<P>, kRcThreads>(), batch);
+    const int64_t nqt = (na + 31) / 32, ntiles = (nb + 31) / 32;
+    const int64_t qgroups = (nqt + kRcGroupTiles - 1) / kRcGroupTiles;
+    int64_t nsg = (3 * (int64_t)resident + qgroups - 1) / qgroups;
+    if (nsg >= 8) nsg = (nsg + 7) & ~int64_t(7);
+    const int64_t cap = ntiles < kMaxSegGroups ? ntiles : kMaxSegGroups;
+    nsg = nsg < 1 ? 1 : (nsg > cap ? cap : nsg);
+    x.nsg = (int32_t)nsg;
+    const int64_t items = qgroups * nsg;
+    const int gx = (int)(items < resident ? items : resident);
+    bool rec = false;
+    int rc;
+    if ((rc = prof_mark(st, rec))) return rc;
+    hipLaunchKernelGGL((rowcol_argmax_kernel<P>), dim3(gx, batch), dim3(kRcThreads), 0, st, x);
+    if (dev_err()) return MR_ERR_DEVICE;
+    if ((rc = prof_close(st, rec))) return rc;
+    NNArgs f = nn_args(a, a->data, 1, b, b->data, 2);
+    f.qsrc = Q_ALL;
+    f.host_count = (int32_t)na;
+    f.keys = kab;
+    f.keys_stride = na;
+    const int rgx = (int)((na + 31) / 32 < (1 << 20) ? (na + 31) / 32 : (1 << 20));
+    hipLaunchKernelGGL((recover_rows_kernel<AR_BF16, P>), dim3(rgx, batch), dim3(kThreads), 0, st, f);
+    const int cgx = (int)((ntiles + kWaves - 1) / kWaves < (1 << 20) ? (ntiles + kWaves - 1) / kWaves : (1 << 20));
+    hipLaunchKernelGGL((recover_cols_kernel<P>), dim3(cgx, batch), dim3(kThreads), 0, st, x);
+    return dev_err();
+}
+
+int launch_rowcol(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* kba, hipStream_t st) {
+    switch ((a->d + 15) / 16) {
+        case 1: return launch_rowcol_t<1>(a, b, kab, kba, st);
+        case 2: return launch_rowcol_t<2>(a, b, kab, kba, st);
+        default: return MR_ERR_SHAPE;
+    }
+}
+
 int mutual_impl(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba, int32_t* pairs, int64_t cap,
                 int64_t* n_pairs, void* ws, size_t ws_bytes, void* stream, int metric) {
     int rc = validate_for(a, b, metric);
@@ -2264,18 +2694,23 @@ int mutual_impl(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba
     hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(batch * nb)), dim3(256), 0, st, kba, batch * nb, (uint64_t)0);
     if (dev_err()) return MR_ERR_DEVICE;
     const void *ad = a->data, *bd = b->data;
-    NNArgs f = nn_args(a, ad, 1, b, bd, 2);
-    f.qsrc = Q_ALL;
-    f.host_count = (int32_t)na;
-    f.keys = kab;
-    f.keys_stride = na;
-    if ((rc = launch_search(f, metric, ar, batch, st))) return rc;
-    NNArgs r = nn_args(b, bd, 2, a, ad, 1);
-    r.qsrc = Q_ALL;
-    r.host_count = (int32_t)nb;
-    r.keys = kba;
-    r.keys_stride = nb;
-    if ((rc = launch_search(r, metric, ar, batch, st))) return rc;
+    if (metric == M_INNER && ar == AR_BF16 && a->d <= 32) {
+        // both directions from one pass over the similarity tiles
+        if ((rc = launch_rowcol(a, b, kab, kba, st))) return rc;
+    } else {
+        NNArgs f = nn_args(a, ad, 1, b, bd, 2);
+        f.qsrc = Q_ALL;
+        f.host_count = (int32_t)na;
+        f.keys = kab;
+        f.keys_stride = na;
+        if ((rc = launch_search(f, metric, ar, batch, st))) return rc;
+        NNArgs r = nn_args(b, bd, 2, a, ad, 1);
+        r.qsrc = Q_ALL;
+        r.host_count = (int32_t)nb;
+        r.keys = kba;
+        r.keys_stride = nb;
+        if ((rc = launch_search(r, metric, ar, batch, st))) return rc;
+    }
     hipLaunchKernelGGL(decode_keys_kernel, dim3(grid_1d(batch * na)), dim3(256), 0, st, kab, batch * na, nn_ab,
                        (float*)nullptr, 0);
     hipLaunchKernelGGL(decode_keys_kernel, dim3(grid_1d(batch * nb)), dim3(256), 0, st, kba, batch * nb, nn_ba,
@@ -2431,18 +2866,6 @@ int validate_nce(const mr_map* a, const mr_map* b, int64_t n_gt) {
     if (npix(b) == 0) return MR_ERR_SHAPE;   // the softmax needs at least one row
     if (n_gt > 0 && npix(a) == 0) return MR_ERR_SHAPE;   // no ground-truth row can name a row of an empty map
     if (a->dtype == MR_F32 && (a->d % 8 != 0 || a->d > 32)) return MR_ERR_SHAPE;
-    return MR_OK;
-}
-
-// hipEvents around one launch for the measurement aid (when it is on and has room).
-int prof_mark(hipStream_t st, bool& rec) {
-    rec = g_prof.on && g_prof.used < g_prof.cap;
-    return rec && hipEventRecord(g_prof.ev[2 * g_prof.used], st) != hipSuccess ? MR_ERR_DEVICE : MR_OK;
-}
-int prof_close(hipStream_t st, bool rec) {
-    if (!rec) return MR_OK;
-    if (hipEventRecord(g_prof.ev[2 * g_prof.used + 1], st) != hipSuccess) return MR_ERR_DEVICE;
-    ++g_prof.used;
     return MR_OK;
 }
 

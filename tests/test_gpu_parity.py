@@ -220,6 +220,68 @@ def test_nn_mixed_sign_best_scores(dtype):
     log("mixed sign", dtype, rep)
 
 
+@pytest.mark.parametrize("d", [8, 16, 24, 32])
+@pytest.mark.parametrize("sizes", [((37, 29), (41, 23)), ((70, 50), (64, 48)), ((64, 64), (64, 64)),
+                                   ((1, 1), (9, 7)), ((9, 7), (1, 1)), ((96, 96), (50, 61))])
+def test_mutual_fused_bf16_equals_two_searches(d, sizes):
+    """bf16 maps (d <= 32) take the fused row + column pass.  Its two NN maps must equal,
+    element by element, the two separate searches of mr_nn_argmax (the same scores and
+    the same comparison rule), and both must pass the oracle rule.  Sizes cover ragged
+    query and database tiles, a partial second query group (70x50 = 3500 queries), whole
+    tiles, single-pixel maps, and several database segments per query group."""
+    (h1, w1), (h2, w2) = sizes
+    p = workloads.make_pair(h1, w1, d, seed=1000 + d + h1, warp="shift", sigma=0.1, rho=0.2, dtype="bf16")
+    q = workloads.make_pair(h2, w2, d, seed=2000 + d + h2, warp="shift", sigma=0.1, rho=0.2, dtype="bf16")
+    A = dev_map(p.D1, h1, w1, p.D1_bits)
+    B = dev_map(q.D2, h2, w2, q.D2_bits)
+    pairs, n, nn_ab, nn_ba = mr.mutual_nn(A, B)
+    i12 = mr.nn_argmax(A, B)
+    i21 = mr.nn_argmax(B, A)
+    torch.cuda.synchronize()
+    g12, g21 = nn_ab[0].cpu().numpy(), nn_ba[0].cpu().numpy()
+    assert (g12 == i12.cpu().numpy()).all()
+    assert (g21 == i21.cpu().numpy()).all()
+    oi, o1, o2 = oracle.nn(p.D1, q.D2)
+    checks.check_nn(g12, oi, o1, o2, p.D1, np.arange(len(p.D1)), q.D2, "bf16")
+    oj, b1, b2 = oracle.nn(q.D2, p.D1)
+    checks.check_nn(g21, oj, b1, b2, q.D2, np.arange(len(q.D2)), p.D1, "bf16")
+    gp = mr.matches(pairs, n)
+    i = np.nonzero(g21[g12] == np.arange(len(g12)))[0]
+    assert gp.tolist() == np.stack([i, g12[i]], 1).tolist()
+
+
+def test_mutual_fused_bf16_batch_and_negative_scores():
+    """The fused pass with a batch of three pairs (each against its own maps), and with
+    every similarity negative (maxima below zero go through the same comparison)."""
+    Bn, H, W, d = 3, 23, 19, 24
+    ps = [workloads.make_pair(H, W, d, seed=1300 + b, warp="shift", sigma=0.1, rho=0.2, dtype="bf16")
+          for b in range(Bn)]
+    A = torch.stack([dev_map(p.D1, H, W, p.D1_bits) for p in ps])
+    Bm = torch.stack([dev_map(p.D2, H, W, p.D2_bits) for p in ps])
+    pairs, n, nn_ab, nn_ba = mr.mutual_nn(A, Bm)
+    torch.cuda.synchronize()
+    for b, p in enumerate(ps):
+        o_pairs, o12, a1, a2, o21, c1, c2 = oracle.mutual_nn(p.D1, p.D2)
+        checks.check_nn(nn_ab[b].cpu().numpy(), o12, a1, a2, p.D1, np.arange(p.N), p.D2, "bf16")
+        checks.check_nn(nn_ba[b].cpu().numpy(), o21, c1, c2, p.D2, np.arange(p.N), p.D1, "bf16")
+    rng = np.random.default_rng(6)
+    e = np.zeros(d)
+    e[0] = 1.0
+
+    def unit(x):
+        return (x / np.linalg.norm(x, axis=1, keepdims=True)).astype(np.float32)
+
+    Ab = workloads.f32_to_bf16_bits(unit(0.9 * e + 0.25 * rng.standard_normal((37 * 29, d)) / np.sqrt(d)))
+    Bb = workloads.f32_to_bf16_bits(unit(-0.9 * e + 0.25 * rng.standard_normal((41 * 23, d)) / np.sqrt(d)))
+    Af, Bf = workloads.bf16_bits_to_f32(Ab), workloads.bf16_bits_to_f32(Bb)
+    pairs, n, nn_ab, nn_ba = mr.mutual_nn(dev_map(Af, 37, 29, Ab), dev_map(Bf, 41, 23, Bb))
+    torch.cuda.synchronize()
+    o_pairs, o12, a1, a2, o21, c1, c2 = oracle.mutual_nn(Af, Bf)
+    assert a1.max() < 0 and c1.max() < 0
+    checks.check_nn(nn_ab[0].cpu().numpy(), o12, a1, a2, Af, np.arange(len(Af)), Bf, "bf16")
+    checks.check_nn(nn_ba[0].cpu().numpy(), o21, c1, c2, Bf, np.arange(len(Bf)), Af, "bf16")
+
+
 def test_mutual_c2_bf16_full_size_sampled():
     """512x384 bf16 pair, full 196608^2 brute force; the oracle checks 4096 random rows and
     4096 random columns (and the reciprocity of the sampled rows)."""
@@ -242,6 +304,11 @@ def test_mutual_c2_bf16_full_size_sampled():
     # the pair list is the reciprocal subset of the GPU's own maps, over all pixels
     i = np.nonzero(g21[g12] == np.arange(p.N))[0]
     assert (gp[:, 0] == i).all() and (gp[:, 1] == g12[i]).all()
+    # the fused pass equals the two separate searches everywhere
+    s12 = mr.nn_argmax(A, B)
+    s21 = mr.nn_argmax(B, A)
+    torch.cuda.synchronize()
+    assert (g12 == s12.cpu().numpy()).all() and (g21 == s21.cpu().numpy()).all()
     log("c2", r1, r2, "pairs", len(gp))
 
 
