@@ -314,10 +314,6 @@ struct NNArgs {
     int32_t host_count;        // query count when dev_count is NULL
     uint64_t* keys;            // [batch][keys_stride] results, merged with atomicMax
     int64_t keys_stride;
-    int32_t* active_out;       // optional: record the query count here (per pair)
-    int64_t active_stride;
-    int32_t* zero_count;       // optional: set this per-pair counter to 0
-    int64_t zero_stride;
     int32_t q_role, db_role;   // 1 = image 1, 2 = image 2 (fixes the split product order)
     // pair graph: the query (database) map of pair b is map q_img[2b] (db_img[2b]) of
     // qmap (dbmap); NULL: map b
@@ -578,6 +574,16 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
     auto fetch = [&](int t, u32x4 (&stage)[MAXC]) {
         const int64_t tb = (int64_t)t * tile_bytes;
         const int64_t limit = (int64_t)ndb * rb;   // bytes of real rows
+        if ((t + 1) * 32 <= ndb) {
+            // a whole tile: every chunk is in bounds (wave-uniform base, per-lane offset)
+            const char* base = dbytes + tb;
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c) {
+                const int ch = threadIdx.x + c * kThreads;
+                stage[c] = ch < nchunk ? *reinterpret_cast<const u32x4*>(base + ch * 16) : u32x4{0u, 0u, 0u, 0u};
+            }
+            return;
+        }
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
             const int ch = threadIdx.x + c * kThreads;
@@ -643,14 +649,18 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
         r.load(lds + (i & 1) * BUF, jl, true, h, d, role);
         if constexpr (AR == AR_X3 && Ep::kind == EP_KEY) {
             if (nact == QT && !ragged) {
+                // the last query tile's chain accumulates straight into the pending
+                // unit (whose previous value the first epilogue has consumed)
+                f32x16 acc[QT > 1 ? QT - 1 : 1];
 #pragma unroll
                 for (int j = 0; j < QT; ++j) {
-                    f32x16 acc = {};
+                    f32x16 x = {};
 #pragma unroll
-                    for (int st = 0; st < P; ++st) acc = r.step(st, q[j], acc);
-                    if (j > 0) ep.template tile<false>(lag, t, h, ndb, j - 1);
+                    for (int st = 0; st < P; ++st) x = r.step(st, q[j], x);
+                    if (j > 0) ep.template tile<false>(acc[j - 1], t, h, ndb, j - 1);
                     else ep.template tile<false>(lag, lag_t, h, ndb, QT - 1);
-                    lag = acc;
+                    if (j < QT - 1) acc[j] = x;
+                    else lag = x;
                     interleave_mfma_valu<P, (Ep::valu + P - 1) / P>();
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -925,10 +935,6 @@ void nn_argmax_kernel(NNArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, so branches on it stay scalar
     const int pair = blockIdx.y;
     const int n = a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count;
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        if (a.active_out) a.active_out[pair * a.active_stride] = n;
-        if (a.zero_count) a.zero_count[pair * a.zero_stride] = 0;
-    }
     const int ntiles = (a.ndb + 31) >> 5;
     const int nqt = (n + 31) >> 5;                        // query tiles
     const int qgroups = (nqt + kWaves * QT - 1) / (kWaves * QT);
@@ -1566,10 +1572,6 @@ __global__ __launch_bounds__(kThreads) void point_nn_kernel(NNArgs a) {
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int pair = blockIdx.y;
     const int n = a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count;
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        if (a.active_out) a.active_out[pair * a.active_stride] = n;
-        if (a.zero_count) a.zero_count[pair * a.zero_stride] = 0;
-    }
     const int ndb = a.ndb;
     if (n <= 0 || ndb <= 0) return;
     const int nqb = (n + QW - 1) / QW;
@@ -1713,16 +1715,25 @@ __global__ void fast_init_kernel(InitArgs a) {
 // One reciprocity check per live pixel u: v = NN(a[u], b), u' = NN(b[v], a).
 // u' == u: keep (u, v).  Otherwise u' becomes live next iteration if nobody has
 // been there (state -1); ballot + prefix sum give each wave one atomic.
+// The frontier counts rotate through three per-pair counters: iteration t reads
+// cnt (its own count), adds the next frontier into cnt_next (cleared by iteration
+// t - 1) and clears cnt_after for iteration t + 1; it also records its count in
+// active[t].  The search kernels then only read their count.
 struct CycleArgs {
     const int32_t* front; const uint64_t* keys_f; const uint64_t* keys_b;
     uint64_t* keys_f_next; uint64_t* keys_b_next; int32_t* front_next;
-    const int32_t* cnt; int32_t* cnt_next; int32_t* state;
+    const int32_t* cnt; int32_t* cnt_next; int32_t* cnt_after; int32_t* state;
+    int32_t* active; int64_t active_stride;   // NULL, or this iteration's entry of [batch][max_iters]
     int64_t slot_stride; int64_t n1; int32_t last;
 };
 
 __global__ __launch_bounds__(256) void fast_cycle_kernel(CycleArgs a) {
     const int pair = blockIdx.y;
     const int n = a.cnt[pair];
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.cnt_after[pair] = 0;
+        if (a.active) a.active[pair * a.active_stride] = n;
+    }
     const int lane = threadIdx.x & 63;
     for (int k0 = blockIdx.x * blockDim.x; k0 < n; k0 += gridDim.x * blockDim.x) {
         const int k = k0 + threadIdx.x;
@@ -2516,7 +2527,7 @@ NNArgs nn_args(const mr_map* q, const void* qdata, int q_role, const mr_map* db,
 }
 
 struct FastLayout {
-    size_t keys_f[2], keys_b[2], front[2], cnt[2], state, blk, total;
+    size_t keys_f[2], keys_b[2], front[2], cnt[3], state, blk, total;
 };
 
 FastLayout fast_layout(const mr_map* a, const mr_map* b, int64_t nseeds) {
@@ -2528,7 +2539,7 @@ FastLayout fast_layout(const mr_map* a, const mr_map* b, int64_t nseeds) {
     for (int i = 0; i < 2; ++i) { L.keys_f[i] = off; off = align256(off + slots * 8); }
     for (int i = 0; i < 2; ++i) { L.keys_b[i] = off; off = align256(off + slots * 8); }
     for (int i = 0; i < 2; ++i) { L.front[i] = off; off = align256(off + slots * 4); }
-    for (int i = 0; i < 2; ++i) { L.cnt[i] = off; off = align256(off + (size_t)batch * 4); }
+    for (int i = 0; i < 3; ++i) { L.cnt[i] = off; off = align256(off + (size_t)batch * 4); }
     L.state = off; off = align256(off + (size_t)batch * (size_t)(n1 > 0 ? n1 : 1) * 4);
     L.blk = off; off = align256(off + (size_t)batch * (size_t)(nblk_of(n1) > 0 ? nblk_of(n1) : 1) * 4);
     L.total = off;
@@ -2746,7 +2757,7 @@ int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, 
     uint64_t* kf[2] = {at<uint64_t>(ws, L.keys_f[0]), at<uint64_t>(ws, L.keys_f[1])};
     uint64_t* kb[2] = {at<uint64_t>(ws, L.keys_b[0]), at<uint64_t>(ws, L.keys_b[1])};
     int32_t* fr[2] = {at<int32_t>(ws, L.front[0]), at<int32_t>(ws, L.front[1])};
-    int32_t* cnt[2] = {at<int32_t>(ws, L.cnt[0]), at<int32_t>(ws, L.cnt[1])};
+    int32_t* cnt[3] = {at<int32_t>(ws, L.cnt[0]), at<int32_t>(ws, L.cnt[1]), at<int32_t>(ws, L.cnt[2])};
     int32_t* state = at<int32_t>(ws, L.state);
     int32_t* blk = at<int32_t>(ws, L.blk);
 
@@ -2768,21 +2779,21 @@ int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, 
             NNArgs f = nn_args(a, ad, 1, b, bd, 2);
             if (edges) { f.q_img = edges; f.db_img = edges + 1; }
             f.qsrc = Q_LIST; f.qlist = fr[c]; f.qlist_stride = slot;
-            f.dev_count = cnt[c]; f.count_stride = 1;
+            f.dev_count = cnt[t % 3]; f.count_stride = 1;
             f.keys = kf[c]; f.keys_stride = slot;
-            if (iter_active) { f.active_out = iter_active + t; f.active_stride = max_iters; }
-            f.zero_count = cnt[x]; f.zero_stride = 1;
             if ((rc = launch_search(f, metric, ar, batch, st))) return rc;
             NNArgs r = nn_args(b, bd, 2, a, ad, 1);
             if (edges) { r.q_img = edges + 1; r.db_img = edges; }
             r.qsrc = Q_KEYS; r.qlist = kf[c]; r.qlist_stride = slot;
-            r.dev_count = cnt[c]; r.count_stride = 1;
+            r.dev_count = cnt[t % 3]; r.count_stride = 1;
             r.keys = kb[c]; r.keys_stride = slot;
             if ((rc = launch_search(r, metric, ar, batch, st))) return rc;
             CycleArgs ca;
             ca.front = fr[c]; ca.keys_f = kf[c]; ca.keys_b = kb[c];
             ca.keys_f_next = kf[x]; ca.keys_b_next = kb[x]; ca.front_next = fr[x];
-            ca.cnt = cnt[c]; ca.cnt_next = cnt[x]; ca.state = state;
+            ca.cnt = cnt[t % 3]; ca.cnt_next = cnt[(t + 1) % 3]; ca.cnt_after = cnt[(t + 2) % 3];
+            ca.state = state;
+            ca.active = iter_active ? iter_active + t : nullptr; ca.active_stride = max_iters;
             ca.slot_stride = slot; ca.n1 = n1; ca.last = (t == max_iters - 1);
             hipLaunchKernelGGL(fast_cycle_kernel, dim3(cyc_grid, batch), dim3(256), 0, st, ca);
             if (dev_err()) return MR_ERR_DEVICE;
