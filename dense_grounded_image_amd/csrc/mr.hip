@@ -319,6 +319,11 @@ struct NNArgs {
     // qmap (dbmap); NULL: map b
     const int32_t* q_img;
     const int32_t* db_img;
+    // 0: grid (workgroups per pair, batch).  Otherwise a one-dimensional grid in which
+    // all xcd_gx workgroups of a pair share one XCD (see xcd_packed_grid); batch is the
+    // pair count.
+    int32_t xcd_gx;
+    int32_t batch;
 };
 
 // Map index of pair b in a stacked collection (a pair graph's edge table, or b itself).
@@ -933,13 +938,24 @@ void nn_argmax_kernel(NNArgs a) {
     const int h = lane >> 5;
     const int jl = lane & 31;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, so branches on it stay scalar
-    const int pair = blockIdx.y;
+    int pair, bx, gx;   // pair, workgroup within the pair, workgroups per pair
+    if (a.xcd_gx) {
+        const int k = (int)blockIdx.x >> 3;
+        gx = a.xcd_gx;
+        bx = k % gx;
+        pair = (int)(blockIdx.x & 7) + 8 * (k / gx);
+        if (pair >= a.batch) return;
+    } else {
+        pair = blockIdx.y;
+        bx = blockIdx.x;
+        gx = gridDim.x;
+    }
     const int n = a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count;
     const int ntiles = (a.ndb + 31) >> 5;
     const int nqt = (n + 31) >> 5;                        // query tiles
     const int qgroups = (nqt + kWaves * QT - 1) / (kWaves * QT);
     if (qgroups == 0 || ntiles == 0) return;
-    int nsg = (int)gridDim.x / qgroups;
+    int nsg = gx / qgroups;
     const int sg_cap = ntiles < kMaxSegGroups ? ntiles : kMaxSegGroups;
     nsg = nsg < 1 ? 1 : (nsg > sg_cap ? sg_cap : nsg);
     if (nsg >= 8) nsg &= ~7;
@@ -991,10 +1007,10 @@ void nn_argmax_kernel(NNArgs a) {
         // database four ways; query blocks are taken one after another
         const int cap = (ntiles + kWaves - 1) / kWaves < kMaxSegGroups ? (ntiles + kWaves - 1) / kWaves
                                                                        : kMaxSegGroups;
-        const int ngroups = (int)gridDim.x < cap ? (int)gridDim.x : cap;
+        const int ngroups = gx < cap ? gx : cap;
         const int nqb = (n + QB - 1) / QB;
         uint64_t* red = reinterpret_cast<uint64_t*>(lds);
-        for (int item = blockIdx.x; item < ngroups * nqb; item += gridDim.x) {
+        for (int item = bx; item < ngroups * nqb; item += gx) {
             const int qb = item / ngroups, grp = item - qb * ngroups;
             const int q0 = qb * QB;
             const int left = n - q0;
@@ -1046,7 +1062,7 @@ void nn_argmax_kernel(NNArgs a) {
         return;
     }
 
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    for (int item = bx; item < items; item += gx) {
         const int qg = item / nsg;
         const int sg = item - qg * nsg;
         // the query tiles are spread evenly over the groups; a group's tiles are dealt
@@ -2409,9 +2425,30 @@ int nn_grid_x(int batch) {
     return grid_per_pair(resident_blocks<nn_argmax_kernel<AR, P>>(), batch);
 }
 
+// Workgroups are dealt to the eight XCDs round-robin by linear workgroup id, and each
+// XCD has its own L2.  When a batch gives each pair only a few workgroups, a
+// two-dimensional grid puts a pair's workgroups (its query groups) on different XCDs,
+// and every XCD streams every pair's database map from memory.  For batches of a
+// multiple of 8 pairs with 2..63 workgroups each, the grid is one-dimensional
+// instead: linear id L runs pair (L mod 8) + 8 * ((L / 8) / gx), workgroup
+// (L / 8) mod gx, so all of a pair's workgroups share the XCD L mod 8 and read its
+// map through one L2.  Larger per-pair grids already keep one eighth of each map per
+// XCD (segment counts are multiples of 8).
+inline int xcd_packed_grid(int gx, int batch) {
+    return (batch % 8 == 0 && gx > 1 && gx < 64) ? gx : 0;
+}
+
 template <int AR, int P>
 void launch_nn_t(const NNArgs& a, int batch, hipStream_t st) {
-    hipLaunchKernelGGL((nn_argmax_kernel<AR, P>), dim3(nn_grid_x<AR, P>(batch), batch), dim3(kThreads), 0, st, a);
+    const int gx = nn_grid_x<AR, P>(batch);
+    if (const int packed = xcd_packed_grid(gx, batch)) {
+        NNArgs b = a;
+        b.xcd_gx = packed;
+        b.batch = batch;
+        hipLaunchKernelGGL((nn_argmax_kernel<AR, P>), dim3(packed * batch), dim3(kThreads), 0, st, b);
+    } else {
+        hipLaunchKernelGGL((nn_argmax_kernel<AR, P>), dim3(gx, batch), dim3(kThreads), 0, st, a);
+    }
 }
 
 // Arithmetic for a map dtype and descriptor length (see the Arith enum).
