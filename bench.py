@@ -355,13 +355,15 @@ def other_bruteforce(args, torch, dev):
     p2 = workloads.config_pair(2)
     A2, B2 = dev_maps(p2, torch, dev)
     ws = torch.empty(mr.workspace_bytes(mr.MR_OP_MUTUAL_NN, A2, B2), dtype=torch.uint8, device=dev)
-    steps = max(3, args.steps // 4)
-    ms, kms, kn = time_steps(lambda: mr.mutual_nn(A2, B2, ws=ws), steps, 2, torch, 2 * steps)
+    # about 3 ms per call: at least 10 timed calls after 3 warm-up calls, so that the
+    # clock ramp of the first calls does not weigh on the mean
+    steps = max(10, args.steps // 2)
+    ms, kms, kn = time_steps(lambda: mr.mutual_nn(A2, B2, ws=ws), steps, 3, torch, 2 * steps)
     fl = 2.0 * p2.N * p2.N * p2.d   # the method's work: the similarity matrix once
     # the two-pass alternative: a row search in each direction (the maps' roles swapped),
     # i.e. the matrix computed twice; the mutual call above computes it once
     wn = torch.empty(mr.workspace_bytes(mr.MR_OP_NN_ARGMAX, A2, B2, p2.N), dtype=torch.uint8, device=dev)
-    ms2, _, _ = time_steps(lambda: (mr.nn_argmax(A2, B2, ws=wn), mr.nn_argmax(B2, A2, ws=wn)), steps, 2, torch)
+    ms2, _, _ = time_steps(lambda: (mr.nn_argmax(A2, B2, ws=wn), mr.nn_argmax(B2, A2, ws=wn)), steps, 3, torch)
     out = {"pairs_per_s": round(1000.0 / ms, 2), "ms_per_call": round(ms, 3),
            "variant": "fused row + column pass (rowcol_argmax_kernel), then both recoveries",
            "two_pass_ms": round(ms2, 3),

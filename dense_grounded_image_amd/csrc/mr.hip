@@ -1203,8 +1203,9 @@ __global__ __launch_bounds__(kThreads) void recover_rows_kernel(NNArgs a) {
 //    through LDS and a 16-value maximum per row (one lane pair per row of the tile),
 //    then a maximum over the workgroup's waves and one atomicMax per b row and
 //    workgroup on (score, ~query block) keys, a query block being the 256
-//    consecutive query pixels of one wave.  recover_cols_kernel resolves each
-//    winning block to the lowest query row of the winning score.
+//    consecutive query pixels of one wave.  The column recovery (rows bucketed by
+//    winning block, recover_cols_gathered_kernel) resolves each winning block to the
+//    lowest query row of the winning score.
 // Both directions compare scores after clearing their 4 low bits, lowest index on
 // ties, exactly like nn_argmax_kernel, so the results equal two separate searches.
 // The b tiles of a workgroup's segment pass through a two-group LDS ring, copied
@@ -1446,14 +1447,128 @@ __global__ __launch_bounds__(kRcThreads) void rowcol_argmax_kernel(RowColArgs a)
     }
 }
 
-// (score, ~query block) -> (score, ~row) for the columns: one b tile per wave.  For
-// each distinct winning block among the tile's 32 rows (a wave-uniform loop), the
-// wave multiplies the b tile (A operand, loaded as the fused pass loaded it) with the
-// block's query tiles (B operands) -- the same instruction, operand layout and step
-// order, so the scores are bitwise those that were compared -- and every row won by
-// that block takes the lowest query whose compared score equals its key's score.
+// Column recovery by query block.  The b rows a block won are gathered into one list
+// per block (count, prefix, scatter), then one workgroup per block loads the block's
+// query tiles once and compares them with every gathered row: each gathered 32-row
+// tile is the A operand of the same instruction, with the same operand layout and
+// step order as the fused pass (an output element depends only on its row and column
+// operands, not on the row's place in the tile), so the scores are bitwise those that
+// were compared.  Each row takes the lowest query of the block whose compared score
+// equals its key's.
+struct ColBuckets {
+    int32_t* cnt;     // [batch][nblocks] rows won per query block
+    int32_t* pos;     // [batch][nblocks] prefix sums, then (after the scatter) end offsets
+    int32_t* list;    // [batch][nb] row ids grouped by block
+    int32_t nblocks;
+};
+
+// Counting and scattering run per chunk of kBucketChunk rows (one workgroup of 256
+// threads, kBucketChunk / 256 rows per thread).  With at most kBucketBins blocks the
+// chunk's histogram is kept in LDS and the workgroup leaves one global atomic per
+// non-empty block (same-address global atomics serialise); otherwise every row adds
+// to the global count itself.
+constexpr int kBucketChunk = 2048;
+constexpr int kBucketBins = 8192;
+
+__global__ __launch_bounds__(256) void col_bucket_count_kernel(RowColArgs a, ColBuckets c) {
+    __shared__ int32_t hist[kBucketBins];
+    const int pair = blockIdx.y;
+    const uint64_t* keys = a.keys_ba + (int64_t)pair * a.nb;
+    int32_t* cnt = c.cnt + (int64_t)pair * c.nblocks;
+    const bool local = c.nblocks <= kBucketBins;
+    if (local) {
+        for (int i = threadIdx.x; i < c.nblocks; i += 256) hist[i] = 0;
+        __syncthreads();
+    }
+    const int64_t r0 = (int64_t)blockIdx.x * kBucketChunk;
+#pragma unroll
+    for (int e = 0; e < kBucketChunk / 256; ++e) {
+        const int64_t i = r0 + e * 256 + threadIdx.x;
+        const uint64_t k = i < a.nb ? keys[i] : 0;
+        const uint32_t b = ~(uint32_t)k;
+        if (k && b < (uint32_t)c.nblocks) {
+            if (local) atomicAdd(&hist[b], 1);
+            else atomicAdd(&cnt[b], 1);
+        }
+    }
+    if (local) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < c.nblocks; i += 256)
+            if (hist[i]) atomicAdd(&cnt[i], hist[i]);
+    }
+}
+
+// exclusive prefix of the counts, one workgroup of 1024 threads per pair, 1024 counts
+// per step
+__global__ __launch_bounds__(1024) void col_bucket_scan_kernel(ColBuckets c) {
+    __shared__ int32_t part[1024 / 64];
+    const int pair = blockIdx.x;
+    const int32_t* cnt = c.cnt + (int64_t)pair * c.nblocks;
+    int32_t* pos = c.pos + (int64_t)pair * c.nblocks;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    int32_t carry = 0;
+    for (int base = 0; base < c.nblocks; base += 1024) {
+        const int i = base + (int)threadIdx.x;
+        const int32_t v = i < c.nblocks ? cnt[i] : 0;
+        int32_t x = v;   // inclusive scan within the wave
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            const int32_t o = __shfl_up(x, m);
+            if (lane >= m) x += o;
+        }
+        if (lane == 63) part[wv] = x;
+        __syncthreads();
+        int32_t before = carry;
+        for (int w = 0; w < wv; ++w) before += part[w];
+        int32_t total = 0;
+        for (int w = 0; w < 1024 / 64; ++w) total += part[w];
+        if (i < c.nblocks) pos[i] = before + x - v;
+        carry += total;
+        __syncthreads();
+    }
+}
+
+// rows -> their block's list; with the LDS histogram a row's place is its block's base
+// for this chunk (one global atomic per non-empty block) plus its rank in the chunk
+__global__ __launch_bounds__(256) void col_bucket_scatter_kernel(RowColArgs a, ColBuckets c) {
+    __shared__ int32_t hist[kBucketBins];
+    const int pair = blockIdx.y;
+    const uint64_t* keys = a.keys_ba + (int64_t)pair * a.nb;
+    int32_t* pos = c.pos + (int64_t)pair * c.nblocks;
+    int32_t* list = c.list + (int64_t)pair * a.nb;
+    const int64_t r0 = (int64_t)blockIdx.x * kBucketChunk;
+    if (c.nblocks > kBucketBins) {
+#pragma unroll
+        for (int e = 0; e < kBucketChunk / 256; ++e) {
+            const int64_t i = r0 + e * 256 + threadIdx.x;
+            const uint64_t k = i < a.nb ? keys[i] : 0;
+            const uint32_t b = ~(uint32_t)k;
+            if (k && b < (uint32_t)c.nblocks) list[atomicAdd(&pos[b], 1)] = (int32_t)i;
+        }
+        return;
+    }
+    for (int i = threadIdx.x; i < c.nblocks; i += 256) hist[i] = 0;
+    __syncthreads();
+    int bk[kBucketChunk / 256], rk[kBucketChunk / 256];
+#pragma unroll
+    for (int e = 0; e < kBucketChunk / 256; ++e) {
+        const int64_t i = r0 + e * 256 + threadIdx.x;
+        const uint64_t k = i < a.nb ? keys[i] : 0;
+        const uint32_t b = ~(uint32_t)k;
+        bk[e] = (k && b < (uint32_t)c.nblocks) ? (int)b : -1;
+        rk[e] = bk[e] >= 0 ? atomicAdd(&hist[bk[e]], 1) : 0;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < c.nblocks; i += 256)
+        if (hist[i]) hist[i] = atomicAdd(&pos[i], hist[i]);   // this chunk's base in block i's list
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kBucketChunk / 256; ++e)
+        if (bk[e] >= 0) list[hist[bk[e]] + rk[e]] = (int32_t)(r0 + e * 256 + threadIdx.x);
+}
+
 template <int P>
-__global__ __launch_bounds__(kThreads) void recover_cols_kernel(RowColArgs a) {
+__global__ __launch_bounds__(kThreads) void recover_cols_gathered_kernel(RowColArgs a, ColBuckets c) {
     using Op = Operand<AR_BF16, P>;
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5;
@@ -1462,84 +1577,64 @@ __global__ __launch_bounds__(kThreads) void recover_cols_kernel(RowColArgs a) {
     const int pair = blockIdx.y;
     const int na = a.na, nb = a.nb, d = a.d;
     const int nqt = (na + 31) >> 5;
-    const int nblocks = (nqt + kRcQT - 1) / kRcQT;
-    const int ntiles = (nb + 31) >> 5;
     const void* abase = static_cast<const uint16_t*>(a.amap) + pair * a.a_pair_elems;
     const void* bbase = static_cast<const uint16_t*>(a.bmap) + pair * a.b_pair_elems;
     uint64_t* keys_ba = a.keys_ba + (int64_t)pair * nb;
-    for (int t = blockIdx.x * kWaves + wv; t < ntiles; t += gridDim.x * kWaves) {
-        const int brow = t * 32 + jl;
-        Op r;
-        r.load(bbase, brow < nb ? brow : 0, brow < nb, h, d, 2);
-        // the keys of the 16 rows (h, v) this lane sees (vectors: the compare loop
-        // below indexes them with a wave-uniform v)
-        f32x16 sc;
-        i32x16 blk, found;
+    const int32_t* cnt = c.cnt + (int64_t)pair * c.nblocks;
+    const int32_t* pos = c.pos + (int64_t)pair * c.nblocks;
+    const int32_t* list = c.list + (int64_t)pair * nb;
+    for (int blk = blockIdx.x; blk < c.nblocks; blk += gridDim.x) {
+        const int n = cnt[blk];
+        if (n == 0) continue;
+        const int begin = pos[blk] - n;   // the scatter advanced pos to the block's end
+        const int tq0 = blk * kRcQT;
+        Op qb[kRcQT];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int row = t * 32 + tile_row(v, h);
-            const uint64_t k = row < nb ? keys_ba[row] : 0;
-            sc[v] = from_ordered((uint32_t)(k >> 32));
-            const uint32_t b = ~(uint32_t)k;
-            blk[v] = k && b < (uint32_t)nblocks ? (int)b : -1;
-            found[v] = INT_MAX;
+        for (int j = 0; j < kRcQT; ++j) {
+            const int qp = (tq0 + j) * 32 + jl;
+            qb[j].load(abase, qp < na ? qp : 0, qp < na, h, d, 1);
         }
-        while (true) {
-            // the lowest unresolved block of the tile (wave-uniform)
-            int lo = INT_MAX;
+        for (int g = wv; g * 32 < n; g += kWaves) {
+            // this lane's A row (tile position jl) with its key's score; the scores of
+            // the rows (h, v) whose results the lane sees come from the lanes holding them
+            const int ia = g * 32 + jl;
+            const int arow = ia < n ? list[begin + ia] : -1;
+            Op r;
+            r.load(bbase, arow >= 0 ? arow : 0, arow >= 0, h, d, 2);
+            const float sc_lane = arow >= 0 ? from_ordered((uint32_t)(keys_ba[arow] >> 32)) : 0.0f;
+            f32x16 sc;
+            i32x16 found;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) lo = blk[v] >= 0 && blk[v] < lo ? blk[v] : lo;
-#pragma unroll
-            for (int m = 32; m >= 1; m >>= 1) {
-                const int o = __shfl_xor(lo, m);
-                lo = o < lo ? o : lo;
-            }
-            lo = __builtin_amdgcn_readfirstlane(lo);
-            if (lo == INT_MAX) break;
-            // which v (in either half) this block won: only those are compared
-            uint32_t vm = 0;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) vm |= blk[v] == lo ? (1u << v) : 0u;
-            vm |= (uint32_t)__shfl_xor((int)vm, 32);
-            vm = __builtin_amdgcn_readfirstlane(vm);
-            const int tq0 = lo * kRcQT;
-            // the block's query tiles, all loads issued before the products
-            Op qb[kRcQT];
-#pragma unroll
-            for (int j = 0; j < kRcQT; ++j) {
-                const int qp = (tq0 + j) * 32 + jl;
-                qb[j].load(abase, qp < na ? qp : 0, qp < na, h, d, 1);
+            for (int v = 0; v < 16; ++v) {
+                sc[v] = __shfl(sc_lane, tile_row(v, h));
+                found[v] = g * 32 + tile_row(v, h) < n ? INT_MAX : INT_MIN;   // INT_MIN: no row there
             }
 #pragma unroll
             for (int j = 0; j < kRcQT; ++j) {
                 if (tq0 + j >= nqt) break;
                 const int qp = (tq0 + j) * 32 + jl;
                 const f32x16 x = r.mfma(qb[j], f32x16{});
-                for (uint32_t m = vm; m; m &= m - 1) {
-                    const int v = __builtin_ctz(m);
-                    if (blk[v] == lo && qp < na && trunc4(x[v]) == sc[v] && qp < found[v]) found[v] = qp;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (qp < na && trunc4(x[v]) == sc[v] && qp < found[v]) found[v] = qp;
+            }
+            // lowest query over the 32 lanes of each half; lane (h, jl < 16) writes the
+            // gathered row at (h, v = jl)
+            int mine = INT_MAX;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                int f = found[v];
+#pragma unroll
+                for (int m = 16; m >= 1; m >>= 1) {
+                    const int o = __shfl_xor(f, m);
+                    f = o < f ? o : f;
                 }
+                if (jl == v) mine = f;
             }
-#pragma unroll
-            for (int v = 0; v < 16; ++v) blk[v] = blk[v] == lo ? -2 : blk[v];
-        }
-        // lowest query over the 32 lanes of each half, then lane (h, jl < 16) writes row (h, v = jl)
-        int mine = INT_MAX;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            int f = found[v];
-#pragma unroll
-            for (int m = 16; m >= 1; m >>= 1) {
-                const int o = __shfl_xor(f, m);
-                f = o < f ? o : f;
-            }
-            if (jl == v) mine = f;
-        }
-        if (jl < 16) {
-            const int row = t * 32 + tile_row(jl, h);
-            if (row < nb) {
-                const uint64_t k = keys_ba[row];
-                keys_ba[row] = (k != 0 && mine != INT_MAX) ? pack_key(from_ordered((uint32_t)(k >> 32)), (uint32_t)mine) : 0;
+            const int myrow = __shfl(arow, tile_row(jl & 15, h));
+            if (jl < 16 && myrow >= 0) {
+                const uint64_t k = keys_ba[myrow];
+                keys_ba[myrow] = mine != INT_MAX ? pack_key(from_ordered((uint32_t)(k >> 32)), (uint32_t)mine) : 0;
             }
         }
     }
@@ -2583,16 +2678,24 @@ FastLayout fast_layout(const mr_map* a, const mr_map* b, int64_t nseeds) {
     return L;
 }
 
-struct MutualLayout { size_t keys_ab, keys_ba, blk, total; };
+// Query blocks of the fused pass (kRcQT query tiles each) for a map of n pixels.
+inline int64_t rc_blocks(int64_t n) { return ((n + 31) / 32 + kRcQT - 1) / kRcQT; }
+
+struct MutualLayout { size_t keys_ab, keys_ba, blk, bcnt, bpos, blist, total; };
 
 MutualLayout mutual_layout(const mr_map* a, const mr_map* b) {
     MutualLayout L;
-    const int batch = a->batch;
+    const size_t batch = (size_t)a->batch;
     const int64_t na = npix(a), nb = npix(b);
+    const size_t nbk = (size_t)(rc_blocks(na) > 0 ? rc_blocks(na) : 1);
     size_t off = 0;
-    L.keys_ab = off; off = align256(off + (size_t)batch * (size_t)(na > 0 ? na : 1) * 8);
-    L.keys_ba = off; off = align256(off + (size_t)batch * (size_t)(nb > 0 ? nb : 1) * 8);
-    L.blk = off; off = align256(off + (size_t)batch * (size_t)(nblk_of(na) > 0 ? nblk_of(na) : 1) * 4);
+    L.keys_ab = off; off = align256(off + batch * (size_t)(na > 0 ? na : 1) * 8);
+    L.keys_ba = off; off = align256(off + batch * (size_t)(nb > 0 ? nb : 1) * 8);
+    L.blk = off; off = align256(off + batch * (size_t)(nblk_of(na) > 0 ? nblk_of(na) : 1) * 4);
+    // column recovery of the fused pass: rows won per query block, their offsets, the rows
+    L.bcnt = off; off = align256(off + batch * nbk * 4);
+    L.bpos = off; off = align256(off + batch * nbk * 4);
+    L.blist = off; off = align256(off + batch * (size_t)(nb > 0 ? nb : 1) * 4);
     L.total = off;
     return L;
 }
@@ -2668,7 +2771,7 @@ int nn_impl(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q
 // two recoveries (tile -> row for the rows, query block -> row for the columns).  The
 // keys are zero on entry.
 template <int P>
-int launch_rowcol_t(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* kba, hipStream_t st) {
+int launch_rowcol_t(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* kba, ColBuckets cb, hipStream_t st) {
     const int batch = a->batch;
     const int64_t na = npix(a), nb = npix(b);
     if (na == 0 || nb == 0) return MR_OK;
@@ -2709,15 +2812,22 @@ int launch_rowcol_t(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* k
     f.keys_stride = na;
     const int rgx = (int)((na + 31) / 32 < (1 << 20) ? (na + 31) / 32 : (1 << 20));
     hipLaunchKernelGGL((recover_rows_kernel<AR_BF16, P>), dim3(rgx, batch), dim3(kThreads), 0, st, f);
-    const int cgx = (int)((ntiles + kWaves - 1) / kWaves < (1 << 20) ? (ntiles + kWaves - 1) / kWaves : (1 << 20));
-    hipLaunchKernelGGL((recover_cols_kernel<P>), dim3(cgx, batch), dim3(kThreads), 0, st, x);
+    // columns: rows bucketed by winning query block, then one workgroup per block
+    const int64_t nbk = cb.nblocks;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_1d(batch * nbk)), dim3(256), 0, st, cb.cnt, batch * nbk, 0);
+    const int chunks = (int)((nb + kBucketChunk - 1) / kBucketChunk);
+    hipLaunchKernelGGL(col_bucket_count_kernel, dim3(chunks, batch), dim3(256), 0, st, x, cb);
+    hipLaunchKernelGGL(col_bucket_scan_kernel, dim3(batch), dim3(1024), 0, st, cb);
+    hipLaunchKernelGGL(col_bucket_scatter_kernel, dim3(chunks, batch), dim3(256), 0, st, x, cb);
+    const int cgx = (int)(nbk < 65536 ? nbk : 65536);
+    hipLaunchKernelGGL((recover_cols_gathered_kernel<P>), dim3(cgx, batch), dim3(kThreads), 0, st, x, cb);
     return dev_err();
 }
 
-int launch_rowcol(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* kba, hipStream_t st) {
+int launch_rowcol(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* kba, ColBuckets cb, hipStream_t st) {
     switch ((a->d + 15) / 16) {
-        case 1: return launch_rowcol_t<1>(a, b, kab, kba, st);
-        case 2: return launch_rowcol_t<2>(a, b, kab, kba, st);
+        case 1: return launch_rowcol_t<1>(a, b, kab, kba, cb, st);
+        case 2: return launch_rowcol_t<2>(a, b, kab, kba, cb, st);
         default: return MR_ERR_SHAPE;
     }
 }
@@ -2744,7 +2854,12 @@ int mutual_impl(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba
     const void *ad = a->data, *bd = b->data;
     if (metric == M_INNER && ar == AR_BF16 && a->d <= 32) {
         // both directions from one pass over the similarity tiles
-        if ((rc = launch_rowcol(a, b, kab, kba, st))) return rc;
+        ColBuckets cb;
+        cb.cnt = at<int32_t>(ws, L.bcnt);
+        cb.pos = at<int32_t>(ws, L.bpos);
+        cb.list = at<int32_t>(ws, L.blist);
+        cb.nblocks = (int32_t)rc_blocks(na);
+        if ((rc = launch_rowcol(a, b, kab, kba, cb, st))) return rc;
     } else {
         NNArgs f = nn_args(a, ad, 1, b, bd, 2);
         f.qsrc = Q_ALL;
