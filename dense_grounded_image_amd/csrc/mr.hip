@@ -459,6 +459,47 @@ template <int QT> struct TileBest {
     }
 };
 
+// Group-level maximum (the rows of the fused row + column pass): per lane and query
+// tile, the raw maximum over the current group of b tiles (one max3 tree per tile,
+// nothing else), and at the end of each group (close) the best compared score and the
+// first group reaching it, named by the caller's group index.  trunc4 is monotone, so the
+// group's compared maximum is trunc4 of its raw maximum, and the lane's NN is the
+// lowest row of that group whose compared score equals the best (found later by
+// recomputing the group).
+template <int QT> struct GroupBest {
+    float gm[QT], bv[QT];
+    int bt[QT];
+    __device__ __forceinline__ GroupBest() {
+#pragma unroll
+        for (int j = 0; j < QT; ++j) { gm[j] = -INFINITY; bv[j] = -INFINITY; bt[j] = -1; }
+    }
+    template <bool RAGGED>
+    __device__ __forceinline__ void tile(const f32x16& acc, int t, int h, int ndb, int j) {
+        float k[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) k[v] = (RAGGED && t * 32 + tile_row(v, h) >= ndb) ? -INFINITY : acc[v];
+        auto mx3 = [](float a, float b, float c) {
+            return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+        };
+        const float m0 = mx3(k[0], k[1], k[2]), m1 = mx3(k[3], k[4], k[5]), m2 = mx3(k[6], k[7], k[8]);
+        const float m3 = mx3(k[9], k[10], k[11]), m4 = mx3(k[12], k[13], k[14]), m5 = mx3(k[15], gm[j], m0);
+        gm[j] = mx3(mx3(m1, m2, m3), m4, m5);
+    }
+    __device__ __forceinline__ void step(const f32x16& acc, int t, int h, int ndb, int j, bool ragged) {
+        if (ragged) tile<true>(acc, t, h, ndb, j);
+        else tile<false>(acc, t, h, ndb, j);
+    }
+    __device__ __forceinline__ void close(int tg) {
+#pragma unroll
+        for (int j = 0; j < QT; ++j) {
+            const float m = trunc4(__builtin_elementwise_maximum(gm[j], bv[j]));
+            bt[j] = m != bv[j] ? tg : bt[j];
+            bv[j] = m;
+            gm[j] = -INFINITY;
+        }
+    }
+};
+
 // Online log-sum-exp of a query's scores over the database rows (the softmax
 // normaliser of the matching loss), in base 2: with k2 = log2(e) / tau and
 // z = score * k2, the state is an integer offset m and s = the sum over the rows seen
@@ -1277,9 +1318,13 @@ __global__ __launch_bounds__(kRcThreads) void rowcol_argmax_kernel(RowColArgs a)
             const bool valid = j < nact && qp < na;
             q[j].load(abase, valid ? qp : 0, valid, h, d, 1);
         }
-        const int t0 = (int)((int64_t)sg * ntiles / nsg);
-        const int t1 = (int)((int64_t)(sg + 1) * ntiles / nsg);
-        TileBest<kRcQT> best;
+        // segments are whole groups of kRcFlush tiles (the host keeps nsg <= groups), so
+        // every group a segment visits is one of the map's fixed groups [8k, 8k + 8)
+        const int ngroups = (ntiles + kRcFlush - 1) / kRcFlush;
+        const int t0 = (int)((int64_t)sg * ngroups / nsg) * kRcFlush;
+        const int t1e = (int)((int64_t)(sg + 1) * ngroups / nsg) * kRcFlush;
+        const int t1 = t1e < ntiles ? t1e : ntiles;
+        GroupBest<kRcQT> best;
 
         // b tiles [tg, tend) are copied into ring set `set` by the workgroup, straight
         // from global memory into LDS (no registers), 16 bytes per lane: the group's
@@ -1427,6 +1472,7 @@ __global__ __launch_bounds__(kRcThreads) void rowcol_argmax_kernel(RowColArgs a)
                     column_out(c, set * kRcFlush, t - tg);
                 }
                 }
+                best.close(tg / kRcFlush);              // rows: the group's maxima
                 __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's copies of the next group
                 merge(set * kRcFlush, tg, tend);        // barrier, then the wave maxima
             }
@@ -1447,19 +1493,21 @@ __global__ __launch_bounds__(kRcThreads) void rowcol_argmax_kernel(RowColArgs a)
     }
 }
 
-// Column recovery by query block.  The b rows a block won are gathered into one list
-// per block (count, prefix, scatter), then one workgroup per block loads the block's
-// query tiles once and compares them with every gathered row: each gathered 32-row
-// tile is the A operand of the same instruction, with the same operand layout and
-// step order as the fused pass (an output element depends only on its row and column
-// operands, not on the row's place in the tile), so the scores are bitwise those that
-// were compared.  Each row takes the lowest query of the block whose compared score
-// equals its key's.
-struct ColBuckets {
-    int32_t* cnt;     // [batch][nblocks] rows won per query block
-    int32_t* pos;     // [batch][nblocks] prefix sums, then (after the scatter) end offsets
-    int32_t* list;    // [batch][nb] row ids grouped by block
-    int32_t nblocks;
+// Recoveries of the fused pass by bucket.  Each direction's keys name a bucket in their
+// low word (a query block for the columns, a group of b tiles for the rows); the
+// entries are gathered into one list per bucket (count, prefix, scatter), then the
+// bucket's shared operands are loaded once and compared with every gathered entry.
+// A gathered 32-entry tile is an operand of the same instruction, with the same
+// operand layout and step order as the fused pass (an output element depends only on
+// its row and column operands, not on their places in the tile), so the scores are
+// bitwise those that were compared.
+struct Buckets {
+    const uint64_t* keys;   // [batch][n] (score, ~bucket), 0 for none
+    int64_t n;
+    int32_t* cnt;     // [batch][nbins] entries per bucket
+    int32_t* pos;     // [batch][nbins] prefix sums, then (after the scatter) end offsets
+    int32_t* list;    // [batch][n] entry ids grouped by bucket
+    int32_t nbins;
 };
 
 // Counting and scattering run per chunk of kBucketChunk rows (one workgroup of 256
@@ -1470,46 +1518,50 @@ struct ColBuckets {
 constexpr int kBucketChunk = 2048;
 constexpr int kBucketBins = 8192;
 
-__global__ __launch_bounds__(256) void col_bucket_count_kernel(RowColArgs a, ColBuckets c) {
+// Both directions in one launch: blockIdx.z selects the bucket set (0 = b0, 1 = b1).
+__global__ __launch_bounds__(256) void bucket_count_kernel(Buckets b0, Buckets b1) {
     __shared__ int32_t hist[kBucketBins];
+    const Buckets c = blockIdx.z ? b1 : b0;
+    if ((int64_t)blockIdx.x * kBucketChunk >= c.n) return;
     const int pair = blockIdx.y;
-    const uint64_t* keys = a.keys_ba + (int64_t)pair * a.nb;
-    int32_t* cnt = c.cnt + (int64_t)pair * c.nblocks;
-    const bool local = c.nblocks <= kBucketBins;
+    const uint64_t* keys = c.keys + (int64_t)pair * c.n;
+    int32_t* cnt = c.cnt + (int64_t)pair * c.nbins;
+    const bool local = c.nbins <= kBucketBins;
     if (local) {
-        for (int i = threadIdx.x; i < c.nblocks; i += 256) hist[i] = 0;
+        for (int i = threadIdx.x; i < c.nbins; i += 256) hist[i] = 0;
         __syncthreads();
     }
     const int64_t r0 = (int64_t)blockIdx.x * kBucketChunk;
 #pragma unroll
     for (int e = 0; e < kBucketChunk / 256; ++e) {
         const int64_t i = r0 + e * 256 + threadIdx.x;
-        const uint64_t k = i < a.nb ? keys[i] : 0;
+        const uint64_t k = i < c.n ? keys[i] : 0;
         const uint32_t b = ~(uint32_t)k;
-        if (k && b < (uint32_t)c.nblocks) {
+        if (k && b < (uint32_t)c.nbins) {
             if (local) atomicAdd(&hist[b], 1);
             else atomicAdd(&cnt[b], 1);
         }
     }
     if (local) {
         __syncthreads();
-        for (int i = threadIdx.x; i < c.nblocks; i += 256)
+        for (int i = threadIdx.x; i < c.nbins; i += 256)
             if (hist[i]) atomicAdd(&cnt[i], hist[i]);
     }
 }
 
 // exclusive prefix of the counts, one workgroup of 1024 threads per pair, 1024 counts
 // per step
-__global__ __launch_bounds__(1024) void col_bucket_scan_kernel(ColBuckets c) {
+__global__ __launch_bounds__(1024) void bucket_scan_kernel(Buckets b0, Buckets b1) {
     __shared__ int32_t part[1024 / 64];
+    const Buckets c = blockIdx.y ? b1 : b0;
     const int pair = blockIdx.x;
-    const int32_t* cnt = c.cnt + (int64_t)pair * c.nblocks;
-    int32_t* pos = c.pos + (int64_t)pair * c.nblocks;
+    const int32_t* cnt = c.cnt + (int64_t)pair * c.nbins;
+    int32_t* pos = c.pos + (int64_t)pair * c.nbins;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     int32_t carry = 0;
-    for (int base = 0; base < c.nblocks; base += 1024) {
+    for (int base = 0; base < c.nbins; base += 1024) {
         const int i = base + (int)threadIdx.x;
-        const int32_t v = i < c.nblocks ? cnt[i] : 0;
+        const int32_t v = i < c.nbins ? cnt[i] : 0;
         int32_t x = v;   // inclusive scan within the wave
 #pragma unroll
         for (int m = 1; m < 64; m <<= 1) {
@@ -1522,7 +1574,7 @@ __global__ __launch_bounds__(1024) void col_bucket_scan_kernel(ColBuckets c) {
         for (int w = 0; w < wv; ++w) before += part[w];
         int32_t total = 0;
         for (int w = 0; w < 1024 / 64; ++w) total += part[w];
-        if (i < c.nblocks) pos[i] = before + x - v;
+        if (i < c.nbins) pos[i] = before + x - v;
         carry += total;
         __syncthreads();
     }
@@ -1530,36 +1582,38 @@ __global__ __launch_bounds__(1024) void col_bucket_scan_kernel(ColBuckets c) {
 
 // rows -> their block's list; with the LDS histogram a row's place is its block's base
 // for this chunk (one global atomic per non-empty block) plus its rank in the chunk
-__global__ __launch_bounds__(256) void col_bucket_scatter_kernel(RowColArgs a, ColBuckets c) {
+__global__ __launch_bounds__(256) void bucket_scatter_kernel(Buckets b0, Buckets b1) {
     __shared__ int32_t hist[kBucketBins];
+    const Buckets c = blockIdx.z ? b1 : b0;
+    if ((int64_t)blockIdx.x * kBucketChunk >= c.n) return;
     const int pair = blockIdx.y;
-    const uint64_t* keys = a.keys_ba + (int64_t)pair * a.nb;
-    int32_t* pos = c.pos + (int64_t)pair * c.nblocks;
-    int32_t* list = c.list + (int64_t)pair * a.nb;
+    const uint64_t* keys = c.keys + (int64_t)pair * c.n;
+    int32_t* pos = c.pos + (int64_t)pair * c.nbins;
+    int32_t* list = c.list + (int64_t)pair * c.n;
     const int64_t r0 = (int64_t)blockIdx.x * kBucketChunk;
-    if (c.nblocks > kBucketBins) {
+    if (c.nbins > kBucketBins) {
 #pragma unroll
         for (int e = 0; e < kBucketChunk / 256; ++e) {
             const int64_t i = r0 + e * 256 + threadIdx.x;
-            const uint64_t k = i < a.nb ? keys[i] : 0;
+            const uint64_t k = i < c.n ? keys[i] : 0;
             const uint32_t b = ~(uint32_t)k;
-            if (k && b < (uint32_t)c.nblocks) list[atomicAdd(&pos[b], 1)] = (int32_t)i;
+            if (k && b < (uint32_t)c.nbins) list[atomicAdd(&pos[b], 1)] = (int32_t)i;
         }
         return;
     }
-    for (int i = threadIdx.x; i < c.nblocks; i += 256) hist[i] = 0;
+    for (int i = threadIdx.x; i < c.nbins; i += 256) hist[i] = 0;
     __syncthreads();
     int bk[kBucketChunk / 256], rk[kBucketChunk / 256];
 #pragma unroll
     for (int e = 0; e < kBucketChunk / 256; ++e) {
         const int64_t i = r0 + e * 256 + threadIdx.x;
-        const uint64_t k = i < a.nb ? keys[i] : 0;
+        const uint64_t k = i < c.n ? keys[i] : 0;
         const uint32_t b = ~(uint32_t)k;
-        bk[e] = (k && b < (uint32_t)c.nblocks) ? (int)b : -1;
+        bk[e] = (k && b < (uint32_t)c.nbins) ? (int)b : -1;
         rk[e] = bk[e] >= 0 ? atomicAdd(&hist[bk[e]], 1) : 0;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < c.nblocks; i += 256)
+    for (int i = threadIdx.x; i < c.nbins; i += 256)
         if (hist[i]) hist[i] = atomicAdd(&pos[i], hist[i]);   // this chunk's base in block i's list
     __syncthreads();
 #pragma unroll
@@ -1567,8 +1621,10 @@ __global__ __launch_bounds__(256) void col_bucket_scatter_kernel(RowColArgs a, C
         if (bk[e] >= 0) list[hist[bk[e]] + rk[e]] = (int32_t)(r0 + e * 256 + threadIdx.x);
 }
 
+// Columns: one workgroup per query block; its waves share the block's gathered b rows,
+// each row taking the lowest query of the block whose compared score equals its key's.
 template <int P>
-__global__ __launch_bounds__(kThreads) void recover_cols_gathered_kernel(RowColArgs a, ColBuckets c) {
+__global__ __launch_bounds__(kThreads) void recover_cols_gathered_kernel(RowColArgs a, Buckets c) {
     using Op = Operand<AR_BF16, P>;
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5;
@@ -1580,10 +1636,10 @@ __global__ __launch_bounds__(kThreads) void recover_cols_gathered_kernel(RowColA
     const void* abase = static_cast<const uint16_t*>(a.amap) + pair * a.a_pair_elems;
     const void* bbase = static_cast<const uint16_t*>(a.bmap) + pair * a.b_pair_elems;
     uint64_t* keys_ba = a.keys_ba + (int64_t)pair * nb;
-    const int32_t* cnt = c.cnt + (int64_t)pair * c.nblocks;
-    const int32_t* pos = c.pos + (int64_t)pair * c.nblocks;
+    const int32_t* cnt = c.cnt + (int64_t)pair * c.nbins;
+    const int32_t* pos = c.pos + (int64_t)pair * c.nbins;
     const int32_t* list = c.list + (int64_t)pair * nb;
-    for (int blk = blockIdx.x; blk < c.nblocks; blk += gridDim.x) {
+    for (int blk = blockIdx.x; blk < c.nbins; blk += gridDim.x) {
         const int n = cnt[blk];
         if (n == 0) continue;
         const int begin = pos[blk] - n;   // the scatter advanced pos to the block's end
@@ -1636,6 +1692,62 @@ __global__ __launch_bounds__(kThreads) void recover_cols_gathered_kernel(RowColA
                 const uint64_t k = keys_ba[myrow];
                 keys_ba[myrow] = mine != INT_MAX ? pack_key(from_ordered((uint32_t)(k >> 32)), (uint32_t)mine) : 0;
             }
+        }
+    }
+}
+
+// Rows: one workgroup per group g of b tiles (the tiles [g * kRcFlush, g * kRcFlush +
+// kRcFlush) of the map).  Each wave loads the group's tiles once as A operands and
+// takes every fourth 32-query tile of the gathered queries as B operands; each query
+// takes the lowest row of the group whose compared score equals its key's.
+template <int P>
+__global__ __launch_bounds__(kThreads) void recover_rows_grouped_kernel(RowColArgs a, Buckets c) {
+    using Op = Operand<AR_BF16, P>;
+    const int lane = threadIdx.x & 63;
+    const int h = lane >> 5;
+    const int jl = lane & 31;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int pair = blockIdx.y;
+    const int na = a.na, nb = a.nb, d = a.d;
+    const int ntiles = (nb + 31) >> 5;
+    const void* abase = static_cast<const uint16_t*>(a.amap) + pair * a.a_pair_elems;
+    const void* bbase = static_cast<const uint16_t*>(a.bmap) + pair * a.b_pair_elems;
+    uint64_t* keys_ab = a.keys_ab + (int64_t)pair * na;
+    const int32_t* cnt = c.cnt + (int64_t)pair * c.nbins;
+    const int32_t* pos = c.pos + (int64_t)pair * c.nbins;
+    const int32_t* list = c.list + (int64_t)pair * na;
+    for (int g = blockIdx.x; g < c.nbins; g += gridDim.x) {
+        const int n = cnt[g];
+        if (n <= wv * 32) continue;   // no query tile for this wave
+        const int begin = pos[g] - n;
+        const int g0 = g * kRcFlush;                                       // the group's first tile
+        const int ng = ntiles - g0 < kRcFlush ? ntiles - g0 : kRcFlush;   // tiles of the group
+        Op bt[kRcFlush];
+#pragma unroll
+        for (int k = 0; k < kRcFlush; ++k) {
+            const int row = (g0 + k) * 32 + jl;
+            bt[k].load(bbase, row < nb ? row : 0, k < ng && row < nb, h, d, 2);
+        }
+        for (int q0 = wv * 32; q0 < n; q0 += kWaves * 32) {
+            const int iq = q0 + jl;
+            const int qrow = iq < n ? list[begin + iq] : -1;
+            Op qo;
+            qo.load(abase, qrow >= 0 ? qrow : 0, qrow >= 0, h, d, 1);
+            const float sc = qrow >= 0 ? from_ordered((uint32_t)(keys_ab[qrow] >> 32)) : 0.0f;
+            int found = INT_MAX;
+#pragma unroll
+            for (int k = 0; k < kRcFlush; ++k) {
+                if (k >= ng) break;
+                const f32x16 x = bt[k].mfma(qo, f32x16{});
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = (g0 + k) * 32 + tile_row(v, h);
+                    if (row < nb && trunc4(x[v]) == sc && row < found) found = row;
+                }
+            }
+            const int o = __shfl_xor(found, 32);
+            found = o < found ? o : found;
+            if (h == 0 && qrow >= 0) keys_ab[qrow] = found != INT_MAX ? pack_key(sc, (uint32_t)found) : 0;
         }
     }
 }
@@ -2681,7 +2793,7 @@ FastLayout fast_layout(const mr_map* a, const mr_map* b, int64_t nseeds) {
 // Query blocks of the fused pass (kRcQT query tiles each) for a map of n pixels.
 inline int64_t rc_blocks(int64_t n) { return ((n + 31) / 32 + kRcQT - 1) / kRcQT; }
 
-struct MutualLayout { size_t keys_ab, keys_ba, blk, bcnt, bpos, blist, total; };
+struct MutualLayout { size_t keys_ab, keys_ba, blk, bcnt, bpos, blist, rcnt, rpos, rlist, total; };
 
 MutualLayout mutual_layout(const mr_map* a, const mr_map* b) {
     MutualLayout L;
@@ -2692,10 +2804,16 @@ MutualLayout mutual_layout(const mr_map* a, const mr_map* b) {
     L.keys_ab = off; off = align256(off + batch * (size_t)(na > 0 ? na : 1) * 8);
     L.keys_ba = off; off = align256(off + batch * (size_t)(nb > 0 ? nb : 1) * 8);
     L.blk = off; off = align256(off + batch * (size_t)(nblk_of(na) > 0 ? nblk_of(na) : 1) * 4);
-    // column recovery of the fused pass: rows won per query block, their offsets, the rows
+    // recoveries of the fused pass: per bucket counts, offsets and entries, for the
+    // columns (b rows by winning query block) and the rows (queries by winning group of
+    // kRcFlush b tiles)
+    const size_t ntb = (size_t)(((nb + 31) / 32 + kRcFlush - 1) / kRcFlush > 0 ? ((nb + 31) / 32 + kRcFlush - 1) / kRcFlush : 1);
     L.bcnt = off; off = align256(off + batch * nbk * 4);
     L.bpos = off; off = align256(off + batch * nbk * 4);
     L.blist = off; off = align256(off + batch * (size_t)(nb > 0 ? nb : 1) * 4);
+    L.rcnt = off; off = align256(off + batch * ntb * 4);
+    L.rpos = off; off = align256(off + batch * ntb * 4);
+    L.rlist = off; off = align256(off + batch * (size_t)(na > 0 ? na : 1) * 4);
     L.total = off;
     return L;
 }
@@ -2771,7 +2889,8 @@ int nn_impl(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q
 // two recoveries (tile -> row for the rows, query block -> row for the columns).  The
 // keys are zero on entry.
 template <int P>
-int launch_rowcol_t(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* kba, ColBuckets cb, hipStream_t st) {
+int launch_rowcol_t(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* kba, Buckets rb, Buckets cb,
+                    hipStream_t st) {
     const int batch = a->batch;
     const int64_t na = npix(a), nb = npix(b);
     if (na == 0 || nb == 0) return MR_OK;
@@ -2794,7 +2913,8 @@ int launch_rowcol_t(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* k
     const int64_t qgroups = (nqt + kRcGroupTiles - 1) / kRcGroupTiles;
     int64_t nsg = (3 * (int64_t)resident + qgroups - 1) / qgroups;
     if (nsg >= 8) nsg = (nsg + 7) & ~int64_t(7);
-    const int64_t cap = ntiles < kMaxSegGroups ? ntiles : kMaxSegGroups;
+    const int64_t ngroups = (ntiles + kRcFlush - 1) / kRcFlush;   // segments are whole groups
+    const int64_t cap = ngroups < kMaxSegGroups ? ngroups : kMaxSegGroups;
     nsg = nsg < 1 ? 1 : (nsg > cap ? cap : nsg);
     x.nsg = (int32_t)nsg;
     const int64_t items = qgroups * nsg;
@@ -2805,29 +2925,29 @@ int launch_rowcol_t(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* k
     hipLaunchKernelGGL((rowcol_argmax_kernel<P>), dim3(gx, batch), dim3(kRcThreads), 0, st, x);
     if (dev_err()) return MR_ERR_DEVICE;
     if ((rc = prof_close(st, rec))) return rc;
-    NNArgs f = nn_args(a, a->data, 1, b, b->data, 2);
-    f.qsrc = Q_ALL;
-    f.host_count = (int32_t)na;
-    f.keys = kab;
-    f.keys_stride = na;
-    const int rgx = (int)((na + 31) / 32 < (1 << 20) ? (na + 31) / 32 : (1 << 20));
-    hipLaunchKernelGGL((recover_rows_kernel<AR_BF16, P>), dim3(rgx, batch), dim3(kThreads), 0, st, f);
-    // columns: rows bucketed by winning query block, then one workgroup per block
-    const int64_t nbk = cb.nblocks;
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_1d(batch * nbk)), dim3(256), 0, st, cb.cnt, batch * nbk, 0);
-    const int chunks = (int)((nb + kBucketChunk - 1) / kBucketChunk);
-    hipLaunchKernelGGL(col_bucket_count_kernel, dim3(chunks, batch), dim3(256), 0, st, x, cb);
-    hipLaunchKernelGGL(col_bucket_scan_kernel, dim3(batch), dim3(1024), 0, st, cb);
-    hipLaunchKernelGGL(col_bucket_scatter_kernel, dim3(chunks, batch), dim3(256), 0, st, x, cb);
-    const int cgx = (int)(nbk < 65536 ? nbk : 65536);
-    hipLaunchKernelGGL((recover_cols_gathered_kernel<P>), dim3(cgx, batch), dim3(kThreads), 0, st, x, cb);
+    // both directions' keys -> per-bucket lists (one launch per step for both), then
+    // one recovery launch per direction
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_1d(batch * (int64_t)rb.nbins)), dim3(256), 0, st, rb.cnt,
+                       batch * (int64_t)rb.nbins, 0);
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_1d(batch * (int64_t)cb.nbins)), dim3(256), 0, st, cb.cnt,
+                       batch * (int64_t)cb.nbins, 0);
+    const int64_t nmax = rb.n > cb.n ? rb.n : cb.n;
+    const int chunks = (int)((nmax + kBucketChunk - 1) / kBucketChunk);
+    hipLaunchKernelGGL(bucket_count_kernel, dim3(chunks, batch, 2), dim3(256), 0, st, rb, cb);
+    hipLaunchKernelGGL(bucket_scan_kernel, dim3(batch, 2), dim3(1024), 0, st, rb, cb);
+    hipLaunchKernelGGL(bucket_scatter_kernel, dim3(chunks, batch, 2), dim3(256), 0, st, rb, cb);
+    hipLaunchKernelGGL((recover_rows_grouped_kernel<P>), dim3((int)(rb.nbins < 65536 ? rb.nbins : 65536), batch),
+                       dim3(kThreads), 0, st, x, rb);
+    hipLaunchKernelGGL((recover_cols_gathered_kernel<P>), dim3((int)(cb.nbins < 65536 ? cb.nbins : 65536), batch),
+                       dim3(kThreads), 0, st, x, cb);
     return dev_err();
 }
 
-int launch_rowcol(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* kba, ColBuckets cb, hipStream_t st) {
+int launch_rowcol(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* kba, Buckets rb, Buckets cb,
+                  hipStream_t st) {
     switch ((a->d + 15) / 16) {
-        case 1: return launch_rowcol_t<1>(a, b, kab, kba, cb, st);
-        case 2: return launch_rowcol_t<2>(a, b, kab, kba, cb, st);
+        case 1: return launch_rowcol_t<1>(a, b, kab, kba, rb, cb, st);
+        case 2: return launch_rowcol_t<2>(a, b, kab, kba, rb, cb, st);
         default: return MR_ERR_SHAPE;
     }
 }
@@ -2854,12 +2974,11 @@ int mutual_impl(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba
     const void *ad = a->data, *bd = b->data;
     if (metric == M_INNER && ar == AR_BF16 && a->d <= 32) {
         // both directions from one pass over the similarity tiles
-        ColBuckets cb;
-        cb.cnt = at<int32_t>(ws, L.bcnt);
-        cb.pos = at<int32_t>(ws, L.bpos);
-        cb.list = at<int32_t>(ws, L.blist);
-        cb.nblocks = (int32_t)rc_blocks(na);
-        if ((rc = launch_rowcol(a, b, kab, kba, cb, st))) return rc;
+        Buckets rb{kab, na, at<int32_t>(ws, L.rcnt), at<int32_t>(ws, L.rpos), at<int32_t>(ws, L.rlist),
+                   (int32_t)(((nb + 31) / 32 + kRcFlush - 1) / kRcFlush)};
+        Buckets cb{kba, nb, at<int32_t>(ws, L.bcnt), at<int32_t>(ws, L.bpos), at<int32_t>(ws, L.blist),
+                   (int32_t)rc_blocks(na)};
+        if ((rc = launch_rowcol(a, b, kab, kba, rb, cb, st))) return rc;
     } else {
         NNArgs f = nn_args(a, ad, 1, b, bd, 2);
         f.qsrc = Q_ALL;
