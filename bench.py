@@ -31,23 +31,27 @@ PEAK_SPLIT_TFLOPS = PEAK_TFLOPS["bf16"] / SPLIT_PRODUCTS
 PEAK_HBM_GBPS = 8000.0
 # fp32 VALU lane-operations per second: the published fp32 vector peak, 157.3 TFLOP/s,
 # is 78.6 T fused multiply-adds per second (32 fp32 lanes per SIMD per clock, 256 CUs x
-# 4 SIMDs x 2.4 GHz, twice the fp64 rate); a plain fp32 VALU operation (subtract,
-# multiply, minimum) counts as one lane-operation like an FMA.
+# 4 SIMDs x 2.4 GHz); a plain fp32 VALU operation (subtract, multiply, minimum) counts as
+# one lane-operation like an FMA.  Measured without packed instructions: one instruction
+# type issues at 16 lanes per clock, the point kernel's mix at up to 23 (56 T/s), so the
+# published figure is an upper bound.
 PEAK_VALU_TOPS = 157.3 / 2
 # Algorithmic VALU work of one (query, point) pair of 3D pointmaps: 3 subtractions, a
 # multiply and 2 fused multiply-adds for the squared distance, and half of a 3-input
 # minimum for the selection.
 POINT_OPS_PER_PAIR = 6.5
-# Transcendental (v_exp_f32) lane-operations per second: a quarter of the plain VALU
-# lane-operation rate.
+# Transcendental (v_exp_f32) lane-operations per second: 8 lanes per SIMD per clock, a
+# quarter of the published rate (measured: 19.3 T/s at 2.39 GHz).
 PEAK_EXP_TOPS = PEAK_VALU_TOPS / 4
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # defaults: about 27 ms of timed calls after 20 warm-up calls (about 11 ms), which
+    # leave the first calls' lower clock out of the mean
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--main-only", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", choices=OTHER, default=None,
@@ -355,15 +359,15 @@ def other_bruteforce(args, torch, dev):
     p2 = workloads.config_pair(2)
     A2, B2 = dev_maps(p2, torch, dev)
     ws = torch.empty(mr.workspace_bytes(mr.MR_OP_MUTUAL_NN, A2, B2), dtype=torch.uint8, device=dev)
-    # about 3 ms per call: at least 10 timed calls after 3 warm-up calls, so that the
-    # clock ramp of the first calls does not weigh on the mean
-    steps = max(10, args.steps // 2)
-    ms, kms, kn = time_steps(lambda: mr.mutual_nn(A2, B2, ws=ws), steps, 3, torch, 2 * steps)
+    # about 2.5 ms per call: 10 warm-up calls (the first calls run at a lower clock),
+    # then at least 10 timed calls
+    steps = max(10, args.steps // 4)
+    ms, kms, kn = time_steps(lambda: mr.mutual_nn(A2, B2, ws=ws), steps, 10, torch, 2 * steps)
     fl = 2.0 * p2.N * p2.N * p2.d   # the method's work: the similarity matrix once
     # the two-pass alternative: a row search in each direction (the maps' roles swapped),
     # i.e. the matrix computed twice; the mutual call above computes it once
     wn = torch.empty(mr.workspace_bytes(mr.MR_OP_NN_ARGMAX, A2, B2, p2.N), dtype=torch.uint8, device=dev)
-    ms2, _, _ = time_steps(lambda: (mr.nn_argmax(A2, B2, ws=wn), mr.nn_argmax(B2, A2, ws=wn)), steps, 3, torch)
+    ms2, _, _ = time_steps(lambda: (mr.nn_argmax(A2, B2, ws=wn), mr.nn_argmax(B2, A2, ws=wn)), steps, 10, torch)
     out = {"pairs_per_s": round(1000.0 / ms, 2), "ms_per_call": round(ms, 3),
            "variant": "fused row + column pass (rowcol_argmax_kernel), then both recoveries",
            "two_pass_ms": round(ms2, 3),
