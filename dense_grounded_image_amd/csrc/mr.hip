@@ -234,12 +234,22 @@ template <int P> struct Operand<AR_X3, P> {
             x[s] = __builtin_bit_cast(bf16x8, raw);
         }
     }
-    // from an fp32 row of the map, split here
+    // from an fp32 row of the map, split here (fetch_f32 + split_f32, which callers may
+    // separate to keep the row's loads in flight meanwhile)
     __device__ __forceinline__ void load_f32(const float* rowp, bool valid, int h, int role) {
+        float4 raw[D / 4];
+        fetch_f32(rowp, valid, raw);
+        split_f32(raw, h, role);
+    }
+    static __device__ __forceinline__ void fetch_f32(const float* rowp, bool valid, float4 (&raw)[D / 4]) {
+#pragma unroll
+        for (int i = 0; i < D / 4; ++i) raw[i] = valid ? reinterpret_cast<const float4*>(rowp)[i] : float4{0.f, 0.f, 0.f, 0.f};
+    }
+    __device__ __forceinline__ void split_f32(const float4 (&raw)[D / 4], int h, int role) {
         uint32_t pl[3][D / 2];   // planes, two bf16 per word
 #pragma unroll
         for (int i = 0; i < D / 4; ++i) {
-            const float4 v = valid ? reinterpret_cast<const float4*>(rowp)[i] : float4{0.f, 0.f, 0.f, 0.f};
+            const float4 v = raw[i];
             uint2 a[3];
             split3x4(v.x, v.y, v.z, v.w, a);
 #pragma unroll
@@ -924,23 +934,15 @@ __device__ __forceinline__ void stream_regs(const void* dbase, int t0, int t1,
 // Small frontiers (all live queries fit in one wave): every wave of the workgroup
 // holds the same queries and streams its own database segment straight from global
 // memory, one tile ahead in registers, with no LDS staging and no barriers.
+// Split fp32 rows are fetched a tile ahead and split after the current tile's
+// products, so each tile's load is in flight during the previous tile's products.
 template <int AR, int P, int QT, class Ep>
 __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1, int ndb,
                                               const Operand<AR, P> (&q)[QT],
                                               int nact, int h, int jl, int d, int role, Ep& ep) {
     if (t0 >= t1) return;
     auto row_of = [&](int t) { return (int64_t)t * 32 + jl; };
-    auto get = [&](Operand<AR, P>& o, int t) {
-        const int64_t row = row_of(t) < ndb ? row_of(t) : 0;
-        if constexpr (AR == AR_X3) o.load_f32(static_cast<const float*>(dbase) + row * d, row_of(t) < ndb, h, role);
-        else o.load(dbase, row, row_of(t) < ndb, h, d, role);
-    };
-    Operand<AR, P> rn;
-    get(rn, t0);
-    for (int t = t0; t < t1; ++t) {
-        const Operand<AR, P> r = rn;
-        const int tn = t + 1 < t1 ? t + 1 : t;
-        get(rn, tn);
+    auto compute = [&](const Operand<AR, P>& r, int t) {
         const bool ragged = (t + 1) * 32 > ndb;
 #pragma unroll
         for (int j = 0; j < QT; ++j) {
@@ -949,6 +951,35 @@ __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1,
                 acc = r.mfma(q[j], acc);
                 ep.step(acc, t, h, ndb, j, ragged);
             }
+        }
+    };
+    if constexpr (AR == AR_X3) {
+        constexpr int D = Operand<AR, P>::D;
+        float4 raw[D / 4];
+        auto fetch = [&](int t) {
+            const int64_t row = row_of(t) < ndb ? row_of(t) : 0;
+            Operand<AR, P>::fetch_f32(static_cast<const float*>(dbase) + row * d, row_of(t) < ndb, raw);
+        };
+        fetch(t0);
+        Operand<AR, P> r;
+        r.split_f32(raw, h, role);
+        for (int t = t0; t < t1; ++t) {
+            fetch(t + 1 < t1 ? t + 1 : t);
+            compute(r, t);
+            r.split_f32(raw, h, role);
+        }
+    } else {
+        auto get = [&](Operand<AR, P>& o, int t) {
+            const int64_t row = row_of(t) < ndb ? row_of(t) : 0;
+            o.load(dbase, row, row_of(t) < ndb, h, d, role);
+        };
+        Operand<AR, P> rn;
+        get(rn, t0);
+        for (int t = t0; t < t1; ++t) {
+            const Operand<AR, P> r = rn;
+            const int tn = t + 1 < t1 ? t + 1 : t;
+            get(rn, tn);
+            compute(r, t);
         }
     }
 }

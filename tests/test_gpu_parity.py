@@ -85,6 +85,32 @@ def test_nn_argmax_query_list_batch():
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_batch16_xcd_packed_grid(dtype):
+    """16 pairs of ragged 37x29 maps in one call.  Each pair then gets only a few dozen
+    workgroups, so the search runs on the one-dimensional grid that keeps a pair's
+    workgroups on one XCD.  Every pair's NN map and fast-scheme output against the
+    oracle, and three pairs equal to single-pair calls."""
+    B_, d, s, o, T = 16, 24, 4, 2, 6
+    ps = [workloads.make_pair(37, 29, d, seed=900 + b, warp="shift", sigma=0.1, rho=0.2, dtype=dtype)
+          for b in range(B_)]
+    A = torch.stack([dev_map(p.D1, p.H, p.W, p.D1_bits) for p in ps])
+    Bm = torch.stack([dev_map(p.D2, p.H, p.W, p.D2_bits) for p in ps])
+    gi = mr.nn_argmax(A, Bm)
+    fp, fn, act = mr.fast_reciprocal(A, Bm, s, o, T)
+    torch.cuda.synchronize()
+    gi = gi.cpu().numpy()
+    for b, p in enumerate(ps):
+        oi, o1, o2 = oracle.nn(p.D1, p.D2)
+        checks.check_nn(gi[b], oi, o1, o2, p.D1, np.arange(p.N), p.D2, dtype)
+        orc = oracle.fast(p.D1, p.H, p.W, p.D2, s, o, T)
+        checks.check_fast(mr.matches(fp, fn, b), orc, p.D1, p.D2, dtype, gpu_active=act[b].cpu().numpy())
+    for b in (0, 9, 15):
+        sp, sn, _ = mr.fast_reciprocal(A[b], Bm[b], s, o, T)
+        assert mr.matches(sp, sn).tolist() == mr.matches(fp, fn, b).tolist()
+    log("batch16", dtype, [int(x) for x in fn.cpu()][:4], "...")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("db_hw", [(64, 48), (50, 60)])
 def test_nn_argmax_query_counts_across_modes(dtype, db_hw):
     """Query lists of 1 .. 545 rows against a database of whole 32-row tiles (64x48)
