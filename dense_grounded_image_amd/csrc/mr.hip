@@ -1655,7 +1655,7 @@ __global__ __launch_bounds__(256) void bucket_scatter_kernel(Buckets b0, Buckets
 // Columns: one workgroup per query block; its waves share the block's gathered b rows,
 // each row taking the lowest query of the block whose compared score equals its key's.
 template <int P>
-__global__ __launch_bounds__(kThreads) void recover_cols_gathered_kernel(RowColArgs a, Buckets c) {
+__device__ __forceinline__ void recover_cols_gathered_body(RowColArgs a, const Buckets& c) {
     using Op = Operand<AR_BF16, P>;
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5;
@@ -1732,7 +1732,7 @@ __global__ __launch_bounds__(kThreads) void recover_cols_gathered_kernel(RowColA
 // takes every fourth 32-query tile of the gathered queries as B operands; each query
 // takes the lowest row of the group whose compared score equals its key's.
 template <int P>
-__global__ __launch_bounds__(kThreads) void recover_rows_grouped_kernel(RowColArgs a, Buckets c) {
+__device__ __forceinline__ void recover_rows_grouped_body(RowColArgs a, const Buckets& c) {
     using Op = Operand<AR_BF16, P>;
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5;
@@ -1781,6 +1781,15 @@ __global__ __launch_bounds__(kThreads) void recover_rows_grouped_kernel(RowColAr
             if (h == 0 && qrow >= 0) keys_ab[qrow] = found != INT_MAX ? pack_key(sc, (uint32_t)found) : 0;
         }
     }
+}
+
+// Both recoveries of the fused pass in one launch: blockIdx.z = 0 the rows (a workgroup
+// per group of b tiles), 1 the columns (a workgroup per query block), so the two
+// overlap on the GPU.
+template <int P>
+__global__ __launch_bounds__(kThreads) void recover_rowcol_kernel(RowColArgs a, Buckets rows, Buckets cols) {
+    if (blockIdx.z == 0) recover_rows_grouped_body<P>(a, rows);
+    else recover_cols_gathered_body<P>(a, cols);
 }
 
 // ---------------------------------------------------------------------------- pointmaps
@@ -1919,6 +1928,28 @@ __global__ void fill_u64_kernel(uint64_t* p, int64_t n, uint64_t v) {
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = v;
+}
+
+// Up to four fills in one launch (blockIdx.y selects the range; 4- or 8-byte elements).
+struct FillRange { void* p; int64_t n; uint64_t v; int32_t bytes; };
+struct FillSet { FillRange r[4]; };
+
+__global__ void fill_multi_kernel(FillSet f) {
+    const FillRange r = f.r[blockIdx.y];
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < r.n; i += (int64_t)gridDim.x * blockDim.x) {
+        if (r.bytes == 8) static_cast<uint64_t*>(r.p)[i] = r.v;
+        else static_cast<uint32_t*>(r.p)[i] = (uint32_t)r.v;
+    }
+}
+
+// keys -> row ids for two key arrays in one launch (blockIdx.y selects), no scores
+__global__ void decode_keys2_kernel(const uint64_t* k0, int64_t n0, int32_t* i0, const uint64_t* k1, int64_t n1,
+                                    int32_t* i1) {
+    const uint64_t* keys = blockIdx.y ? k1 : k0;
+    int32_t* idx = blockIdx.y ? i1 : i0;
+    const int64_t n = blockIdx.y ? n1 : n0;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        idx[i] = key_row(keys[i]);
 }
 
 // keys -> row ids (and optionally scores; point searches store minus the squared
@@ -2956,21 +2987,16 @@ int launch_rowcol_t(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* k
     hipLaunchKernelGGL((rowcol_argmax_kernel<P>), dim3(gx, batch), dim3(kRcThreads), 0, st, x);
     if (dev_err()) return MR_ERR_DEVICE;
     if ((rc = prof_close(st, rec))) return rc;
-    // both directions' keys -> per-bucket lists (one launch per step for both), then
-    // one recovery launch per direction
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_1d(batch * (int64_t)rb.nbins)), dim3(256), 0, st, rb.cnt,
-                       batch * (int64_t)rb.nbins, 0);
-    hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_1d(batch * (int64_t)cb.nbins)), dim3(256), 0, st, cb.cnt,
-                       batch * (int64_t)cb.nbins, 0);
+    // both directions' keys -> per-bucket lists (one launch per step for both; the
+    // counts were zeroed with the keys), then one launch recovering both
     const int64_t nmax = rb.n > cb.n ? rb.n : cb.n;
     const int chunks = (int)((nmax + kBucketChunk - 1) / kBucketChunk);
     hipLaunchKernelGGL(bucket_count_kernel, dim3(chunks, batch, 2), dim3(256), 0, st, rb, cb);
     hipLaunchKernelGGL(bucket_scan_kernel, dim3(batch, 2), dim3(1024), 0, st, rb, cb);
     hipLaunchKernelGGL(bucket_scatter_kernel, dim3(chunks, batch, 2), dim3(256), 0, st, rb, cb);
-    hipLaunchKernelGGL((recover_rows_grouped_kernel<P>), dim3((int)(rb.nbins < 65536 ? rb.nbins : 65536), batch),
-                       dim3(kThreads), 0, st, x, rb);
-    hipLaunchKernelGGL((recover_cols_gathered_kernel<P>), dim3((int)(cb.nbins < 65536 ? cb.nbins : 65536), batch),
-                       dim3(kThreads), 0, st, x, cb);
+    const int nbmax = rb.nbins > cb.nbins ? rb.nbins : cb.nbins;
+    hipLaunchKernelGGL((recover_rowcol_kernel<P>), dim3(nbmax < 65536 ? nbmax : 65536, batch, 2), dim3(kThreads), 0, st,
+                       x, rb, cb);
     return dev_err();
 }
 
@@ -2999,16 +3025,26 @@ int mutual_impl(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba
     uint64_t* kab = at<uint64_t>(ws, L.keys_ab);
     uint64_t* kba = at<uint64_t>(ws, L.keys_ba);
     int32_t* blk = at<int32_t>(ws, L.blk);
-    hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(batch * na)), dim3(256), 0, st, kab, batch * na, (uint64_t)0);
-    hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(batch * nb)), dim3(256), 0, st, kba, batch * nb, (uint64_t)0);
+    const bool fused = metric == M_INNER && ar == AR_BF16 && a->d <= 32;
+    Buckets rb{kab, na, at<int32_t>(ws, L.rcnt), at<int32_t>(ws, L.rpos), at<int32_t>(ws, L.rlist),
+               (int32_t)(((nb + 31) / 32 + kRcFlush - 1) / kRcFlush)};
+    Buckets cb{kba, nb, at<int32_t>(ws, L.bcnt), at<int32_t>(ws, L.bpos), at<int32_t>(ws, L.blist),
+               (int32_t)rc_blocks(na)};
+    // zero the keys (and the fused pass's bucket counts) in one launch
+    FillSet fs;
+    memset(&fs, 0, sizeof(fs));
+    fs.r[0] = FillRange{kab, batch * na, 0, 8};
+    fs.r[1] = FillRange{kba, batch * nb, 0, 8};
+    if (fused) {
+        fs.r[2] = FillRange{rb.cnt, batch * (int64_t)rb.nbins, 0, 4};
+        fs.r[3] = FillRange{cb.cnt, batch * (int64_t)cb.nbins, 0, 4};
+    }
+    hipLaunchKernelGGL(fill_multi_kernel, dim3(grid_1d(batch * (na > nb ? na : nb)), fused ? 4 : 2), dim3(256), 0, st,
+                       fs);
     if (dev_err()) return MR_ERR_DEVICE;
     const void *ad = a->data, *bd = b->data;
-    if (metric == M_INNER && ar == AR_BF16 && a->d <= 32) {
+    if (fused) {
         // both directions from one pass over the similarity tiles
-        Buckets rb{kab, na, at<int32_t>(ws, L.rcnt), at<int32_t>(ws, L.rpos), at<int32_t>(ws, L.rlist),
-                   (int32_t)(((nb + 31) / 32 + kRcFlush - 1) / kRcFlush)};
-        Buckets cb{kba, nb, at<int32_t>(ws, L.bcnt), at<int32_t>(ws, L.bpos), at<int32_t>(ws, L.blist),
-                   (int32_t)rc_blocks(na)};
         if ((rc = launch_rowcol(a, b, kab, kba, rb, cb, st))) return rc;
     } else {
         NNArgs f = nn_args(a, ad, 1, b, bd, 2);
@@ -3024,10 +3060,8 @@ int mutual_impl(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba
         r.keys_stride = nb;
         if ((rc = launch_search(r, metric, ar, batch, st))) return rc;
     }
-    hipLaunchKernelGGL(decode_keys_kernel, dim3(grid_1d(batch * na)), dim3(256), 0, st, kab, batch * na, nn_ab,
-                       (float*)nullptr, 0);
-    hipLaunchKernelGGL(decode_keys_kernel, dim3(grid_1d(batch * nb)), dim3(256), 0, st, kba, batch * nb, nn_ba,
-                       (float*)nullptr, 0);
+    hipLaunchKernelGGL(decode_keys2_kernel, dim3(grid_1d(batch * (na > nb ? na : nb)), 2), dim3(256), 0, st, kab,
+                       batch * na, nn_ab, kba, batch * nb, nn_ba);
     if (dev_err()) return MR_ERR_DEVICE;
     const int nblk = nblk_of(na) > 0 ? nblk_of(na) : 1;
     MutualPred pr{nn_ab, nn_ba, na, nb};
