@@ -405,11 +405,7 @@ __device__ __forceinline__ void tile_track(const f32x16& acc, int t, int h, int 
 // Per-lane running state of a streamed database segment: one entry per query tile
 // j, updated once per 32-row database tile t (RAGGED: rows at or past ndb are
 // masked).  step() takes the ragged flag at run time.
-enum Epilogue { EP_KEY = 0, EP_EXACT = 1, EP_TILE = 2, EP_LSE = 3, EP_GROUP = 4 };
-
-// Tiles per group of the bf16 search's row tracking (GroupBest; the register stream's
-// ring holds one group).
-constexpr int kGroupTiles = 4;
+enum Epilogue { EP_KEY = 0, EP_EXACT = 1, EP_TILE = 2, EP_LSE = 3 };
 
 // Keyed row maximum: (score, row) of the NN while the lane's best score is >= 0.
 template <int QT> struct KeyBest {
@@ -481,8 +477,6 @@ template <int QT> struct TileBest {
 // lowest row of that group whose compared score equals the best (found later by
 // recomputing the group).
 template <int QT> struct GroupBest {
-    static constexpr int kind = EP_GROUP;
-    static constexpr int valu = 8;    // vector instructions per tile, for scheduling
     float gm[QT], bv[QT];
     int bt[QT];
     __device__ __forceinline__ GroupBest() {
@@ -851,27 +845,17 @@ __device__ __forceinline__ void stream_staged(const char* __restrict__ dbytes, i
     fetch(2, slot0);
     put(1, slot1);
     __syncthreads();
-    // group tracking: a group ends after every kGroupTiles / S stages (t0 is a multiple
-    // of kGroupTiles) and at the end of the segment
-    auto close = [&](int k) {
-        if constexpr (Ep::kind == EP_GROUP) {
-            static_assert(kGroupTiles % S == 0, "a stage lies inside one group");
-            if ((k + 1) % (kGroupTiles / S) == 0 || k + 1 == nst) ep.close((t0 + S * k) / kGroupTiles);
-        }
-    };
     for (int k = 0; k < nst; k += 2) {
         // buffers of stages past the end are free: writing them is harmless
         fetch(k + 3, slot1);
         read(k);
         compute(k);
-        close(k);
         put(k + 2, slot0);
         __syncthreads();
         if (k + 1 >= nst) break;
         fetch(k + 4, slot0);
         read(k + 1);
         compute(k + 1);
-        close(k + 1);
         put(k + 3, slot1);
         __syncthreads();
     }
@@ -899,7 +883,6 @@ __device__ __forceinline__ void stream_regs(const void* dbase, int t0, int t1,
                                             const Operand<AR, P> (&q)[QT], int h, int jl, int d,
                                             Ep& ep) {
     static_assert(AR == AR_BF16, "direct database operands are bf16 only");
-    static_assert(Ep::kind != EP_GROUP || D == kGroupTiles, "a ring chunk is one group");
     Operand<AR, P> r[D];
     int off[P];
     Operand<AR, P>::db_offsets(jl, h, d, off);
@@ -941,14 +924,11 @@ __device__ __forceinline__ void stream_regs(const void* dbase, int t0, int t1,
             r[u].load_db(dbytes + tn * tile_bytes, off);
         }
         ep.template tile<false>(prev, t + D - 1, h, 0, QT - 1);
-        if constexpr (Ep::kind == EP_GROUP) ep.close(t / D);   // segments start at multiples of D
     }
     // the last t1 - t < D tiles are already in the ring
 #pragma unroll
     for (int u = 0; u < D - 1; ++u)
         if (t + u < t1) compute(r[u], t + u);
-    if constexpr (Ep::kind == EP_GROUP)
-        if (t < t1) ep.close(t / D);
 }
 
 // Small frontiers (all live queries fit in one wave): every wave of the workgroup
@@ -1000,8 +980,6 @@ __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1,
             const int tn = t + 1 < t1 ? t + 1 : t;
             get(rn, tn);
             compute(r, t);
-            if constexpr (Ep::kind == EP_GROUP)
-                if ((t + 1) % kGroupTiles == 0 || t + 1 == t1) ep.close(t / kGroupTiles);
         }
     }
 }
@@ -1012,9 +990,8 @@ __device__ __forceinline__ void stream_direct(const void* dbase, int t0, int t1,
 // shrinking frontier still spreads over the whole GPU; it is a multiple of 8 when
 // possible so that each XCD keeps streaming the same eighth of the database through
 // its own L2.  Every wave leaves one atomicMax per query and item.  With
-// tile_best arithmetic (bf16) the merged key names (score, group of kGroupTiles
-// tiles), segments are whole groups, and recover_rows_kernel turns it into
-// (score, row).
+// tile_best arithmetic the merged key names (score, tile) and recover_rows_kernel
+// turns it into (score, row).
 // Waves per SIMD the compiler must leave room for (register budget): three for the
 // short bf16 contraction, whose database ring and accumulators otherwise land just
 // above that budget; the split-fp32 and fp32 forms need their registers.
@@ -1050,10 +1027,8 @@ void nn_argmax_kernel(NNArgs a) {
     const int nqt = (n + 31) >> 5;                        // query tiles
     const int qgroups = (nqt + kWaves * QT - 1) / (kWaves * QT);
     if (qgroups == 0 || ntiles == 0) return;
-    // with group tracking (TB) segments are whole groups of kGroupTiles tiles
-    const int nunits = TB ? (ntiles + kGroupTiles - 1) / kGroupTiles : ntiles;
     int nsg = gx / qgroups;
-    const int sg_cap = nunits < kMaxSegGroups ? nunits : kMaxSegGroups;
+    const int sg_cap = ntiles < kMaxSegGroups ? ntiles : kMaxSegGroups;
     nsg = nsg < 1 ? 1 : (nsg > sg_cap ? sg_cap : nsg);
     if (nsg >= 8) nsg &= ~7;
     const int items = qgroups * nsg;
@@ -1120,7 +1095,7 @@ void nn_argmax_kernel(NNArgs a) {
             float sv[QT];
             int rw[QT];   // row, or tile with TB
             if constexpr (TB) {
-                GroupBest<QT> best;
+                TileBest<QT> best;
                 stream_direct<AR, P>(dbytes, t0, t1, a.ndb, q, nact, h, jl, a.d, a.db_role, best);
 #pragma unroll
                 for (int j = 0; j < QT; ++j) { sv[j] = best.bv[j]; rw[j] = best.bt[j]; }
@@ -1170,16 +1145,14 @@ void nn_argmax_kernel(NNArgs a) {
 
         Operand<AR, P> q[QT];
         load_queries(q, g0 + wv, kWaves, nact);
-        const int unit = TB ? kGroupTiles : 1;
-        const int t0 = (int)((int64_t)sg * nunits / nsg) * unit;
-        const int t1e = (int)((int64_t)(sg + 1) * nunits / nsg) * unit;
-        const int t1 = t1e < ntiles ? t1e : ntiles;
+        const int t0 = (int)((int64_t)sg * ntiles / nsg);
+        const int t1 = (int)((int64_t)(sg + 1) * ntiles / nsg);
 
         // (score, row) -- or (score, tile) with TB -- per lane and query tile
         float sv[QT];
         int rw[QT];
         if constexpr (TB) {
-            GroupBest<QT> best;
+            TileBest<QT> best;
             // segments without a ragged tile stream through registers, each wave on its
             // own (a wave short of query tiles multiplies zero operands in the empty
             // slots, whose keys are never written; a wave with none skips the stream);
@@ -1221,22 +1194,15 @@ void nn_argmax_kernel(NNArgs a) {
     }
 }
 
-// (score, group) -> (score, row): a query tile per kRecoverParts workgroups; each wave
-// takes kRecoverCPW of its 32 queries.  For query c the wave loads the rows of c's
-// group of kGroupTiles tiles (all of its queries' tiles at once), as the A operand,
-// and multiplies them with the query block
-// exactly as the streaming pass did (same instruction, same operand layout, same step
-// order), so column c holds bitwise the scores that were compared there; the lowest
-// row of the group whose trunc4 score equals the key's score is c's NN (where a
-// segment covered only part of the group, no lower row of the group has that score:
-// an earlier segment holding one would have won the key).  Keys are rewritten in place.
-// Queries a wave resolves; a query tile takes kRecoverParts workgroups.
-constexpr int kRecoverCPW = 2;
-constexpr int kRecoverParts = 32 / (kWaves * kRecoverCPW);
-
+// (score, tile) -> (score, row): one query tile per workgroup; each wave takes 8 of
+// its 32 queries.  For query c the wave loads the 32 rows of c's tile as the A
+// operand and multiplies them with the query block exactly as the streaming pass
+// did (same instruction, same operand layout, same step order), so column c holds
+// bitwise the scores that were compared there; the lowest row whose trunc4 score
+// equals the key's score is c's NN.  Keys are rewritten in place.
 template <int AR, int P>
 __global__ __launch_bounds__(kThreads) void recover_rows_kernel(NNArgs a) {
-    constexpr int CPW = kRecoverCPW;
+    constexpr int CPW = 32 / kWaves;   // queries resolved per wave
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5;
     const int jl = lane & 31;
@@ -1247,9 +1213,7 @@ __global__ __launch_bounds__(kThreads) void recover_rows_kernel(NNArgs a) {
     const void* qbase = pair_base<AR>(a.qmap, a.q_pair_elems, map_of(a.q_img, pair));
     const void* dbase = pair_base<AR>(a.dbmap, a.db_pair_elems, map_of(a.db_img, pair));
     uint64_t* keys = a.keys + pair * a.keys_stride;
-    for (int item = blockIdx.x; item < nqt * kRecoverParts; item += gridDim.x) {
-        const int g = item / kRecoverParts;                              // query tile
-        const int c0 = (item - g * kRecoverParts) * (kWaves * CPW) + wv * CPW;   // this wave's first column
+    for (int g = blockIdx.x; g < nqt; g += gridDim.x) {
         const int qp = g * 32 + jl;
         int64_t row = qp;
         bool valid = qp < n;
@@ -1260,45 +1224,38 @@ __global__ __launch_bounds__(kThreads) void recover_rows_kernel(NNArgs a) {
         valid = valid && row >= 0 && row < a.nq_rows;
         Operand<AR, P> q;
         q.load(qbase, valid ? row : 0, valid, h, a.d, a.q_role);
-        // this lane's query key; only columns c0.. are read back below, and only this
+        // this lane's query key; only columns 8*wv.. are read back below, and only this
         // wave rewrites them, after the read
         const uint64_t key = qp < n ? keys[qp] : 0;
-        // the key names a group of kGroupTiles tiles: all of them for the wave's CPW
-        // queries, loaded at once
-        int grp[CPW];
-        float best[CPW];
-        Operand<AR, P> r[CPW][kGroupTiles];
+        Operand<AR, P> r[CPW];
+        int tile[CPW];
 #pragma unroll
         for (int k = 0; k < CPW; ++k) {
-            const uint64_t kc = shfl_u64(key, c0 + k);
-            grp[k] = kc ? (int)~(uint32_t)kc : -1;
-            best[k] = from_ordered((uint32_t)(kc >> 32));
-#pragma unroll
-            for (int tt = 0; tt < kGroupTiles; ++tt) {
-                const int64_t drow = ((int64_t)grp[k] * kGroupTiles + tt) * 32 + jl;
-                const bool ok = grp[k] >= 0 && drow < a.ndb;
-                r[k][tt].load(dbase, ok ? drow : 0, ok, h, a.d, a.db_role);
-            }
+            const uint64_t kc = shfl_u64(key, CPW * wv + k);
+            tile[k] = kc ? (int)~(uint32_t)kc : -1;
+            const int64_t drow = (int64_t)tile[k] * 32 + jl;
+            const bool ok = tile[k] >= 0 && drow < a.ndb;
+            r[k].load(dbase, ok ? drow : 0, ok, h, a.d, a.db_role);
         }
         uint64_t out = 0;
 #pragma unroll
         for (int k = 0; k < CPW; ++k) {
+            const int c = CPW * wv + k;
+            const uint64_t kc = shfl_u64(key, c);
+            const float best = from_ordered((uint32_t)(kc >> 32));
+            f32x16 acc = {};
+            acc = r[k].mfma(q, acc);
             int found = INT_MAX;
 #pragma unroll
-            for (int tt = 0; tt < kGroupTiles; ++tt) {
-                f32x16 acc = {};
-                acc = r[k][tt].mfma(q, acc);
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int rr = (grp[k] * kGroupTiles + tt) * 32 + tile_row(v, h);
-                    if (trunc4(acc[v]) == best[k] && rr < a.ndb && rr < found) found = rr;
-                }
+            for (int v = 15; v >= 0; --v) {
+                const int rr = tile[k] * 32 + tile_row(v, h);
+                if (trunc4(acc[v]) == best && rr < a.ndb) found = rr;
             }
             const int o = __shfl_xor(found, 32);
             found = o < found ? o : found;
-            if (jl == c0 + k) out = (grp[k] >= 0 && found != INT_MAX) ? pack_key(best[k], (uint32_t)found) : 0;
+            if (jl == c) out = (kc != 0 && found != INT_MAX) ? pack_key(best, (uint32_t)found) : 0;
         }
-        if (h == 0 && qp < n && jl >= c0 && jl < c0 + CPW) keys[qp] = out;
+        if (h == 0 && qp < n && jl >= CPW * wv && jl < CPW * (wv + 1)) keys[qp] = out;
     }
 }
 
@@ -2807,8 +2764,7 @@ int launch_nn(const NNArgs& a, int ar, int batch, hipStream_t st) {
     if (ar == AR_BF16) {
         // tile keys -> row keys
         const int64_t max_n = a.dev_count ? a.qlist_stride : a.host_count;
-        const int64_t items = (max_n + 31) / 32 * kRecoverParts;
-        const int gx = (int)(items < (1 << 20) ? items : (1 << 20));
+        const int gx = (int)((max_n + 31) / 32 < (1 << 20) ? (max_n + 31) / 32 : (1 << 20));
         if (gx < 1) return MR_OK;
         switch ((a.d + 15) / 16) {
 #define MR_CASE(p) case p: hipLaunchKernelGGL((recover_rows_kernel<AR_BF16, p>), dim3(gx, batch), dim3(kThreads), 0, st, a); break;
