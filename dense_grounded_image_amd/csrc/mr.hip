@@ -2641,7 +2641,10 @@ int64_t seed_count(int32_t h, int32_t w, int32_t stride, int32_t offset) {
     return ny * nx;
 }
 
-int grid_1d(int64_t n, int threads = 256, int cap = 1 << 24) {
+// Workgroups for a grid-stride kernel over n items.  At most 2^20: the kernels loop
+// over any n, and grid.x * threads must stay below the 2^32 work-items that one
+// dimension of a dispatch can hold (2^24 workgroups of 256 would be exactly 2^32).
+int grid_1d(int64_t n, int threads = 256, int cap = 1 << 20) {
     int64_t g = (n + threads - 1) / threads;
     if (g < 1) g = 1;
     return (int)(g > cap ? cap : g);
