@@ -36,7 +36,10 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -65,6 +68,68 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSegGroups = 512;   // database segments per query block (bounds atomic contention)
 constexpr int kCompactChunk = 2048;  // elements per block in the ordered compaction
 constexpr int kMaxD = 64;
+
+// ---------------------------------------------------------------------------- launch log
+
+// MR_LOG set to anything but "" or "0" in the environment (read once per process)
+// makes every entry point print, on stderr, a line with its maps and parameters, one
+// line per kernel launch (kernel, template arguments, grid, block, LDS bytes, stream)
+// and a line with the status it returns.  Off, it costs one branch per launch.
+bool log_on() {
+    static const bool on = [] {
+        const char* e = getenv("MR_LOG");
+        return e && e[0] && strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+
+// `where` is the launching function's __PRETTY_FUNCTION__: its trailing "[...]", when
+// it is a template, gives the launcher's template arguments (which select the kernel's).
+void log_launch(const char* kernel, const char* where, dim3 g, dim3 b, size_t lds, hipStream_t st) {
+    const char* targs = strrchr(where, '[');
+    fprintf(stderr, "[mr]   launch %s%s%s%s grid (%u,%u,%u) block (%u,%u,%u) lds %zu stream %p\n", kernel,
+            targs ? " (launcher " : "", targs ? targs : "", targs ? ")" : "", g.x, g.y, g.z, b.x, b.y, b.z, lds,
+            static_cast<void*>(st));
+}
+
+// Every kernel launch of the library goes through this macro.
+#define MR_LAUNCH(K, GRID, BLOCK, LDS, ST, ...)                                       \
+    do {                                                                              \
+        const dim3 mr_grid_ = (GRID), mr_block_ = (BLOCK);                            \
+        if (log_on()) log_launch(#K, __PRETTY_FUNCTION__, mr_grid_, mr_block_, (LDS), (ST)); \
+        hipLaunchKernelGGL(K, mr_grid_, mr_block_, LDS, ST, __VA_ARGS__);             \
+    } while (0)
+
+const char* dtype_name(int dt) { return dt == MR_F32 ? "f32" : dt == MR_BF16 ? "bf16" : "?"; }
+
+// One entry-point call in the log: its maps and parameters on entry, its status on return.
+class CallLog {
+public:
+    __attribute__((format(printf, 5, 6))) CallLog(const char* name, const mr_map* a, const mr_map* b,
+                                                  const char* fmt, ...)
+        : name_(name) {
+        if (!log_on()) return;
+        char pa[96], pb[96], extra[160];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(extra, sizeof(extra), fmt, ap);
+        va_end(ap);
+        fprintf(stderr, "[mr] %s a %s b %s %s\n", name, map_str(a, pa, sizeof(pa)), map_str(b, pb, sizeof(pb)),
+                extra);
+    }
+    int done(int status) const {
+        if (log_on()) fprintf(stderr, "[mr] %s -> %d (%s)\n", name_, status, mr_status_str(status));
+        return status;
+    }
+
+private:
+    static const char* map_str(const mr_map* m, char* buf, size_t n) {
+        if (!m) return "NULL";
+        snprintf(buf, n, "%dx%dx%dx%d %s @%p", m->batch, m->h, m->w, m->d, dtype_name(m->dtype), m->data);
+        return buf;
+    }
+    const char* name_;
+};
 
 // ---------------------------------------------------------------------------- keys
 
@@ -2717,9 +2782,9 @@ void launch_nn_t(const NNArgs& a, int batch, hipStream_t st) {
         NNArgs b = a;
         b.xcd_gx = packed;
         b.batch = batch;
-        hipLaunchKernelGGL((nn_argmax_kernel<AR, P>), dim3(packed * batch), dim3(kThreads), 0, st, b);
+        MR_LAUNCH((nn_argmax_kernel<AR, P>), dim3(packed * batch), dim3(kThreads), 0, st, b);
     } else {
-        hipLaunchKernelGGL((nn_argmax_kernel<AR, P>), dim3(gx, batch), dim3(kThreads), 0, st, a);
+        MR_LAUNCH((nn_argmax_kernel<AR, P>), dim3(gx, batch), dim3(kThreads), 0, st, a);
     }
 }
 
@@ -2770,7 +2835,7 @@ int launch_nn(const NNArgs& a, int ar, int batch, hipStream_t st) {
         const int gx = (int)((max_n + 31) / 32 < (1 << 20) ? (max_n + 31) / 32 : (1 << 20));
         if (gx < 1) return MR_OK;
         switch ((a.d + 15) / 16) {
-#define MR_CASE(p) case p: hipLaunchKernelGGL((recover_rows_kernel<AR_BF16, p>), dim3(gx, batch), dim3(kThreads), 0, st, a); break;
+#define MR_CASE(p) case p: MR_LAUNCH((recover_rows_kernel<AR_BF16, p>), dim3(gx, batch), dim3(kThreads), 0, st, a); break;
             MR_CASE(1) MR_CASE(2) MR_CASE(3) MR_CASE(4)
 #undef MR_CASE
             default: return MR_ERR_SHAPE;
@@ -2787,7 +2852,7 @@ enum Metric { M_INNER = 0, M_POINT = 1 };
 template <int D>
 void launch_point_t(const NNArgs& a, int batch, hipStream_t st) {
     const int g = grid_per_pair(resident_blocks<point_nn_kernel<D>>(), batch);
-    hipLaunchKernelGGL((point_nn_kernel<D>), dim3(g, batch), dim3(kThreads), 0, st, a);
+    MR_LAUNCH((point_nn_kernel<D>), dim3(g, batch), dim3(kThreads), 0, st, a);
 }
 
 // One NN search under a metric (the similarity kernel of every entry point).
@@ -2935,7 +3000,7 @@ int nn_impl(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint64_t* keys = at<uint64_t>(ws, L.keys);
     const int64_t tot = (int64_t)q->batch * n_q;
-    hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(tot)), dim3(256), 0, st, keys, tot, (uint64_t)0);
+    MR_LAUNCH(fill_u64_kernel, dim3(grid_1d(tot)), dim3(256), 0, st, keys, tot, (uint64_t)0);
     if (dev_err()) return MR_ERR_DEVICE;
     NNArgs a = nn_args(q, q->data, 1, db, db->data, 2);
     a.qsrc = q_idx ? Q_LIST : Q_ALL;
@@ -2945,7 +3010,7 @@ int nn_impl(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q
     a.keys = keys;
     a.keys_stride = n_q;
     if ((rc = launch_search(a, metric, choose_arith(q->dtype, q->d), q->batch, st))) return rc;
-    hipLaunchKernelGGL(decode_keys_kernel, dim3(grid_1d(tot)), dim3(256), 0, st, keys, tot, out_idx, out_score,
+    MR_LAUNCH(decode_keys_kernel, dim3(grid_1d(tot)), dim3(256), 0, st, keys, tot, out_idx, out_score,
                        (int)(metric == M_POINT));
     return dev_err();
 }
@@ -2987,18 +3052,18 @@ int launch_rowcol_t(const mr_map* a, const mr_map* b, uint64_t* kab, uint64_t* k
     bool rec = false;
     int rc;
     if ((rc = prof_mark(st, rec))) return rc;
-    hipLaunchKernelGGL((rowcol_argmax_kernel<P>), dim3(gx, batch), dim3(kRcThreads), 0, st, x);
+    MR_LAUNCH((rowcol_argmax_kernel<P>), dim3(gx, batch), dim3(kRcThreads), 0, st, x);
     if (dev_err()) return MR_ERR_DEVICE;
     if ((rc = prof_close(st, rec))) return rc;
     // both directions' keys -> per-bucket lists (one launch per step for both; the
     // counts were zeroed with the keys), then one launch recovering both
     const int64_t nmax = rb.n > cb.n ? rb.n : cb.n;
     const int chunks = (int)((nmax + kBucketChunk - 1) / kBucketChunk);
-    hipLaunchKernelGGL(bucket_count_kernel, dim3(chunks, batch, 2), dim3(256), 0, st, rb, cb);
-    hipLaunchKernelGGL(bucket_scan_kernel, dim3(batch, 2), dim3(1024), 0, st, rb, cb);
-    hipLaunchKernelGGL(bucket_scatter_kernel, dim3(chunks, batch, 2), dim3(256), 0, st, rb, cb);
+    MR_LAUNCH(bucket_count_kernel, dim3(chunks, batch, 2), dim3(256), 0, st, rb, cb);
+    MR_LAUNCH(bucket_scan_kernel, dim3(batch, 2), dim3(1024), 0, st, rb, cb);
+    MR_LAUNCH(bucket_scatter_kernel, dim3(chunks, batch, 2), dim3(256), 0, st, rb, cb);
     const int nbmax = rb.nbins > cb.nbins ? rb.nbins : cb.nbins;
-    hipLaunchKernelGGL((recover_rowcol_kernel<P>), dim3(nbmax < 65536 ? nbmax : 65536, batch, 2), dim3(kThreads), 0, st,
+    MR_LAUNCH((recover_rowcol_kernel<P>), dim3(nbmax < 65536 ? nbmax : 65536, batch, 2), dim3(kThreads), 0, st,
                        x, rb, cb);
     return dev_err();
 }
@@ -3042,7 +3107,7 @@ int mutual_impl(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba
         fs.r[2] = FillRange{rb.cnt, batch * (int64_t)rb.nbins, 0, 4};
         fs.r[3] = FillRange{cb.cnt, batch * (int64_t)cb.nbins, 0, 4};
     }
-    hipLaunchKernelGGL(fill_multi_kernel, dim3(grid_1d(batch * (na > nb ? na : nb)), fused ? 4 : 2), dim3(256), 0, st,
+    MR_LAUNCH(fill_multi_kernel, dim3(grid_1d(batch * (na > nb ? na : nb)), fused ? 4 : 2), dim3(256), 0, st,
                        fs);
     if (dev_err()) return MR_ERR_DEVICE;
     const void *ad = a->data, *bd = b->data;
@@ -3063,13 +3128,13 @@ int mutual_impl(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba
         r.keys_stride = nb;
         if ((rc = launch_search(r, metric, ar, batch, st))) return rc;
     }
-    hipLaunchKernelGGL(decode_keys2_kernel, dim3(grid_1d(batch * (na > nb ? na : nb)), 2), dim3(256), 0, st, kab,
+    MR_LAUNCH(decode_keys2_kernel, dim3(grid_1d(batch * (na > nb ? na : nb)), 2), dim3(256), 0, st, kab,
                        batch * na, nn_ab, kba, batch * nb, nn_ba);
     if (dev_err()) return MR_ERR_DEVICE;
     const int nblk = nblk_of(na) > 0 ? nblk_of(na) : 1;
     MutualPred pr{nn_ab, nn_ba, na, nb};
-    hipLaunchKernelGGL(compact_count_kernel<MutualPred>, dim3(nblk, batch), dim3(256), 0, st, pr, na, blk, nblk);
-    hipLaunchKernelGGL(compact_scatter_kernel<MutualPred>, dim3(nblk, batch), dim3(256), 0, st, pr, na,
+    MR_LAUNCH(compact_count_kernel<MutualPred>, dim3(nblk, batch), dim3(256), 0, st, pr, na, blk, nblk);
+    MR_LAUNCH(compact_scatter_kernel<MutualPred>, dim3(nblk, batch), dim3(256), 0, st, pr, na,
                        (const int32_t*)blk, nblk, pairs, cap, n_pairs);
     return dev_err();
 }
@@ -3107,7 +3172,7 @@ int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, 
     ia.front0 = fr[0]; ia.keys_f0 = kf[0]; ia.keys_b0 = kb[0]; ia.slot_stride = slot;
     ia.cnt0 = cnt[0]; ia.cnt1 = cnt[1];
     const int64_t init_n = n1 > ns ? n1 : ns;
-    hipLaunchKernelGGL(fast_init_kernel, dim3(grid_1d(init_n > 0 ? init_n : 1), batch), dim3(256), 0, st, ia);
+    MR_LAUNCH(fast_init_kernel, dim3(grid_1d(init_n > 0 ? init_n : 1), batch), dim3(256), 0, st, ia);
     if (dev_err()) return MR_ERR_DEVICE;
 
     if (n1 > 0 && n2 > 0 && ns > 0 && max_iters > 0) {
@@ -3134,19 +3199,19 @@ int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, 
             ca.state = state;
             ca.active = iter_active ? iter_active + t : nullptr; ca.active_stride = max_iters;
             ca.slot_stride = slot; ca.n1 = n1; ca.last = (t == max_iters - 1);
-            hipLaunchKernelGGL(fast_cycle_kernel, dim3(cyc_grid, batch), dim3(256), 0, st, ca);
+            MR_LAUNCH(fast_cycle_kernel, dim3(cyc_grid, batch), dim3(256), 0, st, ca);
             if (dev_err()) return MR_ERR_DEVICE;
         }
     } else if (iter_active && max_iters > 0) {
         // nothing to search: every iteration has no live pixel
         const int64_t n = (int64_t)batch * max_iters;
-        hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_1d(n)), dim3(256), 0, st, iter_active, n, 0);
+        MR_LAUNCH(fill_i32_kernel, dim3(grid_1d(n)), dim3(256), 0, st, iter_active, n, 0);
         if (dev_err()) return MR_ERR_DEVICE;
     }
     const int nblk = nblk_of(n1) > 0 ? nblk_of(n1) : 1;
     FastPred pr{state, n1};
-    hipLaunchKernelGGL(compact_count_kernel<FastPred>, dim3(nblk, batch), dim3(256), 0, st, pr, n1, blk, nblk);
-    hipLaunchKernelGGL(compact_scatter_kernel<FastPred>, dim3(nblk, batch), dim3(256), 0, st, pr, n1,
+    MR_LAUNCH(compact_count_kernel<FastPred>, dim3(nblk, batch), dim3(256), 0, st, pr, n1, blk, nblk);
+    MR_LAUNCH(compact_scatter_kernel<FastPred>, dim3(nblk, batch), dim3(256), 0, st, pr, n1,
                        (const int32_t*)blk, nblk, pairs, cap, n_pairs);
     return dev_err();
 }
@@ -3249,22 +3314,22 @@ int nce_forward_launch(const mr_map* a, const mr_map* b, const int32_t* gt, int6
     if (timed && (rc = prof_mark(st, rec))) return rc;
     rc = with_lse_arith(a->dtype, a->d, [&](auto ar, auto p) {
         constexpr int AR = decltype(ar)::value, P = decltype(p)::value;
-        hipLaunchKernelGGL((lse_partial_kernel<AR, P>), dim3(L.grid, batch), dim3(kThreads), 0, st, x);
+        MR_LAUNCH((lse_partial_kernel<AR, P>), dim3(L.grid, batch), dim3(kThreads), 0, st, x);
         return dev_err();
     });
     if (rc || (rc = prof_close(st, rec))) return rc;
     if (a->dtype == MR_BF16)
-        hipLaunchKernelGGL(nce_terms_kernel<uint16_t>, dim3(L.nblk, batch), dim3(256), 0, st, x);
+        MR_LAUNCH(nce_terms_kernel<uint16_t>, dim3(L.nblk, batch), dim3(256), 0, st, x);
     else
-        hipLaunchKernelGGL(nce_terms_kernel<float>, dim3(L.nblk, batch), dim3(256), 0, st, x);
+        MR_LAUNCH(nce_terms_kernel<float>, dim3(L.nblk, batch), dim3(256), 0, st, x);
     if (dev_err()) return MR_ERR_DEVICE;
-    hipLaunchKernelGGL(nce_loss_kernel, dim3(batch), dim3(256), 0, st, x);
+    MR_LAUNCH(nce_loss_kernel, dim3(batch), dim3(256), 0, st, x);
     return dev_err();
 }
 
 int fill_zero(void* p, int64_t words, hipStream_t st) {   // words of 8 bytes
     if (words <= 0) return MR_OK;
-    hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_1d(words)), dim3(256), 0, st, static_cast<uint64_t*>(p), words,
+    MR_LAUNCH(fill_u64_kernel, dim3(grid_1d(words)), dim3(256), 0, st, static_cast<uint64_t*>(p), words,
                        (uint64_t)0);
     return dev_err();
 }
@@ -3372,9 +3437,9 @@ int infonce_backward_impl(const mr_map* a, const mr_map* b, const int32_t* gt, i
     if (n_gt == 0) {   // loss 0, gradients 0
         if ((rc = fill_zero(out_loss, batch, st))) return rc;
         if (n1 > 0)
-            hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_1d(batch * n1 * d)), dim3(256), 0, st, grad_a,
+            MR_LAUNCH(fill_f32_kernel, dim3(grid_1d(batch * n1 * d)), dim3(256), 0, st, grad_a,
                                (int64_t)batch * n1 * d, 0.0f);
-        hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_1d(batch * n2 * d)), dim3(256), 0, st, grad_b,
+        MR_LAUNCH(fill_f32_kernel, dim3(grid_1d(batch * n2 * d)), dim3(256), 0, st, grad_b,
                            (int64_t)batch * n2 * d, 0.0f);
         return dev_err();
     }
@@ -3406,30 +3471,30 @@ int infonce_backward_impl(const mr_map* a, const mr_map* b, const int32_t* gt, i
         bool rec = false;
         int e;
         if ((e = prof_mark(st, rec))) return e;
-        hipLaunchKernelGGL((nce_grad_kernel<AR, P, false>), dim3(L.grid_r, batch), dim3(kThreads), 0, st, r);
+        MR_LAUNCH((nce_grad_kernel<AR, P, false>), dim3(L.grid_r, batch), dim3(kThreads), 0, st, r);
         if (dev_err()) return (int)MR_ERR_DEVICE;
         if ((e = prof_close(st, rec)) || (e = prof_mark(st, rec))) return e;
-        hipLaunchKernelGGL((nce_grad_kernel<AR, P, true>), dim3(L.grid_c, batch), dim3(kThreads), 0, st, c);
+        MR_LAUNCH((nce_grad_kernel<AR, P, true>), dim3(L.grid_c, batch), dim3(kThreads), 0, st, c);
         if (dev_err()) return (int)MR_ERR_DEVICE;
         return prof_close(st, rec);
     });
     if (rc) return rc;
-    hipLaunchKernelGGL(nce_grad_cols_finish, dim3(grid_1d(n2 * d), batch), dim3(256), 0, st, c, db);
+    MR_LAUNCH(nce_grad_cols_finish, dim3(grid_1d(n2 * d), batch), dim3(256), 0, st, c, db);
     if (dev_err()) return MR_ERR_DEVICE;
     if (a->dtype == MR_BF16)
-        hipLaunchKernelGGL(nce_grad_rows_finish<uint16_t>, dim3(grid_1d(n_gt * d), batch), dim3(256), 0, st, r,
+        MR_LAUNCH(nce_grad_rows_finish<uint16_t>, dim3(grid_1d(n_gt * d), batch), dim3(256), 0, st, r,
                            static_cast<const uint16_t*>(a->data), static_cast<const uint16_t*>(b->data), n1 * d,
                            n2 * d, (int32_t)n1, (int32_t)n2, da, db);
     else
-        hipLaunchKernelGGL(nce_grad_rows_finish<float>, dim3(grid_1d(n_gt * d), batch), dim3(256), 0, st, r,
+        MR_LAUNCH(nce_grad_rows_finish<float>, dim3(grid_1d(n_gt * d), batch), dim3(256), 0, st, r,
                            static_cast<const float*>(a->data), static_cast<const float*>(b->data), n1 * d, n2 * d,
                            (int32_t)n1, (int32_t)n2, da, db);
     if (dev_err()) return MR_ERR_DEVICE;
     const double inv_tau = 1.0 / (double)tau;
     if (n1 > 0)
-        hipLaunchKernelGGL(nce_grad_scale, dim3(grid_1d(batch * n1 * d)), dim3(256), 0, st, da, grad_a,
+        MR_LAUNCH(nce_grad_scale, dim3(grid_1d(batch * n1 * d)), dim3(256), 0, st, da, grad_a,
                            (int64_t)batch * n1 * d, inv_tau);
-    hipLaunchKernelGGL(nce_grad_scale, dim3(grid_1d(batch * n2 * d)), dim3(256), 0, st, db, grad_b,
+    MR_LAUNCH(nce_grad_scale, dim3(grid_1d(batch * n2 * d)), dim3(256), 0, st, db, grad_b,
                        (int64_t)batch * n2 * d, inv_tau);
     return dev_err();
 }
@@ -3515,87 +3580,109 @@ size_t mr_workspace_bytes(int op, const mr_map* a, const mr_map* b, int64_t n_q,
 
 int mr_infonce_forward(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau,
                        float* out_terms, double* out_loss, void* ws, size_t ws_bytes, void* stream) {
-    return infonce_impl(a, b, gt, n_gt, tau, out_terms, out_loss, ws, ws_bytes, stream);
+    const CallLog lg("mr_infonce_forward", a, b, "n_gt %lld tau %g ws %zu", (long long)n_gt, (double)tau, ws_bytes);
+    return lg.done(infonce_impl(a, b, gt, n_gt, tau, out_terms, out_loss, ws, ws_bytes, stream));
 }
 
 int mr_infonce_backward(const mr_map* a, const mr_map* b, const int32_t* gt, int64_t n_gt, float tau,
                         float* out_terms, double* out_loss, float* grad_a, float* grad_b, void* ws, size_t ws_bytes,
                         void* stream) {
-    return infonce_backward_impl(a, b, gt, n_gt, tau, out_terms, out_loss, grad_a, grad_b, ws, ws_bytes, stream);
+    const CallLog lg("mr_infonce_backward", a, b, "n_gt %lld tau %g ws %zu", (long long)n_gt, (double)tau, ws_bytes);
+    return lg.done(
+        infonce_backward_impl(a, b, gt, n_gt, tau, out_terms, out_loss, grad_a, grad_b, ws, ws_bytes, stream));
 }
 
 int mr_nn_argmax(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q, int32_t* out_idx,
                  float* out_score, void* ws, size_t ws_bytes, void* stream) {
-    return nn_impl(q, db, q_idx, n_q, out_idx, out_score, ws, ws_bytes, stream, M_INNER);
+    const CallLog lg("mr_nn_argmax", q, db, "n_q %lld%s ws %zu", (long long)n_q, q_idx ? " (listed)" : "", ws_bytes);
+    return lg.done(nn_impl(q, db, q_idx, n_q, out_idx, out_score, ws, ws_bytes, stream, M_INNER));
 }
 
 int mr_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba, int32_t* pairs, int64_t cap,
                  int64_t* n_pairs, void* ws, size_t ws_bytes, void* stream) {
-    return mutual_impl(a, b, nn_ab, nn_ba, pairs, cap, n_pairs, ws, ws_bytes, stream, M_INNER);
+    const CallLog lg("mr_mutual_nn", a, b, "cap %lld ws %zu", (long long)cap, ws_bytes);
+    return lg.done(mutual_impl(a, b, nn_ab, nn_ba, pairs, cap, n_pairs, ws, ws_bytes, stream, M_INNER));
 }
 
 int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, int32_t max_iters,
                        int32_t* pairs, int64_t cap, int64_t* n_pairs, int32_t* iter_active, void* ws,
                        size_t ws_bytes, void* stream) {
-    return fast_impl(a, b, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, ws_bytes, stream, M_INNER);
+    const CallLog lg("mr_fast_reciprocal", a, b, "stride %d offset %d iters %d cap %lld ws %zu", stride, offset,
+                     max_iters, (long long)cap, ws_bytes);
+    return lg.done(
+        fast_impl(a, b, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, ws_bytes, stream, M_INNER));
 }
 
 int mr_fast_reciprocal_static(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset,
                               int32_t max_iters, int32_t* pairs, int64_t cap, int64_t* n_pairs,
                               int32_t* iter_active, void* stream) {
-    // the same validation order as mr_fast_reciprocal, then the size check against the
-    // static buffer before anything is launched
-    int rc = validate_for(a, b, M_INNER);
-    if (rc) return rc;
-    if (stride < 1 || offset < 0 || max_iters < 0) return MR_ERR_PARAM;
-    if (!pairs || !n_pairs) return MR_ERR_NULL;
-    const int64_t ns = seed_count(a->h, a->w, stride, offset);
-    if (cap < ns) return MR_ERR_CAPACITY;
-    if (fast_layout(a, b, ns).total > kStaticScratchBytes) return MR_ERR_SCRATCH;
-    void* ws = nullptr;
-    if ((rc = static_scratch(&ws))) return rc;
-    return fast_impl(a, b, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, kStaticScratchBytes,
-                     stream, M_INNER);
+    const CallLog lg("mr_fast_reciprocal_static", a, b, "stride %d offset %d iters %d cap %lld", stride, offset,
+                     max_iters, (long long)cap);
+    return lg.done([&]() -> int {
+        // the same validation order as mr_fast_reciprocal, then the size check against
+        // the static buffer before anything is launched
+        int rc = validate_for(a, b, M_INNER);
+        if (rc) return rc;
+        if (stride < 1 || offset < 0 || max_iters < 0) return MR_ERR_PARAM;
+        if (!pairs || !n_pairs) return MR_ERR_NULL;
+        const int64_t ns = seed_count(a->h, a->w, stride, offset);
+        if (cap < ns) return MR_ERR_CAPACITY;
+        if (fast_layout(a, b, ns).total > kStaticScratchBytes) return MR_ERR_SCRATCH;
+        void* ws = nullptr;
+        if ((rc = static_scratch(&ws))) return rc;
+        return fast_impl(a, b, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, kStaticScratchBytes,
+                         stream, M_INNER);
+    }());
 }
 
 int mr_point_nn(const mr_map* q, const mr_map* db, const int32_t* q_idx, int64_t n_q, int32_t* out_idx,
                 float* out_dist2, void* ws, size_t ws_bytes, void* stream) {
-    return nn_impl(q, db, q_idx, n_q, out_idx, out_dist2, ws, ws_bytes, stream, M_POINT);
+    const CallLog lg("mr_point_nn", q, db, "n_q %lld%s ws %zu", (long long)n_q, q_idx ? " (listed)" : "", ws_bytes);
+    return lg.done(nn_impl(q, db, q_idx, n_q, out_idx, out_dist2, ws, ws_bytes, stream, M_POINT));
 }
 
 int mr_point_mutual_nn(const mr_map* a, const mr_map* b, int32_t* nn_ab, int32_t* nn_ba, int32_t* pairs,
                        int64_t cap, int64_t* n_pairs, void* ws, size_t ws_bytes, void* stream) {
-    return mutual_impl(a, b, nn_ab, nn_ba, pairs, cap, n_pairs, ws, ws_bytes, stream, M_POINT);
+    const CallLog lg("mr_point_mutual_nn", a, b, "cap %lld ws %zu", (long long)cap, ws_bytes);
+    return lg.done(mutual_impl(a, b, nn_ab, nn_ba, pairs, cap, n_pairs, ws, ws_bytes, stream, M_POINT));
 }
 
 int mr_point_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, int32_t max_iters,
                              int32_t* pairs, int64_t cap, int64_t* n_pairs, int32_t* iter_active, void* ws,
                              size_t ws_bytes, void* stream) {
-    return fast_impl(a, b, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, ws_bytes, stream, M_POINT);
+    const CallLog lg("mr_point_fast_reciprocal", a, b, "stride %d offset %d iters %d cap %lld ws %zu", stride, offset,
+                     max_iters, (long long)cap, ws_bytes);
+    return lg.done(
+        fast_impl(a, b, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, ws_bytes, stream, M_POINT));
 }
 
 int mr_fast_reciprocal_graph(const mr_map* images, const int32_t* edges, int32_t n_edges, int32_t stride,
                              int32_t offset, int32_t max_iters, int32_t* pairs, int64_t cap, int64_t* n_pairs,
                              int32_t* iter_active, void* ws, size_t ws_bytes, void* stream) {
-    int rc = validate_map(images);
-    if (rc) return rc;
-    if (!edges) return MR_ERR_NULL;
-    if (n_edges < 1 || n_edges > 65535) return MR_ERR_PARAM;
-    for (int64_t e = 0; e < 2 * (int64_t)n_edges; ++e)
-        if (edges[e] < 0 || edges[e] >= images->batch) return MR_ERR_PARAM;
-    if (stride < 1 || offset < 0 || max_iters < 0) return MR_ERR_PARAM;
-    const mr_map g = graph_map(images, n_edges);
-    const size_t at_edges = graph_edges_offset(&g, stride, offset);
-    if ((rc = check_ws(ws, ws_bytes, graph_ws_bytes(images, n_edges, stride, offset)))) return rc;
-    if (!pairs || !n_pairs) return MR_ERR_NULL;
-    if (cap < seed_count(g.h, g.w, stride, offset)) return MR_ERR_CAPACITY;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    int32_t* dev_edges = at<int32_t>(ws, at_edges);
-    if (hipMemcpyAsync(dev_edges, edges, (size_t)n_edges * 2 * sizeof(int32_t), hipMemcpyHostToDevice, st) !=
-        hipSuccess)
-        return MR_ERR_DEVICE;
-    return fast_impl(&g, &g, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, ws_bytes, stream,
-                     M_INNER, dev_edges);
+    const CallLog lg("mr_fast_reciprocal_graph", images, images,
+                     "edges %d stride %d offset %d iters %d cap %lld ws %zu", n_edges, stride, offset, max_iters,
+                     (long long)cap, ws_bytes);
+    return lg.done([&]() -> int {
+        int rc = validate_map(images);
+        if (rc) return rc;
+        if (!edges) return MR_ERR_NULL;
+        if (n_edges < 1 || n_edges > 65535) return MR_ERR_PARAM;
+        for (int64_t e = 0; e < 2 * (int64_t)n_edges; ++e)
+            if (edges[e] < 0 || edges[e] >= images->batch) return MR_ERR_PARAM;
+        if (stride < 1 || offset < 0 || max_iters < 0) return MR_ERR_PARAM;
+        const mr_map g = graph_map(images, n_edges);
+        const size_t at_edges = graph_edges_offset(&g, stride, offset);
+        if ((rc = check_ws(ws, ws_bytes, graph_ws_bytes(images, n_edges, stride, offset)))) return rc;
+        if (!pairs || !n_pairs) return MR_ERR_NULL;
+        if (cap < seed_count(g.h, g.w, stride, offset)) return MR_ERR_CAPACITY;
+        hipStream_t st = static_cast<hipStream_t>(stream);
+        int32_t* dev_edges = at<int32_t>(ws, at_edges);
+        if (hipMemcpyAsync(dev_edges, edges, (size_t)n_edges * 2 * sizeof(int32_t), hipMemcpyHostToDevice, st) !=
+            hipSuccess)
+            return MR_ERR_DEVICE;
+        return fast_impl(&g, &g, stride, offset, max_iters, pairs, cap, n_pairs, iter_active, ws, ws_bytes, stream,
+                         M_INNER, dev_edges);
+    }());
 }
 
 int mr_profile_begin(int32_t max_launches) {

@@ -294,6 +294,16 @@ int mr_profile_begin(int32_t max_launches);
 int mr_profile_end(double* total_ms, int64_t* launches);
 int mr_profile_end_each(double* total_ms, int64_t* launches, float* each_ms, int32_t cap);
 
+/* ---------------------------------------------------------------------------
+ * Launch log (no function): with the environment variable MR_LOG set to anything
+ * but "" or "0" when the library first checks it (once per process), every entry
+ * point writes to stderr one line on entry (its maps: batch x h x w x d, dtype,
+ * address; and its sizes and parameters), one line per kernel launch (kernel,
+ * the launching function's template arguments, grid, block, LDS bytes, stream)
+ * and one line with the status it returns.  Lines start with "[mr]".  Lines of
+ * calls made from several threads may interleave.  Unset, nothing is printed.
+ * --------------------------------------------------------------------------- */
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,8 @@
  *
  * Usage: abi_driver [fuzz_cases]   -- prints one summary line, exit status 0 on success;
  *        abi_driver overflow       -- a deliberate heap over-read by the library, which
- *                                     AddressSanitizer must report.
+ *                                     AddressSanitizer must report;
+ *        abi_driver log            -- valid calls of every entry point, for the launch log.
  */
 #include <math.h>
 #include <stddef.h>
@@ -504,8 +505,48 @@ static int overflow_control(void) {
     return 0;
 }
 
+/* Valid calls of every entry point with succeeding HIP doubles, for the launch log
+ * (MR_LOG): prints how many calls and launches were made, so that the log's lines can
+ * be counted against them. */
+static int log_calls(void) {
+    g_fail = 0;
+    void* o = FAKE;
+    long calls = 0;
+    const long l0 = g_launches;
+    mr_map *a = mkd(1, 40, 30, 24, MR_F32), *b = mkd(1, 36, 28, 24, MR_F32);
+    mr_map *ha = mkd(1, 40, 30, 24, MR_BF16), *hb = mkd(1, 36, 28, 24, MR_BF16);
+    mr_map *pa = mkd(1, 40, 30, 3, MR_F32), *pb = mkd(1, 36, 28, 3, MR_F32), *imgs = mkd(3, 40, 30, 24, MR_F32);
+    int rc = 0;
+#define LOGGED(call) do { rc |= (call); ++calls; } while (0)
+    LOGGED(mr_nn_argmax(a, b, NULL, 1200, o, o, FAKE_WS, mr_workspace_bytes(MR_OP_NN_ARGMAX, a, b, 1200, 1, 0), NULL));
+    LOGGED(mr_mutual_nn(a, b, o, o, o, 1008, o, FAKE_WS, mr_workspace_bytes(MR_OP_MUTUAL_NN, a, b, 0, 1, 0), NULL));
+    LOGGED(mr_mutual_nn(ha, hb, o, o, o, 1008, o, FAKE_WS, mr_workspace_bytes(MR_OP_MUTUAL_NN, ha, hb, 0, 1, 0), NULL));
+    LOGGED(mr_fast_reciprocal(a, b, 8, 4, 10, o, 20, o, o, FAKE_WS,
+                              mr_workspace_bytes(MR_OP_FAST_RECIPROCAL, a, b, 0, 8, 4), NULL));
+    LOGGED(mr_fast_reciprocal_static(a, b, 8, 4, 10, o, 20, o, o, NULL));
+    LOGGED(mr_point_nn(pa, pb, NULL, 1200, o, o, FAKE_WS, mr_workspace_bytes(MR_OP_POINT_NN, pa, pb, 1200, 1, 0), NULL));
+    LOGGED(mr_point_mutual_nn(pa, pb, o, o, o, 1008, o, FAKE_WS,
+                              mr_workspace_bytes(MR_OP_POINT_MUTUAL_NN, pa, pb, 0, 1, 0), NULL));
+    LOGGED(mr_point_fast_reciprocal(pa, pb, 8, 4, 10, o, 20, o, NULL, FAKE_WS,
+                                    mr_workspace_bytes(MR_OP_POINT_FAST_RECIPROCAL, pa, pb, 0, 8, 4), NULL));
+    int32_t* e = (int32_t*)malloc(4 * sizeof(int32_t));
+    e[0] = 0; e[1] = 1; e[2] = 2; e[3] = 0;
+    LOGGED(mr_fast_reciprocal_graph(imgs, e, 2, 8, 4, 10, o, 20, o, NULL, FAKE_WS,
+                                    mr_workspace_bytes(MR_OP_FAST_RECIPROCAL_GRAPH, imgs, imgs, 2, 8, 4), NULL));
+    LOGGED(mr_infonce_forward(ha, hb, o, 100, 0.1f, o, o, FAKE_WS, mr_workspace_bytes(MR_OP_INFONCE, ha, hb, 100, 0, 0),
+                              NULL));
+    LOGGED(mr_infonce_backward(ha, hb, o, 100, 0.1f, o, o, o, o, FAKE_WS,
+                               mr_workspace_bytes(MR_OP_INFONCE_BACKWARD, ha, hb, 100, 0, 0), NULL));
+    LOGGED(mr_nn_argmax(a, b, NULL, 7, o, NULL, FAKE_WS, 0, NULL)); /* an argument error: no launch */
+#undef LOGGED
+    printf("calls %ld launches %ld status_or %d\n", calls, g_launches - l0, rc);
+    free(e); free(a); free(b); free(ha); free(hb); free(pa); free(pb); free(imgs);
+    return 0;
+}
+
 int main(int argc, char** argv) {
     if (argc > 1 && strcmp(argv[1], "overflow") == 0) return overflow_control();
+    if (argc > 1 && strcmp(argv[1], "log") == 0) return log_calls();
     const long fuzz = argc > 1 ? atol(argv[1]) : 4000;
     long reached[2] = {0, 0};
     for (int mode = 1; mode >= 0; --mode) {

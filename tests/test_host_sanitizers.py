@@ -78,3 +78,27 @@ def test_sanitizer_sees_an_over_read(driver):
     assert r.returncode != 0
     assert "heap-buffer-overflow" in r.stderr
     assert "mr_fast_reciprocal_graph" in r.stderr
+
+
+def test_launch_log(driver):
+    """MR_LOG=1 prints each call with its maps, each launch, and each returned status;
+    without it the library prints nothing."""
+    r = _run(driver, "log")
+    assert r.returncode == 0, r.stderr[-3000:]
+    assert "[mr]" not in r.stderr
+    env_run = subprocess.run([driver, "log"], capture_output=True, text=True, timeout=120,
+                             env={**{k: v for k, v in os.environ.items() if k not in ENV_KEYS}, "MR_LOG": "1"})
+    assert env_run.returncode == 0, env_run.stderr[-3000:]
+    stats = dict(zip(env_run.stdout.split()[0::2], env_run.stdout.split()[1::2]))
+    lines = env_run.stderr.splitlines()
+    launches = [l for l in lines if l.startswith("[mr]   launch ")]
+    entries = [l for l in lines if l.startswith("[mr] mr_") and " -> " not in l]
+    statuses = [l for l in lines if l.startswith("[mr] mr_") and " -> " in l]
+    assert len(launches) == int(stats["launches"]) > 0
+    assert len(entries) == len(statuses) == int(stats["calls"])
+    # every valid call returns ok, the argument error its status; launches carry shapes
+    assert sum(l.endswith("-> 0 (ok)") for l in statuses) == len(statuses) - 1
+    assert statuses[-1].startswith("[mr] mr_nn_argmax -> 4 ")
+    assert all(" grid (" in l and " block (" in l for l in launches)
+    assert any("rowcol_argmax_kernel" in l for l in launches)
+    assert entries[0].startswith("[mr] mr_nn_argmax a 1x40x30x24 f32")
