@@ -165,7 +165,8 @@ def run_fast(p, batch_pairs, args, torch, dev, prof=True, point=False):
     act = active.cpu().numpy()
     q, flops = fast_work(act, p.N, p.d)
     return dict(ms=ms, kernel_ms=kms, launches=kn, nn_queries=q, flops=flops, each=each,
-                active=act[0].tolist(), matches=[int(x) for x in n_pairs.cpu()], batch=A.shape[0])
+                active=act[0].tolist(), matches=[int(x) for x in n_pairs.cpu()], batch=A.shape[0],
+                pairs0=pairs[0, :int(n_pairs[0])].cpu().numpy())
 
 
 def rounds_roofline(r, N, d, elem_bytes, peak_tflops):
@@ -274,7 +275,10 @@ def roofline_lse(scores_per_step, d, steps, kernel_ms, launches):
                      "frac": round(flops / PEAK_TFLOPS["bf16"], 4)}}
 
 
-def cpu_baseline(p):
+def cpu_baseline(p, gpu=None):
+    """The oracle timed on the host on this pair (and per core on it and the 64x48 pair);
+    with `gpu` (the library's result on the same pair), also the pass/fail count of each
+    parity rule of the fast scheme between the two."""
     import oracle
     import workloads
     threads = oracle.default_threads()
@@ -295,6 +299,17 @@ def cpu_baseline(p):
         per_core[name] = {"pairs_per_s": round(1.0 / dt1, 4), "seconds": round(dt1, 3), "threads": 1,
                           "nn_queries_per_s": round(r1["nn_queries"] / dt1, 1)}
     out["per_core"] = per_core
+    if gpu is not None:
+        from tests.checks import fast_rule_counts
+        t = time.perf_counter()
+        rules, summary = fast_rule_counts(gpu["pairs0"], r, p.D1, p.D2, "f32", nthreads=threads,
+                                          gpu_active=gpu["active"])
+        for v in rules.values():
+            if not v["failed"]:
+                del v["examples"]
+        out["parity_vs_gpu"] = {"workload": "pair-512x384-f32", "rules": rules, "summary": summary,
+                                "all_passed": all(v["failed"] == 0 for v in rules.values()),
+                                "seconds": round(time.perf_counter() - t, 2)}
     return out
 
 
@@ -532,7 +547,7 @@ def main():
 
     if not args.no_cpu:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(p)
+        out["cpu_baseline"] = cpu_baseline(p, gpu=r)
         if not args.main_only:
             out["cpu_baseline"]["other_samples"] = cpu_samples()
     print(json.dumps(out), flush=True)

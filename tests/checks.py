@@ -87,43 +87,100 @@ def check_one_to_one_sorted(pairs):
     assert len(np.unique(v)) == len(v), "a pixel of image 2 is matched twice"
 
 
+def _reciprocal_ok(pairs, A, B, dtype, nthreads=None, metric=0):
+    """Rule (ii) per pair: (forward ok, backward ok) boolean arrays."""
+    u, v = pairs[:, 0], pairs[:, 1]
+    _, f1, _ = oracle.nn_rows(A, u, B, nthreads, metric=metric)
+    _, b1, _ = oracle.nn_rows(B, v, A, nthreads, metric=metric)
+    s = oracle.similarity_pairs(A, B, u, v, metric=metric)
+    return _near_enough(s, f1, dtype, metric), _near_enough(s, b1, dtype, metric)
+
+
 def check_reciprocal(pairs, A, B, dtype, nthreads=None, metric=0):
     """Rule (ii) for every listed GPU pair."""
     pairs = np.asarray(pairs).reshape(-1, 2)
     if len(pairs) == 0:
         return
-    u, v = pairs[:, 0], pairs[:, 1]
-    _, f1, _ = oracle.nn_rows(A, u, B, nthreads, metric=metric)
-    _, b1, _ = oracle.nn_rows(B, v, A, nthreads, metric=metric)
-    s = oracle.similarity_pairs(A, B, u, v, metric=metric)
-    assert _near_enough(s, f1, dtype, metric).all(), "a GPU pair is not a forward NN within tolerance"
-    assert _near_enough(s, b1, dtype, metric).all(), "a GPU pair is not a backward NN within tolerance"
+    fwd, bwd = _reciprocal_ok(pairs, A, B, dtype, nthreads, metric)
+    assert fwd.all(), "a GPU pair is not a forward NN within tolerance"
+    assert bwd.all(), "a GPU pair is not a backward NN within tolerance"
+
+
+def fast_rule_counts(gpu_pairs, orc, A, B, dtype, nthreads=None, metric=0, gpu_active=None):
+    """Rules (i)-(v) counted rather than asserted, for reports.  For each rule: how many
+    items pass and fail, and up to three failing items.  Items are oracle clean pairs
+    (i), GPU pairs (ii), steps between consecutive GPU pairs (iii, ascending u), GPU
+    pairs (iii, v used once), pairs of either set (iv, set equality), iterations (iv,
+    live counts) and the one bound each of (v).  A rule that does not apply (iv when
+    some chain is unclean; the live counts when none are given) counts 0 and 0."""
+    gpu_pairs = np.asarray(gpu_pairs).reshape(-1, 2)
+    gset = {(int(a), int(b)) for a, b in gpu_pairs}
+    oset = {(int(a), int(b)) for a, b in orc["pairs"]}
+    clean = {(int(a), int(b)) for (a, b), c in zip(orc["pairs"], orc["clean"]) if c}
+    unclean = int((np.asarray(orc["seed_clean"]) == 0).sum())
+    gpu_only, oracle_only = gset - oset, oset - gset
+    rules = {}
+
+    def put(name, passed, failed_items):
+        failed_items = sorted(failed_items)
+        rules[name] = dict(passed=int(passed), failed=len(failed_items),
+                           examples=[[int(x) for x in np.atleast_1d(f)] for f in failed_items[:3]])
+
+    u, v = gpu_pairs[:, 0], gpu_pairs[:, 1]
+    steps = np.nonzero(np.diff(u) <= 0)[0] + 1
+    put("iii_ascending_in_u", max(len(u) - 1, 0) - len(steps), [(int(u[k - 1]), int(u[k])) for k in steps])
+    vals, cnt = np.unique(v, return_counts=True)
+    put("iii_v_used_once", len(v) - int((cnt - 1).sum()), [int(x) for x in vals[cnt > 1]])
+    missing = clean - gset
+    put("i_clean_pairs_found", len(clean) - len(missing), missing)
+    if len(gpu_pairs):
+        fwd, bwd = _reciprocal_ok(gpu_pairs, A, B, dtype, nthreads, metric)
+        ok = fwd & bwd
+        put("ii_eps_reciprocal", int(ok.sum()), [tuple(map(int, gpu_pairs[k])) for k in np.nonzero(~ok)[0]])
+    else:
+        put("ii_eps_reciprocal", 0, [])
+    if unclean == 0:
+        put("iv_equal_sets", len(gset & oset), gpu_only | oracle_only)
+        if gpu_active is not None:
+            ga = np.asarray(gpu_active).reshape(-1)[:len(orc["fresh"])].tolist()
+            fr = orc["fresh"].tolist()
+            put("iv_live_counts", sum(a == b for a, b in zip(ga, fr)),
+                [(t, a, b) for t, (a, b) in enumerate(zip(ga, fr)) if a != b])
+        else:
+            put("iv_live_counts", 0, [])
+    else:
+        put("iv_equal_sets", 0, [])
+        put("iv_live_counts", 0, [])
+    put("v_gpu_only_within_unclean", int(len(gpu_only) <= unclean),
+        [] if len(gpu_only) <= unclean else [(len(gpu_only), unclean)])
+    put("v_oracle_only_within_unclean", int(len(oracle_only) <= unclean),
+        [] if len(oracle_only) <= unclean else [(len(oracle_only), unclean)])
+    summary = dict(gpu=len(gset), oracle=len(oset), clean=len(clean), common=len(gset & oset),
+                   gpu_only=len(gpu_only), oracle_only=len(oracle_only), unclean_seeds=unclean)
+    return rules, summary
 
 
 def check_fast(gpu_pairs, orc, A, B, dtype, nthreads=None, metric=0, gpu_active=None):
     """Rules (i)-(v) against a full oracle run `orc` (dict from oracle.fast);
     gpu_active: the GPU's live count per iteration, or None."""
-    gpu_pairs = np.asarray(gpu_pairs).reshape(-1, 2)
-    check_one_to_one_sorted(gpu_pairs)
-    gset = {(int(a), int(b)) for a, b in gpu_pairs}
-    oset = {(int(a), int(b)) for a, b in orc["pairs"]}
-    clean = {(int(a), int(b)) for (a, b), c in zip(orc["pairs"], orc["clean"]) if c}
-    missing = clean - gset
-    assert not missing, f"{len(missing)} clean oracle pairs missing, e.g. {sorted(missing)[:3]}"
-    check_reciprocal(gpu_pairs, A, B, dtype, nthreads, metric)
-    unclean = int((np.asarray(orc["seed_clean"]) == 0).sum())
-    gpu_only, oracle_only = gset - oset, oset - gset
-    if unclean == 0:
-        assert not gpu_only and not oracle_only, \
-            f"every chain is clean, yet {len(gpu_only)} GPU-only and {len(oracle_only)} oracle-only pairs, " \
-            f"e.g. {sorted(gpu_only)[:3]} {sorted(oracle_only)[:3]}"
-        if gpu_active is not None:
-            ga = np.asarray(gpu_active).reshape(-1)[:len(orc["fresh"])].tolist()
-            assert ga == orc["fresh"].tolist(), f"live counts {ga} != oracle first visits {orc['fresh'].tolist()}"
-    assert len(gpu_only) <= unclean, f"{len(gpu_only)} GPU-only pairs but only {unclean} unclean chains"
-    assert len(oracle_only) <= unclean, f"{len(oracle_only)} oracle-only pairs but only {unclean} unclean chains"
-    return dict(gpu=len(gset), oracle=len(oset), clean=len(clean), common=len(gset & oset),
-                gpu_only=len(gpu_only), oracle_only=len(oracle_only), unclean_seeds=unclean)
+    R, summary = fast_rule_counts(gpu_pairs, orc, A, B, dtype, nthreads, metric, gpu_active)
+    assert not R["iii_ascending_in_u"]["failed"], "pairs not strictly ascending in u"
+    assert not R["iii_v_used_once"]["failed"], "a pixel of image 2 is matched twice"
+    r = R["i_clean_pairs_found"]
+    assert not r["failed"], f"{r['failed']} clean oracle pairs missing, e.g. {r['examples']}"
+    r = R["ii_eps_reciprocal"]
+    assert not r["failed"], f"{r['failed']} GPU pairs not an NN within tolerance both ways, e.g. {r['examples']}"
+    r = R["iv_equal_sets"]
+    assert not r["failed"], \
+        f"every chain is clean, yet {summary['gpu_only']} GPU-only and {summary['oracle_only']} oracle-only " \
+        f"pairs, e.g. {r['examples']}"
+    r = R["iv_live_counts"]
+    assert not r["failed"], f"live counts differ from the oracle's first visits at (t, gpu, oracle) {r['examples']}"
+    assert not R["v_gpu_only_within_unclean"]["failed"], \
+        f"{summary['gpu_only']} GPU-only pairs but only {summary['unclean_seeds']} unclean chains"
+    assert not R["v_oracle_only_within_unclean"]["failed"], \
+        f"{summary['oracle_only']} oracle-only pairs but only {summary['unclean_seeds']} unclean chains"
+    return summary
 
 
 def oracle_chains(A, B, seeds, T, nthreads=None, eps=None, metric=0):

@@ -76,3 +76,37 @@ def test_unclean_chains_bound_the_difference():
     assert len(set(big) - set(map(tuple, orc["pairs"].tolist()))) > unclean
     with pytest.raises(AssertionError, match="GPU-only pairs"):
         checks.check_fast(np.array(big), orc, p.D1, p.D2, "f32")
+
+
+def test_rule_counts_report_each_planted_mistake():
+    """The counted form of the rules (used in the benchmark's report) counts every item:
+    all pass on the oracle's own output, and each planted mistake shows up in its rule
+    with the right number of failing items."""
+    p = _pair()
+    orc = oracle.fast(p.D1, p.H, p.W, p.D2, 4, 2, 10)
+    n = len(orc["pairs"])
+    R, s = checks.fast_rule_counts(orc["pairs"], orc, p.D1, p.D2, "f32", gpu_active=orc["fresh"])
+    assert all(r["failed"] == 0 for r in R.values()), R
+    assert R["i_clean_pairs_found"]["passed"] == R["ii_eps_reciprocal"]["passed"] == n
+    assert R["iv_equal_sets"]["passed"] == n and R["iv_live_counts"]["passed"] == 10
+    assert R["iii_ascending_in_u"]["passed"] == n - 1 and R["iii_v_used_once"]["passed"] == n
+    # two pairs dropped: (i) and (iv) fail by two, nothing else
+    R, _ = checks.fast_rule_counts(orc["pairs"][2:], orc, p.D1, p.D2, "f32")
+    assert R["i_clean_pairs_found"]["failed"] == 2 and R["iv_equal_sets"]["failed"] == 2
+    assert R["i_clean_pairs_found"]["examples"] == sorted(map(list, orc["pairs"][:2].tolist()))
+    assert R["ii_eps_reciprocal"]["failed"] == 0 and R["iv_live_counts"]["failed"] == 0
+    # a pair that is not mutual, placed out of order, and reusing a pixel of image 2
+    v0 = int(orc["pairs"][0, 1])
+    used_u = set(orc["pairs"][:, 0].tolist())
+    free_u = next(x for x in range(p.N) if x not in used_u)   # below the last u: out of order
+    assert free_u < orc["pairs"][-1, 0]
+    bad = np.concatenate([orc["pairs"], [[free_u, v0]]])
+    R, _ = checks.fast_rule_counts(bad, orc, p.D1, p.D2, "f32")
+    assert R["iii_v_used_once"]["failed"] == 1 and R["iii_v_used_once"]["examples"] == [[v0]]
+    assert R["iii_ascending_in_u"]["failed"] == 1
+    assert R["ii_eps_reciprocal"]["failed"] >= 1
+    # live counts one iteration off: the iterations whose counts differ
+    shifted = np.concatenate([orc["fresh"][:1], orc["fresh"][:-1]])
+    R, _ = checks.fast_rule_counts(orc["pairs"], orc, p.D1, p.D2, "f32", gpu_active=shifted)
+    diff = int((shifted != orc["fresh"]).sum())
+    assert diff > 0 and R["iv_live_counts"]["failed"] == diff
