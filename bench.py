@@ -83,12 +83,14 @@ def dev_maps(p, torch, dev):
     return A.to(dev).unsqueeze(0), B.to(dev).unsqueeze(0)
 
 
-def time_steps(fn, steps, warmup, torch, prof_launches=0, each=None):
+def time_steps(fn, steps, warmup, torch, prof_launches=0, each=None, queries=None):
     """Warm up, then time exactly `steps` calls between two synchronisations with nothing
     else on the stream.  With prof_launches, the same steps run once more with the
     library's per-launch hipEvents on (they cost a few microseconds per launch, so they
     stay out of the pass that gives the step time) for the similarity kernel's average
-    launch duration.  Returns (ms per step, summed similarity-kernel ms, launches timed)."""
+    launch duration; `each` receives every launch's milliseconds and `queries` every
+    search launch's query count (summed over the batch).  Returns (ms per step, summed
+    similarity-kernel ms, launches timed)."""
     import dense_grounded_image_amd as mr
     for _ in range(warmup):
         fn()
@@ -107,7 +109,12 @@ def time_steps(fn, steps, warmup, torch, prof_launches=0, each=None):
         for _ in range(steps):
             fn()
         torch.cuda.synchronize()
-        if each is None:
+        if queries is not None:
+            kms, kn, per, qs = mr.profile_end_queries(prof_launches)
+            queries.extend(qs)
+            if each is not None:
+                each.extend(per)
+        elif each is None:
             kms, kn = mr.profile_end()
         else:
             kms, kn, per = mr.profile_end_each(prof_launches)
@@ -143,11 +150,18 @@ def oracle_host():
     return cpu, os.cpu_count() or 0
 
 
-def fast_work(active, N, d):
-    """Algorithmic work of one fast-scheme call: every live pixel is one forward and one
-    backward NN query, each 2*N*d flops against the other map."""
-    q = 2 * int(active.sum())
-    return q, 2.0 * N * d * q
+def fast_work(searched, N, d):
+    """Algorithmic work of one fast-scheme call: every NN query the call searched costs
+    2*N*d flops against the other map.  A call searches the forward NN of each live
+    pixel and the backward NN of each pixel of image 2 it lands on, once per call (an
+    answer already found is reused), so `searched` comes from the library's per-launch
+    query counts, not from the live counts."""
+    return searched, 2.0 * N * d * searched
+
+
+def searched_per_step(queries, steps):
+    """NN queries the search launches ran per call (uncounted launches excluded)."""
+    return sum(q for q in queries if q >= 0) / steps
 
 
 def run_fast(p, batch_pairs, args, torch, dev, prof=True, point=False):
@@ -158,13 +172,15 @@ def run_fast(p, batch_pairs, args, torch, dev, prof=True, point=False):
         A, B = batch_pairs
     f = mr.FastReciprocal(A, B, p.stride, p.offset, p.max_iters, point=point)
     launches = 2 * p.max_iters * args.steps
-    each = []
-    ms, kms, kn = time_steps(lambda: f(A, B), args.steps, args.warmup, torch, launches if prof else 0, each)
+    each, queries = [], []
+    ms, kms, kn = time_steps(lambda: f(A, B), args.steps, args.warmup, torch, launches if prof else 0, each,
+                             queries)
     pairs, n_pairs, active = f(A, B)
     torch.cuda.synchronize()
     act = active.cpu().numpy()
-    q, flops = fast_work(act, p.N, p.d)
-    return dict(ms=ms, kernel_ms=kms, launches=kn, nn_queries=q, flops=flops, each=each,
+    q, flops = fast_work(searched_per_step(queries, args.steps), p.N, p.d)
+    return dict(ms=ms, kernel_ms=kms, launches=kn, nn_queries=q, flops=flops, each=each, queries=queries,
+                nn_answers=2 * int(act.sum()),
                 active=act[0].tolist(), matches=[int(x) for x in n_pairs.cpu()], batch=A.shape[0],
                 pairs0=pairs[0, :int(n_pairs[0])].cpu().numpy())
 
@@ -172,24 +188,28 @@ def run_fast(p, batch_pairs, args, torch, dev, prof=True, point=False):
 def rounds_roofline(r, N, d, elem_bytes, peak_tflops):
     """Per round of the fast scheme: its two similarity launches' measured time (averaged
     over the timed calls) against the round's lower bound max(flops / matrix peak,
-    bytes / HBM), flops 4*|U_t|*N*d and bytes two map reads of N*d elements; overall,
-    the summed bounds over the summed kernel time.  peak_tflops is the ceiling of the
-    arithmetic the kernel executes (for fp32 maps the split ceiling, bf16 peak / 6)."""
-    each, act = r["each"], r["active"]
+    bytes / HBM), flops 2*N*d per query the two launches searched (the forward NN of the
+    |U_t| live pixels, the backward NN of the landing pixels not searched before) and
+    bytes two map reads of N*d elements; overall, the summed bounds over the summed
+    kernel time.  peak_tflops is the ceiling of the arithmetic the kernel executes (for
+    fp32 maps the split ceiling, bf16 peak / 6)."""
+    each, act, qs = r["each"], r["active"], r["queries"]
     per_call = 2 * len(act)
-    if not each or len(each) % per_call:
+    if not each or len(each) % per_call or len(qs) != len(each):
         return None
     calls = len(each) // per_call
     out, lb_sum, t_sum = [], 0.0, 0.0
     for t, u in enumerate(act):
         ms = sum(each[c * per_call + 2 * t] + each[c * per_call + 2 * t + 1] for c in range(calls)) / calls
-        fl = 4.0 * u * N * d
+        qf = sum(qs[c * per_call + 2 * t] for c in range(calls)) / calls
+        qb = sum(qs[c * per_call + 2 * t + 1] for c in range(calls)) / calls
+        fl = 2.0 * (qf + qb) * N * d
         by = 2.0 * N * d * elem_bytes if u else 0.0
         lb = max(fl / (peak_tflops * 1e12), by / (PEAK_HBM_GBPS * 1e9)) * 1e3
         lb_sum += lb
         t_sum += ms
-        out.append({"t": t, "active": int(u), "ms": round(ms, 4), "lb_ms": round(lb, 4),
-                    "frac": round(lb / ms, 4) if ms > 0 else None})
+        out.append({"t": t, "active": int(u), "backward_searched": int(round(qb)), "ms": round(ms, 4),
+                    "lb_ms": round(lb, 4), "frac": round(lb / ms, 4) if ms > 0 else None})
     return {"rounds": out, "lb_ms": round(lb_sum, 4), "kernel_ms": round(t_sum, 4),
             "frac": round(lb_sum / t_sum, 4) if t_sum else None}
 
@@ -438,11 +458,11 @@ def other_graph(args, torch, dev):
     print("bench: collection ready", file=sys.stderr, flush=True)
     g = mr.FastReciprocalGraph(imgs, edges, 8, 4, 10)
     steps, warm = max(2, args.steps // 10), 1
-    ms, kms, kn = time_steps(lambda: g(imgs), steps, warm, torch, 20 * steps)
+    queries = []
+    ms, kms, kn = time_steps(lambda: g(imgs), steps, warm, torch, 20 * steps, queries=queries)
     _, npairs, active = g(imgs)
     torch.cuda.synchronize()
-    act = active.cpu().numpy()
-    q, flops = fast_work(act, 512 * 384, 24)
+    q, flops = fast_work(searched_per_step(queries, steps), 512 * 384, 24)
     return {"pairs_per_s": round(len(edges) * 1000.0 / ms, 2), "ms_per_call": round(ms, 3),
             "edges": int(len(edges)), "images": n, "images_bytes": int(imgs.numel() * 4),
             "nn_queries_per_s": round(q * 1000.0 / ms, 1), "matches_total": int(npairs.sum()),
@@ -531,7 +551,12 @@ def main():
                                "seed stride 8 offset 4 (3072 seeds), 10 iterations",
                    "H": 512, "W": 384, "d": 24, "batch": 1, "stride": 8, "offset": 4, "max_iters": 10},
         "nn_queries_per_s": round(r["nn_queries"] * 1000.0 / r["ms"], 1),
-        "nn_queries_per_step": r["nn_queries"], "iter_active": r["active"], "matches": r["matches"][0],
+        "nn_queries_per_step": r["nn_queries"],
+        "nn_answers_per_step": r["nn_answers"],
+        "nn_queries_note": "queries searched per call: the forward NN of every live pixel and the backward "
+                           "NN of each landing pixel once per call; nn_answers counts both NN of every live "
+                           "pixel, backward ones found earlier in the call reused",
+        "iter_active": r["active"], "matches": r["matches"][0],
         "roofline": roofline(r["flops"], args.steps, r["kernel_ms"], r["launches"], "f32",
                              measured_traffic("nn_argmax_pair512x384_f32_traffic.json")),
         "step_mfma_frac": round(r["flops"] / (r["ms"] * 1e-3) / 1e12 / PEAK_SPLIT_TFLOPS, 4),

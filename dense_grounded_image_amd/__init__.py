@@ -31,7 +31,7 @@ STATUS = {0: "MR_OK", 1: "MR_ERR_NULL", 2: "MR_ERR_SHAPE", 3: "MR_ERR_DTYPE", 4:
 EXPORTS = ("mr_workspace_bytes", "mr_status_str", "mr_seed_count", "mr_nn_argmax", "mr_mutual_nn",
            "mr_fast_reciprocal", "mr_fast_reciprocal_static", "mr_fast_reciprocal_graph", "mr_point_nn", "mr_point_mutual_nn",
            "mr_point_fast_reciprocal", "mr_infonce_forward", "mr_infonce_backward",
-           "mr_profile_begin", "mr_profile_end", "mr_profile_end_each")
+           "mr_profile_begin", "mr_profile_end", "mr_profile_end_each", "mr_profile_end_queries")
 
 
 class MrMap(ctypes.Structure):
@@ -90,6 +90,8 @@ def load_library(path: str = LIB_PATH):
     lib.mr_profile_end.restype = ctypes.c_int
     lib.mr_profile_end_each.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), P, i32]
     lib.mr_profile_end_each.restype = ctypes.c_int
+    lib.mr_profile_end_queries.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i64), P, P, i32]
+    lib.mr_profile_end_queries.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -425,3 +427,16 @@ def profile_end_each(cap: int):
     each = (ctypes.c_float * max(1, cap))()
     _check("mr_profile_end_each", load_library().mr_profile_end_each(ctypes.byref(ms), ctypes.byref(n), each, cap))
     return ms.value, n.value, [float(x) for x in each[:min(cap, n.value)]]
+
+
+def profile_end_queries(cap: int):
+    """Returns (summed milliseconds, launches timed, each launch's milliseconds, each
+    launch's query count summed over the batch (-1: not counted)), at most cap of each."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    each = (ctypes.c_float * max(1, cap))()
+    qs = (ctypes.c_int64 * max(1, cap))()
+    _check("mr_profile_end_queries",
+           load_library().mr_profile_end_queries(ctypes.byref(ms), ctypes.byref(n), each, qs, cap))
+    k = min(cap, n.value)
+    return ms.value, n.value, [float(x) for x in each[:k]], [int(x) for x in qs[:k]]

@@ -51,7 +51,7 @@
 // copy per GPU, held until the process ends.  Host code never passes this name to a
 // kernel or a copy (on the host it is only a stand-in for the symbol): the device
 // address comes from hipGetSymbolAddress, per device.
-constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
 static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 namespace {
@@ -371,7 +371,7 @@ template <int AR, int P> constexpr int qt_of() { return AR == AR_X3 && P > 9 ? 2
 
 // ---------------------------------------------------------------------------- NN kernel
 
-enum QuerySource { Q_ALL = 0, Q_LIST = 1, Q_KEYS = 2 };
+enum QuerySource { Q_ALL = 0, Q_LIST = 1 };
 
 struct NNArgs {
     const void* qmap;        // [batch][nq_rows][d]
@@ -382,7 +382,7 @@ struct NNArgs {
     int32_t ndb;
     int32_t d;
     int32_t qsrc;            // QuerySource
-    const void* qlist;       // int32 rows (Q_LIST) or uint64 keys (Q_KEYS), [batch][qlist_stride]
+    const int32_t* qlist;    // int32 rows (Q_LIST), [batch][qlist_stride]
     int64_t qlist_stride;
     const int32_t* dev_count;  // per-pair query count on the device, or NULL
     int64_t count_stride;
@@ -1109,10 +1109,7 @@ void nn_argmax_kernel(NNArgs a) {
                 const int qp = (tb + j * ts) * 32 + jl;
                 int64_t row = qp;
                 bool valid = qp < n;
-                if (valid && a.qsrc == Q_LIST)
-                    row = static_cast<const int32_t*>(a.qlist)[pair * a.qlist_stride + qp];
-                else if (valid && a.qsrc == Q_KEYS)
-                    row = key_row(static_cast<const uint64_t*>(a.qlist)[pair * a.qlist_stride + qp]);
+                if (valid && a.qsrc == Q_LIST) row = a.qlist[pair * a.qlist_stride + qp];
                 valid = valid && row >= 0 && row < a.nq_rows;
                 if constexpr (AR == AR_X3)
                     q[j].load_f32(static_cast<const float*>(qbase) + (valid ? row : 0) * a.d, valid, h, a.q_role);
@@ -1282,10 +1279,7 @@ __global__ __launch_bounds__(kThreads) void recover_rows_kernel(NNArgs a) {
         const int qp = g * 32 + jl;
         int64_t row = qp;
         bool valid = qp < n;
-        if (valid && a.qsrc == Q_LIST)
-            row = static_cast<const int32_t*>(a.qlist)[pair * a.qlist_stride + qp];
-        else if (valid && a.qsrc == Q_KEYS)
-            row = key_row(static_cast<const uint64_t*>(a.qlist)[pair * a.qlist_stride + qp]);
+        if (valid && a.qsrc == Q_LIST) row = a.qlist[pair * a.qlist_stride + qp];
         valid = valid && row >= 0 && row < a.nq_rows;
         Operand<AR, P> q;
         q.load(qbase, valid ? row : 0, valid, h, a.d, a.q_role);
@@ -1924,10 +1918,7 @@ __global__ __launch_bounds__(kThreads) void point_nn_kernel(NNArgs a) {
             qp[j] = qb * QW + j * 64 + lane;
             int64_t row = qp[j];
             bool valid = qp[j] < n;
-            if (valid && a.qsrc == Q_LIST)
-                row = static_cast<const int32_t*>(a.qlist)[pair * a.qlist_stride + qp[j]];
-            else if (valid && a.qsrc == Q_KEYS)
-                row = key_row(static_cast<const uint64_t*>(a.qlist)[pair * a.qlist_stride + qp[j]]);
+            if (valid && a.qsrc == Q_LIST) row = a.qlist[pair * a.qlist_stride + qp[j]];
             valid = valid && row >= 0 && row < a.nq_rows;
 #pragma unroll
             for (int c = 0; c < D; ++c) x[j][c] = valid ? qbase[row * D + c] : 0.0f;
@@ -2032,37 +2023,95 @@ __global__ void decode_keys_kernel(const uint64_t* keys, int64_t n, int32_t* idx
 
 // Fast scheme set-up: per pixel of image a, state = -2 for seeds (live), -1 otherwise;
 // seed k (row-major on the grid) goes to frontier slot k; counters and round-0 keys reset.
+// Memo of the backward NN of the fast scheme: one int32 per pixel v of image 2 (per
+// pair).  The NN of a pixel never changes, and a pixel of image 2 is often reached
+// again in a later iteration (a chain that converges there lands on it twice), so each
+// pixel's backward NN is searched once per call.  Rows and list entries are below 2^28.
+constexpr int32_t kMemoRow = 0x0FFFFFFF;
+constexpr int32_t kMemoFinal = 0x20000000;    // | u: NN(b[v], a) = u, found in an earlier iteration
+constexpr int32_t kMemoPending = 0x40000000;  // | e: searched in this iteration, entry e of the list
+constexpr int32_t kMemoClaimed = 0x7FFFFFFF;  // taken by this iteration's gather, entry not yet written
+                                              // (0: never searched)
+
 struct InitArgs {
     int32_t* state; int64_t n1; int32_t w;
     int32_t stride, offset, nx, nseeds;
     int32_t* front0; uint64_t* keys_f0; uint64_t* keys_b0; int64_t slot_stride;
     int32_t* cnt0; int32_t* cnt1;
+    int32_t* memo; int64_t n2; int32_t* bcnt0; int32_t* bcnt1;
 };
 
 __global__ void fast_init_kernel(InitArgs a) {
     const int pair = blockIdx.y;
-    for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < a.n1;
+    const int64_t n = a.n1 > a.n2 ? a.n1 : a.n2;
+    for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < n;
          p += (int64_t)gridDim.x * blockDim.x) {
-        const int32_t y = (int32_t)(p / a.w), x = (int32_t)(p - (int64_t)y * a.w);
-        const bool seed = y >= a.offset && x >= a.offset && (y - a.offset) % a.stride == 0 &&
-                          (x - a.offset) % a.stride == 0;
-        a.state[pair * a.n1 + p] = seed ? -2 : -1;
-        if (seed) {
-            const int64_t k = (int64_t)((y - a.offset) / a.stride) * a.nx + (x - a.offset) / a.stride;
-            a.front0[pair * a.slot_stride + k] = (int32_t)p;
+        if (p < a.n1) {
+            const int32_t y = (int32_t)(p / a.w), x = (int32_t)(p - (int64_t)y * a.w);
+            const bool seed = y >= a.offset && x >= a.offset && (y - a.offset) % a.stride == 0 &&
+                              (x - a.offset) % a.stride == 0;
+            a.state[pair * a.n1 + p] = seed ? -2 : -1;
+            if (seed) {
+                const int64_t k = (int64_t)((y - a.offset) / a.stride) * a.nx + (x - a.offset) / a.stride;
+                a.front0[pair * a.slot_stride + k] = (int32_t)p;
+            }
         }
         if (p < a.nseeds) {
             a.keys_f0[pair * a.slot_stride + p] = 0;
             a.keys_b0[pair * a.slot_stride + p] = 0;
         }
+        if (p < a.n2) a.memo[pair * a.n2 + p] = 0;
     }
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         a.cnt0[pair] = a.nseeds;
         a.cnt1[pair] = 0;
+        a.bcnt0[pair] = 0;
+        a.bcnt1[pair] = 0;
     }
 }
 
-// One reciprocity check per live pixel u: v = NN(a[u], b), u' = NN(b[v], a).
+// The backward queries of one iteration: the landing pixels v = NN(a[u], b) of the live
+// pixels whose backward NN is not known yet, each once (a CAS on the memo claims v;
+// ballot + prefix sum give each wave one atomic on the list count).  The list counts
+// alternate between two per-pair counters: iteration t appends to bcnt and clears
+// bcnt_next for iteration t + 1.
+struct GatherArgs {
+    const uint64_t* keys_f; const int32_t* cnt; int32_t* memo; int64_t n2;
+    int32_t* blist; int32_t* bcnt; int32_t* bcnt_next; int64_t slot_stride;
+};
+
+__global__ __launch_bounds__(256) void fast_gather_kernel(GatherArgs a) {
+    const int pair = blockIdx.y;
+    const int n = a.cnt[pair];
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.bcnt_next[pair] = 0;
+    const int lane = threadIdx.x & 63;
+    int32_t* memo = a.memo + pair * a.n2;
+    for (int64_t k0 = (int64_t)blockIdx.x * blockDim.x; k0 < n; k0 += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t k = k0 + threadIdx.x;
+        int32_t v = -1;
+        bool push = false;
+        if (k < n) {
+            v = key_row(a.keys_f[pair * a.slot_stride + k]);
+            push = v >= 0 && v < a.n2 && memo[v] == 0 && atomicCAS(&memo[v], 0, kMemoClaimed) == 0;
+        }
+        const uint64_t mask = __ballot(push);
+        if (mask) {
+            const int leader = __ffsll((unsigned long long)mask) - 1;
+            int at = 0;
+            if (lane == leader) at = atomicAdd(&a.bcnt[pair], (int)__popcll(mask));
+            at = __shfl(at, leader);
+            if (push) {
+                const int e = at + (int)__popcll(mask & __lanemask_lt());
+                a.blist[pair * a.slot_stride + e] = v;
+                memo[v] = kMemoPending | e;
+            }
+        }
+    }
+}
+
+// One reciprocity check per live pixel u: v = NN(a[u], b), u' = NN(b[v], a), with u'
+// from the memo (an earlier iteration) or from this iteration's backward keys (the
+// memo's list entry; the first thread to read it records u' in the memo).
 // u' == u: keep (u, v).  Otherwise u' becomes live next iteration if nobody has
 // been there (state -1); ballot + prefix sum give each wave one atomic.
 // The frontier counts rotate through three per-pair counters: iteration t reads
@@ -2075,6 +2124,7 @@ struct CycleArgs {
     const int32_t* cnt; int32_t* cnt_next; int32_t* cnt_after; int32_t* state;
     int32_t* active; int64_t active_stride;   // NULL, or this iteration's entry of [batch][max_iters]
     int64_t slot_stride; int64_t n1; int32_t last;
+    int32_t* memo; int64_t n2;
 };
 
 __global__ __launch_bounds__(256) void fast_cycle_kernel(CycleArgs a) {
@@ -2093,7 +2143,16 @@ __global__ __launch_bounds__(256) void fast_cycle_kernel(CycleArgs a) {
             const int64_t slot = pair * a.slot_stride + k;
             const int32_t u = a.front[slot];
             const int32_t v = key_row(a.keys_f[slot]);
-            u2 = key_row(a.keys_b[slot]);
+            if (v >= 0 && v < a.n2) {
+                int32_t* mv = a.memo + pair * a.n2 + v;
+                const int32_t m = *mv;
+                if (m & kMemoFinal) {
+                    u2 = m & kMemoRow;
+                } else if ((m & kMemoRow) < a.slot_stride) {
+                    u2 = key_row(a.keys_b[pair * a.slot_stride + (m & kMemoRow)]);
+                    if (u2 >= 0) *mv = kMemoFinal | u2;
+                }
+            }
             a.keys_f_next[slot] = 0;
             a.keys_b_next[slot] = 0;
             if (v >= 0 && u2 >= 0) {
@@ -2670,8 +2729,25 @@ struct Profiler {
     bool on = false;
     int cap = 0, used = 0;
     hipEvent_t* ev = nullptr;
+    int64_t* queries = nullptr;   // device [cap]: queries each timed search launch ran
+    bool* counted = nullptr;      // host [cap]: whether the launch's entry of `queries` was written
 };
 thread_local Profiler g_prof;
+
+// Queries a search launch runs, summed over the batch (its per-pair device counts, or
+// the host count for every pair), into one entry of the profiling window.  Launched on
+// the call's stream just before the launch's start event, so it is not timed.
+__global__ __launch_bounds__(256) void prof_count_kernel(const int32_t* cnt, int64_t stride, int32_t host_n,
+                                                         int32_t batch, int64_t* out) {
+    __shared__ unsigned long long total;
+    if (threadIdx.x == 0) total = 0;
+    __syncthreads();
+    unsigned long long part = 0;
+    for (int p = threadIdx.x; p < batch; p += blockDim.x) part += (unsigned long long)(cnt ? cnt[p * stride] : host_n);
+    atomicAdd(&total, part);
+    __syncthreads();
+    if (threadIdx.x == 0) *out = (int64_t)total;
+}
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -2794,9 +2870,20 @@ int choose_arith(int dtype, int d) {
     return (d % 8 == 0 && d <= 32) ? AR_X3 : AR_F32;
 }
 
+// With a profiling window open: count the launch's queries, then its start event.
+int prof_search_begin(const NNArgs& a, int batch, hipStream_t st, bool& prof) {
+    prof = g_prof.on && g_prof.used < g_prof.cap;
+    if (!prof) return MR_OK;
+    MR_LAUNCH(prof_count_kernel, dim3(1), dim3(256), 0, st, a.dev_count, a.count_stride, a.host_count, batch,
+              g_prof.queries + g_prof.used);
+    if (dev_err()) return MR_ERR_DEVICE;
+    g_prof.counted[g_prof.used] = true;
+    return hipEventRecord(g_prof.ev[2 * g_prof.used], st) != hipSuccess ? MR_ERR_DEVICE : MR_OK;
+}
+
 int launch_nn(const NNArgs& a, int ar, int batch, hipStream_t st) {
-    const bool prof = g_prof.on && g_prof.used < g_prof.cap;
-    if (prof && hipEventRecord(g_prof.ev[2 * g_prof.used], st) != hipSuccess) return MR_ERR_DEVICE;
+    bool prof = false;
+    if (prof_search_begin(a, batch, st, prof)) return MR_ERR_DEVICE;
     if (ar == AR_F32) {
         switch ((a.d + 1) / 2) {
 #define MR_CASE(p) case p: launch_nn_t<AR_F32, p>(a, batch, st); break;
@@ -2858,8 +2945,8 @@ void launch_point_t(const NNArgs& a, int batch, hipStream_t st) {
 // One NN search under a metric (the similarity kernel of every entry point).
 int launch_search(const NNArgs& a, int metric, int ar, int batch, hipStream_t st) {
     if (metric != M_POINT) return launch_nn(a, ar, batch, st);
-    const bool prof = g_prof.on && g_prof.used < g_prof.cap;
-    if (prof && hipEventRecord(g_prof.ev[2 * g_prof.used], st) != hipSuccess) return MR_ERR_DEVICE;
+    bool prof = false;
+    if (prof_search_begin(a, batch, st, prof)) return MR_ERR_DEVICE;
     switch (a.d) {
         case 1: launch_point_t<1>(a, batch, st); break;
         case 2: launch_point_t<2>(a, batch, st); break;
@@ -2901,7 +2988,7 @@ NNArgs nn_args(const mr_map* q, const void* qdata, int q_role, const mr_map* db,
 }
 
 struct FastLayout {
-    size_t keys_f[2], keys_b[2], front[2], cnt[3], state, blk, total;
+    size_t keys_f[2], keys_b[2], front[2], cnt[3], state, blk, memo, blist, bcnt[2], total;
 };
 
 FastLayout fast_layout(const mr_map* a, const mr_map* b, int64_t nseeds) {
@@ -2916,6 +3003,10 @@ FastLayout fast_layout(const mr_map* a, const mr_map* b, int64_t nseeds) {
     for (int i = 0; i < 3; ++i) { L.cnt[i] = off; off = align256(off + (size_t)batch * 4); }
     L.state = off; off = align256(off + (size_t)batch * (size_t)(n1 > 0 ? n1 : 1) * 4);
     L.blk = off; off = align256(off + (size_t)batch * (size_t)(nblk_of(n1) > 0 ? nblk_of(n1) : 1) * 4);
+    const int64_t n2 = npix(b);
+    L.memo = off; off = align256(off + (size_t)batch * (size_t)(n2 > 0 ? n2 : 1) * 4);
+    L.blist = off; off = align256(off + slots * 4);
+    for (int i = 0; i < 2; ++i) { L.bcnt[i] = off; off = align256(off + (size_t)batch * 4); }
     L.total = off;
     return L;
 }
@@ -3164,6 +3255,9 @@ int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, 
     int32_t* cnt[3] = {at<int32_t>(ws, L.cnt[0]), at<int32_t>(ws, L.cnt[1]), at<int32_t>(ws, L.cnt[2])};
     int32_t* state = at<int32_t>(ws, L.state);
     int32_t* blk = at<int32_t>(ws, L.blk);
+    int32_t* memo = at<int32_t>(ws, L.memo);
+    int32_t* blist = at<int32_t>(ws, L.blist);
+    int32_t* bcnt[2] = {at<int32_t>(ws, L.bcnt[0]), at<int32_t>(ws, L.bcnt[1])};
 
     InitArgs ia;
     ia.state = state; ia.n1 = n1; ia.w = a->w; ia.stride = stride; ia.offset = offset;
@@ -3171,7 +3265,8 @@ int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, 
     ia.nseeds = (int32_t)ns;
     ia.front0 = fr[0]; ia.keys_f0 = kf[0]; ia.keys_b0 = kb[0]; ia.slot_stride = slot;
     ia.cnt0 = cnt[0]; ia.cnt1 = cnt[1];
-    const int64_t init_n = n1 > ns ? n1 : ns;
+    ia.memo = memo; ia.n2 = n2; ia.bcnt0 = bcnt[0]; ia.bcnt1 = bcnt[1];
+    const int64_t init_n = n1 > n2 ? n1 : n2;
     MR_LAUNCH(fast_init_kernel, dim3(grid_1d(init_n > 0 ? init_n : 1), batch), dim3(256), 0, st, ia);
     if (dev_err()) return MR_ERR_DEVICE;
 
@@ -3186,10 +3281,15 @@ int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, 
             f.dev_count = cnt[t % 3]; f.count_stride = 1;
             f.keys = kf[c]; f.keys_stride = slot;
             if ((rc = launch_search(f, metric, ar, batch, st))) return rc;
+            GatherArgs ga;
+            ga.keys_f = kf[c]; ga.cnt = cnt[t % 3]; ga.memo = memo; ga.n2 = n2;
+            ga.blist = blist; ga.bcnt = bcnt[c]; ga.bcnt_next = bcnt[x]; ga.slot_stride = slot;
+            MR_LAUNCH(fast_gather_kernel, dim3(cyc_grid, batch), dim3(256), 0, st, ga);
+            if (dev_err()) return MR_ERR_DEVICE;
             NNArgs r = nn_args(b, bd, 2, a, ad, 1);
             if (edges) { r.q_img = edges + 1; r.db_img = edges; }
-            r.qsrc = Q_KEYS; r.qlist = kf[c]; r.qlist_stride = slot;
-            r.dev_count = cnt[t % 3]; r.count_stride = 1;
+            r.qsrc = Q_LIST; r.qlist = blist; r.qlist_stride = slot;
+            r.dev_count = bcnt[c]; r.count_stride = 1;
             r.keys = kb[c]; r.keys_stride = slot;
             if ((rc = launch_search(r, metric, ar, batch, st))) return rc;
             CycleArgs ca;
@@ -3199,6 +3299,7 @@ int fast_impl(const mr_map* a, const mr_map* b, int32_t stride, int32_t offset, 
             ca.state = state;
             ca.active = iter_active ? iter_active + t : nullptr; ca.active_stride = max_iters;
             ca.slot_stride = slot; ca.n1 = n1; ca.last = (t == max_iters - 1);
+            ca.memo = memo; ca.n2 = n2;
             MR_LAUNCH(fast_cycle_kernel, dim3(cyc_grid, batch), dim3(256), 0, st, ca);
             if (dev_err()) return MR_ERR_DEVICE;
         }
@@ -3688,23 +3789,30 @@ int mr_fast_reciprocal_graph(const mr_map* images, const int32_t* edges, int32_t
 int mr_profile_begin(int32_t max_launches) {
     if (g_prof.on || max_launches < 1) return MR_ERR_PARAM;
     g_prof.ev = static_cast<hipEvent_t*>(calloc((size_t)2 * max_launches, sizeof(hipEvent_t)));
-    if (!g_prof.ev) return MR_ERR_DEVICE;
-    for (int i = 0; i < 2 * max_launches; ++i) {
-        if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
-            for (int k = 0; k < i; ++k) (void)hipEventDestroy(g_prof.ev[k]);
-            free(g_prof.ev);
-            g_prof.ev = nullptr;
-            return MR_ERR_DEVICE;
-        }
+    g_prof.counted = static_cast<bool*>(calloc((size_t)max_launches, sizeof(bool)));
+    int made = 0;
+    if (g_prof.ev && g_prof.counted)
+        while (made < 2 * max_launches && hipEventCreate(&g_prof.ev[made]) == hipSuccess) ++made;
+    void* q = nullptr;
+    const bool ok = made == 2 * max_launches &&
+                    hipMalloc(&q, (size_t)max_launches * sizeof(int64_t)) == hipSuccess;
+    if (!ok) {
+        for (int k = 0; k < made; ++k) (void)hipEventDestroy(g_prof.ev[k]);
+        free(g_prof.ev);
+        free(g_prof.counted);
+        g_prof = Profiler();
+        return MR_ERR_DEVICE;
     }
+    g_prof.queries = static_cast<int64_t*>(q);
     g_prof.cap = max_launches;
     g_prof.used = 0;
     g_prof.on = true;
     return MR_OK;
 }
 
-int mr_profile_end_each(double* total_ms, int64_t* launches, float* each_ms, int32_t cap) {
-    if (!g_prof.on || cap < 0 || (cap > 0 && !each_ms)) return MR_ERR_PARAM;
+int mr_profile_end_queries(double* total_ms, int64_t* launches, float* each_ms, int64_t* each_queries,
+                           int32_t cap) {
+    if (!g_prof.on || cap < 0 || (cap > 0 && !each_ms && !each_queries)) return MR_ERR_PARAM;
     double tot = 0.0;
     int rc = MR_OK;
     for (int i = 0; i < g_prof.used; ++i) {
@@ -3713,18 +3821,34 @@ int mr_profile_end_each(double* total_ms, int64_t* launches, float* each_ms, int
             hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess)
             rc = MR_ERR_DEVICE;
         tot += ms;
-        if (i < cap) each_ms[i] = ms;
+        if (i < cap && each_ms) each_ms[i] = ms;
+    }
+    const int nq = g_prof.used < cap ? g_prof.used : cap;
+    if (each_queries && nq > 0) {
+        // the counts were written on the calls' streams, before the end events waited for above
+        if (hipMemcpy(each_queries, g_prof.queries, (size_t)nq * sizeof(int64_t), hipMemcpyDeviceToHost) !=
+            hipSuccess)
+            rc = MR_ERR_DEVICE;
+        for (int i = 0; i < nq; ++i)
+            if (!g_prof.counted[i]) each_queries[i] = -1;
     }
     for (int i = 0; i < 2 * g_prof.cap; ++i) (void)hipEventDestroy(g_prof.ev[i]);
     free(g_prof.ev);
+    free(g_prof.counted);
+    (void)hipFree(g_prof.queries);
     if (total_ms) *total_ms = tot;
     if (launches) *launches = g_prof.used;
     g_prof = Profiler();
     return rc;
 }
 
+int mr_profile_end_each(double* total_ms, int64_t* launches, float* each_ms, int32_t cap) {
+    if (cap > 0 && !each_ms) return MR_ERR_PARAM;
+    return mr_profile_end_queries(total_ms, launches, each_ms, nullptr, cap);
+}
+
 int mr_profile_end(double* total_ms, int64_t* launches) {
-    return mr_profile_end_each(total_ms, launches, nullptr, 0);
+    return mr_profile_end_queries(total_ms, launches, nullptr, nullptr, 0);
 }
 
 }  // extern "C"

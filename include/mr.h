@@ -155,11 +155,11 @@ int mr_fast_reciprocal(const mr_map* a, const mr_map* b, int32_t stride, int32_t
  * callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation).  Same arguments (minus ws and
  * ws_bytes), results, validation and error codes as mr_fast_reciprocal.
- *   Scratch: a static device array of 8 MiB per GPU, held by the library until the
+ *   Scratch: a static device array of 16 MiB per GPU, held by the library until the
  *   process ends; the calling thread's current device must be the one `stream` and
  *   the maps belong to.  Problems needing more (mr_workspace_bytes with
- *   MR_OP_FAST_RECIPROCAL above 8 MiB: e.g. more than nine 512x384 pairs per call
- *   at stride 8; one 1024x768 pair needs 3.5 MiB) return MR_ERR_SCRATCH before
+ *   MR_OP_FAST_RECIPROCAL above 16 MiB: e.g. more than nine 512x384 pairs per call
+ *   at stride 8; one 1024x768 pair needs 6.5 MiB) return MR_ERR_SCRATCH before
  *   anything is launched.  The call allocates
  *   nothing: no hipMalloc, hipFree or allocating library routine.
  *   Every call on a GPU shares that GPU's buffer, and each call re-initialises the
@@ -288,11 +288,23 @@ int mr_infonce_backward(const mr_map* a, const mr_map* b, const int32_t* gt, int
  * milliseconds and the number of launches timed, release the events.
  * mr_profile_end_each: the same, and also each launch's time in milliseconds,
  * in launch order, into each_ms[0 .. min(cap, launches)) (cap >= 0; each_ms may
- * be NULL only when cap = 0).  Both return MR_ERR_PARAM without an open window.
+ * be NULL only when cap = 0).
+ * mr_profile_end_queries: the same, and also into each_queries[0 .. min(cap,
+ * launches)) the number of queries each search launch ran, summed over the batch
+ * (-1 for the loss kernels' launches, which are not counted).  The fast scheme
+ * searches the backward NN of a pixel of image 2 once per call, so its backward
+ * launches run fewer queries than there are live pixels; these counts give the
+ * work each launch did.  Either array may be NULL (not both when cap > 0).
+ * All three return MR_ERR_PARAM without an open window.  A window holds
+ * max_launches * 8 bytes of device memory (the counts) and its events from
+ * mr_profile_begin until it ends; a count is taken by a one-workgroup kernel on the
+ * call's stream just before the launch's start event, so it is not timed.
  * --------------------------------------------------------------------------- */
 int mr_profile_begin(int32_t max_launches);
 int mr_profile_end(double* total_ms, int64_t* launches);
 int mr_profile_end_each(double* total_ms, int64_t* launches, float* each_ms, int32_t cap);
+int mr_profile_end_queries(double* total_ms, int64_t* launches, float* each_ms, int64_t* each_queries,
+                           int32_t cap);
 
 /* ---------------------------------------------------------------------------
  * Launch log (no function): with the environment variable MR_LOG set to anything

@@ -122,6 +122,22 @@ int hipGetSymbolAddress(void** p, const void* sym) {
     if (!r) *p = g_symbol_stand_in; /* never dereferenced: the launches are doubles too */
     return r;
 }
+static char g_device_stand_in[4096] __attribute__((aligned(256)));
+int hipMalloc(void** p, size_t n) {
+    int r = hip_result();
+    if (!r) *p = n <= sizeof(g_device_stand_in) ? (void*)g_device_stand_in : (void*)(uintptr_t)(1u << 28);
+    return r;
+}
+int hipFree(void* p) { (void)p; return hip_result(); }
+/* the only blocking copy is device -> host of the profiling window's counts: write a
+ * recognisable value into every byte of the host side, so that an over-long size shows
+ * up as a heap overflow and the caller's use of the values can be checked */
+int hipMemcpy(void* dst, const void* src, size_t n, int kind) {
+    (void)src; (void)kind;
+    int r = hip_result();
+    if (!r) memset(dst, 7, n);
+    return r;
+}
 int hipMemcpyAsync(void* dst, const void* src, size_t n, int kind, void* stream) {
     (void)dst; (void)kind; (void)stream;
     /* the only copy the library makes is host -> device of the graph's edges: read the
@@ -382,6 +398,19 @@ static void validation_cases(void) {
             if (n != 3 || ms != 0.75 || each[0] != 0.25f || each[2] != 0.25f) {
                 ++g_failures; fprintf(stderr, "profile window: %ld launches, %g ms\n", (long)n, ms);
             }
+            /* per-launch query counts: three counted launches, copied into a block of
+             * exactly three entries (the double writes 0x0707... into each) */
+            CHECK(mr_profile_begin(3), MR_OK, 1);
+            for (int k = 0; k < 2; ++k) REACH(mr_nn_argmax(a, b, NULL, 1024, FAKE, NULL, FAKE_WS, need, NULL));
+            int64_t* qs = (int64_t*)malloc(3 * sizeof(int64_t));
+            qs[2] = -5;
+            CHECK(mr_profile_end_queries(&ms, &n, NULL, qs, 3), MR_OK, 1);
+            ++g_cases;
+            if (n != 2 || qs[0] != 0x0707070707070707ll || qs[1] != qs[0] || qs[2] != -5) {
+                ++g_failures; fprintf(stderr, "profile counts: %ld launches\n", (long)n);
+            }
+            REJECT(mr_profile_end_queries(&ms, &n, NULL, qs, 3), MR_ERR_PARAM); /* closed */
+            free(qs);
             free(a); free(b);
         }
     }

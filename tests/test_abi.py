@@ -124,7 +124,7 @@ def test_fast_reciprocal_validation(lib):
 
 def test_fast_reciprocal_static_validation(lib):
     """The workspace-free call validates like mr_fast_reciprocal and rejects problems
-    larger than its static scratch (8 MiB) before anything is launched."""
+    larger than its static scratch (16 MiB) before anything is launched."""
     a, b = M(64, 48), M(64, 48)
     out = ctypes.c_void_p(FAKE)
     call = lambda a=a, b=b, stride=8, offset=4, T=10, pairs=out, cap=48, n=out: \
@@ -137,13 +137,13 @@ def test_fast_reciprocal_static_validation(lib):
     assert call(cap=47) == CAP
     assert call(a=M(dtype=7), b=M(dtype=7)) == DTYPE
     assert call(a=M(), b=M(batch=2)) == SHAPE
-    # 2048 x 2048 pixels: the per-pixel state alone is 16 MiB
+    # 2048 x 2048 pixels: the per-pixel state and the backward memo are 16 MiB each
     big = M(2048, 2048)
-    assert lib.mr_workspace_bytes(2, R(big), R(big), 0, 8, 4) > (8 << 20)
+    assert lib.mr_workspace_bytes(2, R(big), R(big), 0, 8, 4) > (16 << 20)
     assert call(a=big, b=big, cap=1 << 20) == SCRATCH
-    # ten 512x384 pairs at stride 8 need more than 8 MiB, nine fit
+    # ten 512x384 pairs at stride 8 need more than 16 MiB, nine fit
     assert call(a=M(512, 384, batch=10), b=M(512, 384, batch=10), cap=3072) == SCRATCH
-    assert lib.mr_workspace_bytes(2, R(M(512, 384, batch=9)), R(M(512, 384, batch=9)), 0, 8, 4) <= (8 << 20)
+    assert lib.mr_workspace_bytes(2, R(M(512, 384, batch=9)), R(M(512, 384, batch=9)), 0, 8, 4) <= (16 << 20)
 
 
 def test_mutual_and_nn_validation(lib):
