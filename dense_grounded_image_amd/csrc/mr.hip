@@ -695,13 +695,29 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
     auto fetch = [&](int t, u32x4 (&stage)[MAXC]) {
         const int64_t tb = (int64_t)t * tile_bytes;
         const int64_t limit = (int64_t)ndb * rb;   // bytes of real rows
+        if constexpr (AR == AR_X3) {
+            // rows are whole 16-byte chunks: every lane loads one chunk per slot, lanes
+            // past the tile's real rows (or past the tile) a copy of its last real chunk,
+            // so the load count never depends on the lane or the tile and the compiler
+            // waits only for the older stage.  Rows of a ragged tile past the map's end
+            // then hold finite stale data, which the ragged epilogue masks.
+            const int rows = ndb - t * 32 < 32 ? ndb - t * 32 : 32;
+            const int nvalid = rows * (rb >> 4);
+            const char* base = dbytes + tb;
+#pragma unroll
+            for (int c = 0; c < MAXC; ++c) {
+                const int ch = threadIdx.x + c * kThreads;
+                stage[c] = *reinterpret_cast<const u32x4*>(base + (ch < nvalid ? ch : nvalid - 1) * 16);
+            }
+            return;
+        }
         if ((t + 1) * 32 <= ndb) {
             // a whole tile: every chunk is in bounds (wave-uniform base, per-lane offset)
             const char* base = dbytes + tb;
 #pragma unroll
             for (int c = 0; c < MAXC; ++c) {
                 const int ch = threadIdx.x + c * kThreads;
-                stage[c] = ch < nchunk ? *reinterpret_cast<const u32x4*>(base + ch * 16) : u32x4{0u, 0u, 0u, 0u};
+                if (ch < nchunk) stage[c] = *reinterpret_cast<const u32x4*>(base + ch * 16);
             }
             return;
         }
@@ -806,15 +822,20 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
     // LDS buffer i&1 at the end of iteration i-1, and read after that iteration's barrier
     fetch(t0, stage0);
     put(0, stage0);
-    if (nt > 1) fetch(t0 + 1, stage1);
+    if (AR == AR_X3) fetch(t0 + (nt > 1 ? 1 : 0), stage1);
+    else if (nt > 1) fetch(t0 + 1, stage1);
     __syncthreads();
+    // (split fp32: the fetches past the last tile re-read it, so that every iteration
+    // issues the same loads)
     for (int i = 0; i < nt; i += 2) {
-        if (i + 2 < nt) fetch(t0 + i + 2, stage0);
+        if (AR == AR_X3) fetch(t0 + (i + 2 < nt ? i + 2 : nt - 1), stage0);
+        else if (i + 2 < nt) fetch(t0 + i + 2, stage0);
         compute(i);
         if (i + 1 < nt) put(1, stage1);
         __syncthreads();
         if (i + 1 >= nt) break;
-        if (i + 3 < nt) fetch(t0 + i + 3, stage1);
+        if (AR == AR_X3) fetch(t0 + (i + 3 < nt ? i + 3 : nt - 1), stage1);
+        else if (i + 3 < nt) fetch(t0 + i + 3, stage1);
         compute(i + 1);
         if (i + 2 < nt) put(0, stage0);
         __syncthreads();
@@ -1087,7 +1108,7 @@ void nn_argmax_kernel(NNArgs a) {
         bx = blockIdx.x;
         gx = gridDim.x;
     }
-    const int n = a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count;
+    const int n = __builtin_amdgcn_readfirstlane(a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count);
     const int ntiles = (a.ndb + 31) >> 5;
     const int nqt = (n + 31) >> 5;                        // query tiles
     const int qgroups = (nqt + kWaves * QT - 1) / (kWaves * QT);
@@ -1152,8 +1173,8 @@ void nn_argmax_kernel(NNArgs a) {
             Operand<AR, P> q[QT];
             load_queries(q, q0 >> 5, 1, nact);
             const int seg = grp * kWaves + wv, nseg = ngroups * kWaves;
-            const int t0 = (int)((int64_t)seg * ntiles / nseg);
-            const int t1 = (int)((int64_t)(seg + 1) * ntiles / nseg);
+            const int t0 = __builtin_amdgcn_readfirstlane((int)((int64_t)seg * ntiles / nseg));
+            const int t1 = __builtin_amdgcn_readfirstlane((int)((int64_t)(seg + 1) * ntiles / nseg));
             float sv[QT];
             int rw[QT];   // row, or tile with TB
             if constexpr (TB) {
@@ -1203,12 +1224,14 @@ void nn_argmax_kernel(NNArgs a) {
         // round-robin to its waves (tile g0 + wv + kWaves*j)
         const int g0 = (int)((int64_t)qg * nqt / qgroups);
         const int g1 = (int)((int64_t)(qg + 1) * nqt / qgroups);
-        const int nact = g0 + wv < g1 ? (g1 - g0 - wv + kWaves - 1) / kWaves : 0;
+        const int nact = __builtin_amdgcn_readfirstlane(g0 + wv < g1 ? (g1 - g0 - wv + kWaves - 1) / kWaves : 0);
 
         Operand<AR, P> q[QT];
         load_queries(q, g0 + wv, kWaves, nact);
-        const int t0 = (int)((int64_t)sg * ntiles / nsg);
-        const int t1 = (int)((int64_t)(sg + 1) * ntiles / nsg);
+        // the segment bounds are wave-uniform: kept in scalar registers, the tile loop's
+        // control and the tiles' base addresses stay off the vector ALUs
+        const int t0 = __builtin_amdgcn_readfirstlane((int)((int64_t)sg * ntiles / nsg));
+        const int t1 = __builtin_amdgcn_readfirstlane((int)((int64_t)(sg + 1) * ntiles / nsg));
 
         // (score, row) -- or (score, tile) with TB -- per lane and query tile
         float sv[QT];
@@ -1270,7 +1293,7 @@ __global__ __launch_bounds__(kThreads) void recover_rows_kernel(NNArgs a) {
     const int jl = lane & 31;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform, so branches on it stay scalar
     const int pair = blockIdx.y;
-    const int n = a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count;
+    const int n = __builtin_amdgcn_readfirstlane(a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count);
     const int nqt = (n + 31) >> 5;
     const void* qbase = pair_base<AR>(a.qmap, a.q_pair_elems, map_of(a.q_img, pair));
     const void* dbase = pair_base<AR>(a.dbmap, a.db_pair_elems, map_of(a.db_img, pair));
@@ -1893,7 +1916,7 @@ __global__ __launch_bounds__(kThreads) void point_nn_kernel(NNArgs a) {
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int pair = blockIdx.y;
-    const int n = a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count;
+    const int n = __builtin_amdgcn_readfirstlane(a.dev_count ? a.dev_count[pair * a.count_stride] : a.host_count);
     const int ndb = a.ndb;
     if (n <= 0 || ndb <= 0) return;
     const int nqb = (n + QW - 1) / QW;
@@ -2314,7 +2337,7 @@ void lse_partial_kernel(NceArgs a) {
         const int sg = item - qg * nsg;
         const int g0 = (int)((int64_t)qg * nqt / qgroups);
         const int g1 = (int)((int64_t)(qg + 1) * nqt / qgroups);
-        const int nact = g0 + wv < g1 ? (g1 - g0 - wv + kWaves - 1) / kWaves : 0;
+        const int nact = __builtin_amdgcn_readfirstlane(g0 + wv < g1 ? (g1 - g0 - wv + kWaves - 1) / kWaves : 0);
         Operand<AR, P> q[QT];
 #pragma unroll
         for (int j = 0; j < QT; ++j) {
@@ -2502,7 +2525,7 @@ void nce_grad_kernel(NceGradArgs a) {
         const int sg = item - qg * nsg;
         const int g0 = (int)((int64_t)qg * nqt / qgroups);
         const int g1 = (int)((int64_t)(qg + 1) * nqt / qgroups);
-        const int nact = g0 + wv < g1 ? (g1 - g0 - wv + kWaves - 1) / kWaves : 0;
+        const int nact = __builtin_amdgcn_readfirstlane(g0 + wv < g1 ? (g1 - g0 - wv + kWaves - 1) / kWaves : 0);
         Operand<AR, P> q[kGradQT];
         float lq[kGradQT];                            // row pass: the query's lse2
 #pragma unroll
