@@ -681,6 +681,8 @@ __device__ __forceinline__ void interleave_mfma_valu() {
 // four waves multiplies the staged tile against its own QT query tiles held in
 // registers; the per-lane state ep (one of the epilogue states above) takes each
 // product tile.
+constexpr int kSplitValu = 26;   // vector instructions of one lane's split-fp32 staging (a chunk of four)
+
 template <int AR, int P, int QT, class Ep>
 __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, int rb, int t0, int t1, int ndb,
                                              char* lds, const Operand<AR, P> (&q)[QT],
@@ -739,24 +741,51 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
             stage[c] = v;
         }
     };
+    // split fp32 staging in three parts, one per query tile's chain (part k forms plane
+    // k; the last part also writes the three planes to LDS)
+    struct Split { f32x2 a, b; uint2 pl[3]; };
+    auto put_part = [&](int k, int buf, const u32x4 (&stage)[MAXC], Split& sp) {
+        static_assert(AR != AR_X3 || MAXC == 1, "one chunk per lane");
+        if (k == 0) {
+            sp.a = f32x2{__uint_as_float(stage[0][0]), __uint_as_float(stage[0][1])};
+            sp.b = f32x2{__uint_as_float(stage[0][2]), __uint_as_float(stage[0][3])};
+        }
+        const bf16x2 ha = __builtin_convertvector(sp.a, bf16x2);
+        const bf16x2 hb = __builtin_convertvector(sp.b, bf16x2);
+        sp.pl[k] = uint2{__builtin_bit_cast(uint32_t, ha), __builtin_bit_cast(uint32_t, hb)};
+        if (k < 2) {
+            sp.a = sp.a - __builtin_convertvector(ha, f32x2);
+            sp.b = sp.b - __builtin_convertvector(hb, f32x2);
+            return;
+        }
+        constexpr int D = 8 * P / 3;
+        const int ch = threadIdx.x;
+        const int cw = ch < nchunk ? ch : nchunk - 1;
+        const int r = cw / (D / 4), c0 = (cw - r * (D / 4)) * 4;
+        char* dst = lds + buf * BUF + r * 6 * D + c0 * 2;
+#pragma unroll
+        for (int q3 = 0; q3 < 3; ++q3) *reinterpret_cast<uint2*>(dst + q3 * 2 * D) = sp.pl[q3];
+    };
     auto put = [&](int buf, const u32x4 (&stage)[MAXC]) {
 #pragma unroll
         for (int c = 0; c < MAXC; ++c) {
             const int ch = threadIdx.x + c * kThreads;
-            if (ch < nchunk) {
-                if constexpr (AR == AR_X3) {
-                    // four fp32 components -> their h, m, l bf16 in the row's three planes
-                    constexpr int D = 8 * P / 3;
-                    const int r = ch / (D / 4), c0 = (ch - r * (D / 4)) * 4;
-                    uint2 a[3];
-                    split3x4(__uint_as_float(stage[c][0]), __uint_as_float(stage[c][1]),
-                             __uint_as_float(stage[c][2]), __uint_as_float(stage[c][3]), a);
-                    char* dst = lds + buf * BUF + r * 6 * D + c0 * 2;
+            if constexpr (AR == AR_X3) {
+                // four fp32 components -> their h, m, l bf16 in the row's three planes.
+                // Branch-free: lanes past the tile's chunks hold the same chunk as the
+                // tile's last lane (the fetch clamps both to the last real chunk) and write
+                // it to the same place, so the staging can sit between matrix instructions.
+                constexpr int D = 8 * P / 3;
+                const int cw = ch < nchunk ? ch : nchunk - 1;
+                const int r = cw / (D / 4), c0 = (cw - r * (D / 4)) * 4;
+                uint2 a[3];
+                split3x4(__uint_as_float(stage[c][0]), __uint_as_float(stage[c][1]),
+                         __uint_as_float(stage[c][2]), __uint_as_float(stage[c][3]), a);
+                char* dst = lds + buf * BUF + r * 6 * D + c0 * 2;
 #pragma unroll
-                    for (int k = 0; k < 3; ++k) *reinterpret_cast<uint2*>(dst + k * 2 * D) = a[k];
-                } else {
-                    *reinterpret_cast<u32x4*>(lds + buf * BUF + ch * 16) = stage[c];
-                }
+                for (int k = 0; k < 3; ++k) *reinterpret_cast<uint2*>(dst + k * 2 * D) = a[k];
+            } else if (ch < nchunk) {
+                *reinterpret_cast<u32x4*>(lds + buf * BUF + ch * 16) = stage[c];
             }
         }
     };
@@ -779,7 +808,12 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
         pending = false;
     };
 
-    auto compute = [&](int i) {
+    // mid(k), k = 0, 1, 2: the parts of the next tile's staging (split fp32: the split
+    // and its LDS write), issued inside compute -- on the interleaved path one part per
+    // query tile's chain, between its matrix instructions, so that the vector work runs
+    // while the matrix core is busy (the matrix core hides only a few vector
+    // instructions behind each of its own, and none of another wave's)
+    auto compute = [&](int i, auto&& mid) {
         const int t = t0 + i;
         const bool ragged = (t + 1) * 32 > ndb;
         Operand<AR, P> r;
@@ -789,6 +823,7 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
                 // the last query tile's chain accumulates straight into the pending
                 // unit (whose previous value the first epilogue has consumed)
                 f32x16 acc[QT > 1 ? QT - 1 : 1];
+                constexpr int JM = QT > 1 ? 1 : 0;   // the chain that carries the staging
 #pragma unroll
                 for (int j = 0; j < QT; ++j) {
                     f32x16 x = {};
@@ -798,7 +833,15 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
                     else ep.template tile<false>(lag, lag_t, h, ndb, QT - 1);
                     if (j < QT - 1) acc[j] = x;
                     else lag = x;
-                    interleave_mfma_valu<P, (Ep::valu + P - 1) / P>();
+                    if constexpr (QT == 3) {
+                        mid(j);
+                        interleave_mfma_valu<P, (Ep::valu + kSplitValu / 3 + P - 1) / P>();
+                    } else if (j == JM) {
+                        mid(0); mid(1); mid(2);
+                        interleave_mfma_valu<P, (Ep::valu + kSplitValu + P - 1) / P>();
+                    } else {
+                        interleave_mfma_valu<P, (Ep::valu + P - 1) / P>();
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 lag_t = t;
@@ -815,6 +858,7 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
                 ep.step(acc, t, h, ndb, j, ragged);
             }
         }
+        mid(0); mid(1); mid(2);
     };
 
     if (nt <= 0) return;
@@ -827,18 +871,31 @@ __device__ __forceinline__ void stream_tiles(const char* __restrict__ dbytes, in
     __syncthreads();
     // (split fp32: the fetches past the last tile re-read it, so that every iteration
     // issues the same loads)
-    for (int i = 0; i < nt; i += 2) {
-        if (AR == AR_X3) fetch(t0 + (i + 2 < nt ? i + 2 : nt - 1), stage0);
-        else if (i + 2 < nt) fetch(t0 + i + 2, stage0);
-        compute(i);
-        if (i + 1 < nt) put(1, stage1);
-        __syncthreads();
-        if (i + 1 >= nt) break;
-        if (AR == AR_X3) fetch(t0 + (i + 3 < nt ? i + 3 : nt - 1), stage1);
-        else if (i + 3 < nt) fetch(t0 + i + 3, stage1);
-        compute(i + 1);
-        if (i + 2 < nt) put(0, stage0);
-        __syncthreads();
+    if constexpr (AR == AR_X3) {
+        // the LDS write of the next tile runs inside the products of this one; past the
+        // last tile it writes the re-read copy into the buffer nobody reads again
+        Split sp;
+        for (int i = 0; i < nt; i += 2) {
+            fetch(t0 + (i + 2 < nt ? i + 2 : nt - 1), stage0);
+            compute(i, [&](int k) { put_part(k, 1, stage1, sp); });
+            __syncthreads();
+            if (i + 1 >= nt) break;
+            fetch(t0 + (i + 3 < nt ? i + 3 : nt - 1), stage1);
+            compute(i + 1, [&](int k) { put_part(k, 0, stage0, sp); });
+            __syncthreads();
+        }
+    } else {
+        for (int i = 0; i < nt; i += 2) {
+            if (i + 2 < nt) fetch(t0 + i + 2, stage0);
+            compute(i, [](int) {});
+            if (i + 1 < nt) put(1, stage1);
+            __syncthreads();
+            if (i + 1 >= nt) break;
+            if (i + 3 < nt) fetch(t0 + i + 3, stage1);
+            compute(i + 1, [](int) {});
+            if (i + 2 < nt) put(0, stage0);
+            __syncthreads();
+        }
     }
     if constexpr (AR == AR_X3 && Ep::kind == EP_KEY) flush();
 }
