@@ -48,9 +48,12 @@ def seeds_of(H, W, stride, offset):
 # ============================================================================ NN argmax
 
 @pytest.mark.parametrize("dtype,d", [("f32", 24), ("bf16", 24), ("f32", 1), ("f32", 3), ("f32", 17),
-                                     ("f32", 64), ("bf16", 8), ("bf16", 64)])
+                                     ("f32", 64), ("bf16", 8), ("bf16", 64), ("f32", 8), ("f32", 16),
+                                     ("f32", 32)])
 def test_nn_argmax_ragged(dtype, d):
-    """All queries, 37x29 against 41x23 pixels (neither a multiple of the 16-row tile)."""
+    """All queries, 37x29 against 41x23 pixels (neither a multiple of the 32-row tile).
+    fp32 maps with d = 8, 16, 24, 32 take the exact three-way bf16 split (three query
+    tiles per wave, two at d = 32), the others fp32 products."""
     rng = np.random.default_rng(100 + d)
     p = workloads.make_pair(37, 29, d, seed=100 + d, warp="shift", sigma=0.1, rho=0.2, dtype=dtype)
     q = workloads.make_pair(41, 23, d, seed=200 + d, warp="shift", sigma=0.1, rho=0.2, dtype=dtype)
@@ -379,6 +382,22 @@ def test_fast_full(cfg, dtype):
     assert act[0] == len(seeds_of(p.H, p.W, cfg["stride"], cfg["offset"]))
     assert (np.diff(act) <= 0).all()
     log("fast", cfg, dtype, rep, act.tolist())
+
+
+@pytest.mark.parametrize("d", [8, 16, 32])
+def test_fast_split_fp32_other_d(d):
+    """The fast scheme on fp32 maps with d = 8, 16, 32 (the split products with three
+    query tiles per wave, two at d = 32): 720 seeds fill whole query groups, so the
+    interleaved full-tile path runs, against the oracle."""
+    p = workloads.make_pair(90, 70, d, seed=900 + d, warp="affine", sigma=0.15, rho=0.3, dtype="f32")
+    A, B = pair_maps(p)
+    fp, fn, act = mr.fast_reciprocal(A, B, 3, 1, 6)
+    torch.cuda.synchronize()
+    orc = oracle.fast(p.D1, p.H, p.W, p.D2, 3, 1, 6)
+    act = act[0].cpu().numpy()
+    rep = checks.check_fast(mr.matches(fp, fn), orc, p.D1, p.D2, "f32", gpu_active=act)
+    assert act[0] == len(seeds_of(p.H, p.W, 3, 1))
+    log("fast split fp32", d, rep, act.tolist())
 
 
 def test_fast_is_subset_of_gpu_mutual_and_stride1_equals_it():
