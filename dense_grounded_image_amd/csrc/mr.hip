@@ -2528,6 +2528,7 @@ __global__ __launch_bounds__(256) void nce_loss_kernel(NceArgs a) {
 // with p split into two bf16 parts (hi + lo, relative error below 2^-17) and X the
 // staged tile read transposed (fp32 maps: its three bf16 planes).  d <= 32.
 constexpr int kGradQT = 1;   // query tiles per wave
+constexpr int kGradTStride = 36;   // halfwords per column of a transposed staged tile
 
 struct NceGradArgs {
     const void* qmap;        // query rows: a (row pass, through the ground truth) or b (column pass)
@@ -2550,7 +2551,12 @@ void nce_grad_kernel(NceGradArgs a) {
     static_assert(AR == AR_BF16 || AR == AR_X3, "bf16 maps or the split fp32 arithmetic");
     using Elem = typename ArithTraits<AR>::elem;
     constexpr int TILE = 32 * lds_row_bytes<AR, P>();   // a staged 32-row tile: bf16 rows, or [h|m|l] planes
+    constexpr int NPL = AR == AR_X3 ? 3 : 1;            // bf16 planes of a staged row
+    // the same tile transposed, per plane: column c's 32 rows at c * kGradTStride
+    // halfwords (8-byte aligned runs of 4 rows, padded against bank conflicts)
+    constexpr int TILE_T = NPL * 32 * kGradTStride;      // halfwords
     __shared__ __attribute__((aligned(16))) char lds[2 * TILE];
+    __shared__ __attribute__((aligned(16))) uint16_t ldsT[2 * TILE_T];
     __shared__ float lse_x[2][32];                    // column pass: lse2 of the staged rows
     const int lane = threadIdx.x & 63;
     const int h = lane >> 5;
@@ -2628,6 +2634,7 @@ void nce_grad_kernel(NceGradArgs a) {
         };
         auto put = [&](int buf, u32x4 v, float l) {
             if ((int)threadIdx.x < nchunk) {
+                uint16_t* tdst = ldsT + buf * TILE_T;
                 if constexpr (AR == AR_X3) {
                     // four fp32 components -> their h, m, l parts in the row's three planes
                     const int r = threadIdx.x / (d / 4), c0 = (threadIdx.x - r * (d / 4)) * 4;
@@ -2636,33 +2643,44 @@ void nce_grad_kernel(NceGradArgs a) {
                              __uint_as_float(v[3]), e3);
                     char* dst = lds + buf * TILE + r * 6 * d + c0 * 2;
 #pragma unroll
-                    for (int k = 0; k < 3; ++k) *reinterpret_cast<uint2*>(dst + k * 2 * d) = e3[k];
+                    for (int k = 0; k < 3; ++k) {
+                        *reinterpret_cast<uint2*>(dst + k * 2 * d) = e3[k];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            tdst[(k * 32 + c0 + e) * kGradTStride + r] =
+                                (uint16_t)((e & 1 ? (e < 2 ? e3[k].x : e3[k].y) >> 16 : (e < 2 ? e3[k].x : e3[k].y)) & 0xFFFF);
+                    }
                 } else {
                     *reinterpret_cast<u32x4*>(lds + buf * TILE + threadIdx.x * 16) = v;
+                    const int r = threadIdx.x / (rb / 16), c0 = (threadIdx.x - r * (rb / 16)) * 8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        tdst[(c0 + e) * kGradTStride + r] = (uint16_t)((v[e >> 1] >> (16 * (e & 1))) & 0xFFFF);
                 }
             }
             if (COLS && threadIdx.x < 32) lse_x[buf][threadIdx.x] = l;
         };
         auto compute = [&](int buf, int t, auto ragged) {
             constexpr bool RAGGED = decltype(ragged)::value;
-            constexpr int NPL = AR == AR_X3 ? 3 : 1;  // bf16 planes of a staged row
             const uint16_t* xs = reinterpret_cast<const uint16_t*>(lds + buf * TILE);
             Operand<AR, P> xo;
             xo.load(xs, jl, true, h, d, COLS ? 1 : 2);
             // the tile read transposed: lane (h, c) holds plane k of X[row R(s, h, e)][c],
             // e = 0..7, with R the accumulator's row order, so k-slot 8h + e of step s
-            // pairs p and X
+            // pairs p and X.  R(s, h, e) runs over rows 16s + 4h + (0..3) for e < 4 and
+            // 16s + 8 + 4h + (0..3) for e >= 4: two 8-byte reads of column c.
             bf16x8 xt[NPL][2];
+            const uint16_t* xtc = ldsT + buf * TILE_T + (jl < d ? jl : 0) * kGradTStride + 4 * h;
 #pragma unroll
             for (int k = 0; k < NPL; ++k)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int r = tile_row(8 * s2 + e, h);
-                        xt[k][s2][e] =
-                            __builtin_bit_cast(__bf16, jl < d ? xs[(r * NPL + k) * d + jl] : (uint16_t)0);
-                    }
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const uint2 lo4 = *reinterpret_cast<const uint2*>(xtc + k * 32 * kGradTStride + 16 * s2);
+                    const uint2 hi4 = *reinterpret_cast<const uint2*>(xtc + k * 32 * kGradTStride + 16 * s2 + 8);
+                    u32x4 w = {lo4.x, lo4.y, hi4.x, hi4.y};
+                    if (jl >= d) w = u32x4{0u, 0u, 0u, 0u};
+                    xt[k][s2] = __builtin_bit_cast(bf16x8, w);
+                }
             float lx[16];
             if (COLS) {
 #pragma unroll
