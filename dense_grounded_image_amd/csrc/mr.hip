@@ -2611,8 +2611,8 @@ void nce_grad_kernel(NceGradArgs a) {
                     q[j].load(qbase, valid ? row : 0, valid, h, d, COLS ? 2 : 1);
             }
         }
-        const int t0 = (int)((int64_t)sg * ntiles / nsg);
-        const int t1 = (int)((int64_t)(sg + 1) * ntiles / nsg);
+        const int t0 = __builtin_amdgcn_readfirstlane((int)((int64_t)sg * ntiles / nsg));
+        const int t1 = __builtin_amdgcn_readfirstlane((int)((int64_t)(sg + 1) * ntiles / nsg));
         f32x16 o[kGradQT];
 #pragma unroll
         for (int j = 0; j < kGradQT; ++j) o[j] = f32x16{};
@@ -2664,7 +2664,15 @@ void nce_grad_kernel(NceGradArgs a) {
             constexpr bool RAGGED = decltype(ragged)::value;
             const uint16_t* xs = reinterpret_cast<const uint16_t*>(lds + buf * TILE);
             Operand<AR, P> xo;
-            xo.load(xs, jl, true, h, d, COLS ? 1 : 2);
+            if constexpr (AR == AR_BF16) {
+                // k-slots past d repeat the row's first chunk: the query operand is zero
+                // there, so the scores are unchanged (as in the search's register stream)
+                int off[P];
+                Operand<AR, P>::db_offsets(jl, h, d, off);
+                xo.load_db(reinterpret_cast<const char*>(xs), off);
+            } else {
+                xo.load(xs, jl, true, h, d, COLS ? 1 : 2);
+            }
             // the tile read transposed: lane (h, c) holds plane k of X[row R(s, h, e)][c],
             // e = 0..7, with R the accumulator's row order, so k-slot 8h + e of step s
             // pairs p and X.  R(s, h, e) runs over rows 16s + 4h + (0..3) for e < 4 and
@@ -2677,8 +2685,8 @@ void nce_grad_kernel(NceGradArgs a) {
                 for (int s2 = 0; s2 < 2; ++s2) {
                     const uint2 lo4 = *reinterpret_cast<const uint2*>(xtc + k * 32 * kGradTStride + 16 * s2);
                     const uint2 hi4 = *reinterpret_cast<const uint2*>(xtc + k * 32 * kGradTStride + 16 * s2 + 8);
-                    u32x4 w = {lo4.x, lo4.y, hi4.x, hi4.y};
-                    if (jl >= d) w = u32x4{0u, 0u, 0u, 0u};
+                    // (lanes c >= d repeat column 0: their output columns are never read)
+                    const u32x4 w = {lo4.x, lo4.y, hi4.x, hi4.y};
                     xt[k][s2] = __builtin_bit_cast(bf16x8, w);
                 }
             float lx[16];
